@@ -1,0 +1,191 @@
+"""Benchmark of the quantized MoE layer on one MI355X.
+
+Workload (the headline decode configuration): one Xing4.0-29B-A4B MoE layer --
+hidden 3584, 64 routed experts top-4 + 1 shared, expert_ffn 1024, sigmoid router,
+routed_scaling 2.0, IQ4_NL experts -- decoding 1000 independent tokens, T=1 per call.
+The layer is placed 32 times in HBM (12.9 GB) and token i uses placement i mod 32, so
+the 256 MB last-level cache cannot serve one token's expert reads from an earlier
+token's.  A step is the 1000-token sweep, captured once as a HIP graph and replayed.
+
+Printed JSON line: tok/s for the whole sweep; the roofline of the expert FFN (the
+dominant kernels: bucket + gate/up + down + combine) from HIP events around each
+token's moe_expert_forward, with the stream kept busy so that host launch time does
+not enter; the CPU oracle timed on a bounded sample of the same tokens.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+N_TOKENS = 1000
+PLACEMENTS = 32
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--distinct-layers", type=int, default=4,
+                   help="distinct seeded layers generated; placements reuse them at distinct addresses")
+    p.add_argument("--cpu-sample", type=int, default=24, help="tokens the CPU oracle runs (0: skip)")
+    p.add_argument("--no-graph", action="store_true", help="replay eagerly instead of through a HIP graph")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    import quantized_moe_decode_sigmoid_amd as qm
+    import synth
+
+    shape = synth.WORKLOADS["xing4"]
+    H, E, K, F = shape.hidden, shape.n_experts, shape.top_k, shape.ffn
+    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    eb = qm.moe_expert_bytes(cfg)
+
+    t0 = time.time()
+    distinct = max(1, min(args.distinct_layers, PLACEMENTS))
+    layers = [synth.layer_inputs(shape, layer=l) for l in range(distinct)]
+    x_bits = synth.tokens(shape, N_TOKENS)
+    gen_s = time.time() - t0
+
+    # placements: packed arena + shared + router weight at distinct addresses
+    arenas, shareds, gates = [], [], []
+    staged = []
+    for l in layers:
+        a = torch.from_numpy(l["arena"]).to(dev)
+        s = torch.from_numpy(l["shared"]).to(dev)
+        pa, ps = torch.empty_like(a), torch.empty_like(s)
+        qm.moe_pack_experts(cfg, E, a, pa)
+        qm.moe_pack_experts(cfg, 1, s, ps)
+        staged.append((pa, ps, torch.from_numpy(l["gate_w"]).to(dev)))
+        del a, s
+    for c in range(PLACEMENTS):
+        pa, ps, g = staged[c % distinct]
+        arenas.append(pa.clone())
+        shareds.append(ps.clone())
+        gates.append(g.clone())
+    del staged
+    torch.cuda.synchronize()
+
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    out = torch.empty((N_TOKENS, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((N_TOKENS, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((N_TOKENS, K), dtype=torch.float32, device=dev)
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device=dev)
+
+    def sweep():
+        for i in range(N_TOKENS):
+            c = i % PLACEMENTS
+            qm.moe_layer_forward(cfg, 1, x[i:i + 1], gates[c], None, arenas[c], shareds[c], out[i:i + 1],
+                                 ids[i:i + 1], wts[i:i + 1], ws)
+
+    stream = torch.cuda.Stream()
+    graph = None
+    with torch.cuda.stream(stream):
+        sweep()  # eager warm-up outside the graph (also the first-call figure)
+        torch.cuda.synchronize()
+        if not args.no_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=stream):
+                sweep()
+        run = graph.replay if graph is not None else sweep
+        t_first = time.time()
+        run()
+        torch.cuda.synchronize()
+        first_ms = (time.time() - t_first) * 1e3
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_wall = time.time()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            run()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.time() - t_wall
+        total_ms = ev0.elapsed_time(ev1)
+
+        # expert FFN timing: HIP events around each token's moe_expert_forward on this
+        # stream, queued behind a spin kernel so the GPU never waits for the host
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(N_TOKENS)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(N_TOKENS)]
+        torch.cuda._sleep(400_000_000)
+        for i in range(N_TOKENS):
+            c = i % PLACEMENTS
+            qm.moe_route(cfg, 1, x[i:i + 1], gates[c], None, ids[i:i + 1], wts[i:i + 1], ws)
+            starts[i].record(stream)
+            qm.moe_expert_forward(cfg, 1, x[i:i + 1], ids[i:i + 1], wts[i:i + 1], arenas[c], shareds[c],
+                                  out[i:i + 1], ws)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+    ffn_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
+
+    ms_per_step = total_ms / args.steps
+    tok_s = N_TOKENS / (ms_per_step / 1e3)
+    expert_bytes_per_token = (K + shape.n_shared) * eb
+    ffn_avg_s = float(np.mean(ffn_us)) / 1e6
+    achieved = expert_bytes_per_token / ffn_avg_s / 1e9
+    layer_bytes = expert_bytes_per_token + E * H * 4 + H * 2 + H * 4
+
+    cpu = None
+    if args.cpu_sample > 0:
+        import oracle
+        n = args.cpu_sample
+        c0 = time.time()
+        for i in range(n):
+            l = layers[(i % PLACEMENTS) % distinct]
+            oracle.layer(x_bits[i:i + 1], l["gate_w"], l["arena"], l["shared"], K, F, shape.routed_scale)
+        cs = time.time() - c0
+        cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"{n} of the {N_TOKENS} tokens, one oracle.layer call (T=1) each, {cs:.1f} s"}
+
+    res = {
+        "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "xing4 MoE layer decode, T=1 per call: hidden 3584, 64 experts top-4 + 1 shared, "
+                               "ffn 1024, IQ4_NL experts, sigmoid router, scale 2.0; 1000 tokens per step over "
+                               f"{PLACEMENTS} placements of {distinct} distinct seeded layers",
+                   "tokens_per_step": N_TOKENS, "graph": graph is not None},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "expert FFN (moe_expert_forward: bucket, gate/up, down, combine)",
+                     "bytes_per_launch": expert_bytes_per_token, "avg_us": round(float(np.mean(ffn_us)), 3),
+                     "median_us": round(float(np.median(ffn_us)), 3)},
+        "cpu_baseline": cpu,
+        "layer_gbs": round(layer_bytes * tok_s / 1e9, 1),
+        "first_step_ms": round(first_ms, 3),
+        "wall_s": round(wall_s, 3),
+        "setup_s": round(gen_s, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * moe.h -- C ABI of libmoe: one quantized Mixture-of-Experts FFN layer on an
+ * MI355X (gfx950) GPU.
+ *
+ * The layer (shape of Xing4.0-29B-A4B: PocketLLM design record, section 1
+ * shape table; HelloSun xing4_0-29b-IQ4_NL_EPQ model card, "Model and
+ * routing" table):
+ *   - a sigmoid router over E experts with an optional selection-only bias
+ *     (ffn_exp_probs_b, "noaux_tc"), top-K, weights normalised over the K
+ *     selected scores and multiplied by routed_scale (2.0);
+ *   - per selected expert a SwiGLU FFN y = W_down(silu(W_gate x) * (W_up x))
+ *     (zLLM "Algorithm Layer", FFN section) with IQ4_NL weights (32-weight
+ *     blocks, one fp16 scale, 4-bit indices into a 16-entry non-linear table);
+ *   - an always-on shared expert of weight 1;
+ *   - the routed + shared sum in fp32 (design record, section 2), the top-K
+ *     summed in slot order with no atomics (design record, section 4).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named *_dev are device pointers; the caller owns all memory
+ *     (inputs, outputs, arenas, workspace).  The library keeps no device
+ *     state, allocates nothing and never synchronizes: each call validates its
+ *     arguments on the host, then enqueues kernels on `stream` (0 = the null
+ *     stream) and returns.  Device memory is never read back to the host.
+ *   - Validation failures return a negative status before anything is
+ *     enqueued.  Every device pointer must be 16-byte aligned (MOE_EALIGN).
+ *     A call with T == 0 tokens is a no-op that checks only cfg and T
+ *     (except moe_bucket, which then writes all-zero counts and offsets).
+ *   - Values that are only known on the device (expert ids outside [0, E),
+ *     non-finite activations) are not checked: behaviour is undefined.
+ *   - Row-major layouts.  bf16 is the upper half of an IEEE fp32, fp16 is
+ *     IEEE binary16, both little-endian.
+ *   - Calls on one stream are ordered; calls sharing a workspace must not
+ *     overlap in time.
+ */
+#ifndef QMOE_MOE_H
+#define QMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes. */
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* a null required pointer, a bad size or shape */
+  MOE_EALIGN = -2,       /* a device pointer not 16-byte aligned */
+  MOE_EWORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes() */
+  MOE_EUNSUPPORTED = -4, /* a shape outside the supported set (see moe_config) */
+  MOE_ELAUNCH = -5       /* the HIP runtime refused a launch */
+} moe_status;
+
+/* Arithmetic contract of the expert FFN.
+ * FP32: weights are the exact IQ4_NL values d*level, the activation product
+ *       silu(g)*u is kept in fp32, all sums in fp32 (decode-sized calls).
+ * BF16: weights are rounded to bf16 (nearest even) in LDS and the product
+ *       silu(g)*u is rounded to bf16 before the down projection; products run
+ *       on bf16 MFMA with fp32 accumulation (batched / prefill calls).
+ * AUTO: FP32 when T*K <= 16*E (at most 16 routes per expert on average),
+ *       else BF16.  The router and the combine are fp32 in every mode. */
+typedef enum { MOE_PREC_AUTO = 0, MOE_PREC_FP32 = 1, MOE_PREC_BF16 = 2 } moe_precision;
+
+/* Layer shape.  Supported: hidden % 256 == 0, ffn % 128 == 0,
+ * 1 <= n_experts <= 256, 1 <= top_k <= min(n_experts, 8), n_shared in {0, 1},
+ * routed_scale finite.  Tokens per call: 0 <= T <= 65536. */
+typedef struct {
+  int32_t hidden;     /* H: model width */
+  int32_t ffn;        /* F: expert intermediate width */
+  int32_t n_experts;  /* E: routed experts */
+  int32_t top_k;      /* K: experts per token */
+  int32_t n_shared;   /* shared experts (0 or 1) */
+  float routed_scale; /* multiplies the normalised routed weights (2.0) */
+  int32_t precision;  /* moe_precision */
+} moe_config;
+
+/* ---- queries (host only, no GPU work) ----------------------------------- */
+
+int moe_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_string(int status);
+
+/* MOE_OK if the shape is supported, else MOE_EINVAL / MOE_EUNSUPPORTED. */
+moe_status moe_check_config(const moe_config* cfg);
+
+/* Bytes of one expert in either layout: 3 matrices of F*H/32 IQ4_NL blocks of
+ * 18 bytes (the model card's 6,193,152 B for H=3584, F=1024).  0 if the
+ * configuration is invalid. */
+size_t moe_expert_bytes(const moe_config* cfg);
+
+/* Precision the expert FFN will use for T tokens (resolves AUTO). */
+int32_t moe_resolved_precision(const moe_config* cfg, int32_t T);
+
+/* Workspace bytes moe_route / moe_expert_forward / moe_layer_forward need for
+ * T tokens (the maximum of the three).  0 if the configuration is invalid. */
+size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
+
+/* ---- expert arena --------------------------------------------------------
+ * GGUF order (input of moe_pack_experts): expert e starts at e*expert_bytes;
+ * inside it W_gate [F rows][H/32 blocks], W_up [F][H/32], W_down [H][F/32],
+ * each block 18 bytes: fp16 scale d, then 16 bytes where byte j holds the
+ * index of weight j in its low nibble and of weight j+16 in its high nibble
+ * (the ggml IQ4_NL definition the model card's checker follows).
+ *
+ * Packed order (what the compute entry points read): the same bytes regrouped
+ * per matrix into 1152-byte tiles of 16 rows x 4 blocks, so that a wavefront
+ * streams each tile with one 16-byte load per lane: tile (rt, kg) covers rows
+ * 16*rt..16*rt+15 and blocks 4*kg..4*kg+3 and sits at tile index
+ * rt*(NB/4) + kg (NB = blocks per row).  Bytes [0, 1024): lane slot s
+ * (row 16*rt + s%16, nibble word w = s/16) holds nibble bytes 4w..4w+3 of
+ * blocks 4kg+0..4kg+3 of that row, 4 bytes each.  Bytes [1024, 1152): the 64
+ * fp16 scales, scale of (row 16*rt + 4*G + i, block 4*kg + b) at
+ * 1024 + 32*G + 8*b + 2*i.  Packing is a permutation of bytes: an expert
+ * keeps moe_expert_bytes() bytes and the same start offset. */
+
+/* Repack n_experts consecutive experts from GGUF order (src_dev) into packed
+ * order (dst_dev).  src and dst must not overlap.  Run once at load. */
+moe_status moe_pack_experts(const moe_config* cfg, int32_t n_experts, const void* src_dev, void* dst_dev,
+                            hipStream_t stream);
+
+/* Dequantize one matrix of one packed expert to fp32, row-major:
+ * matrix 0 = W_gate [F][H], 1 = W_up [F][H], 2 = W_down [H][F].
+ * precision FP32: the exact weights d*level.  BF16: those weights rounded to
+ * bf16 (nearest even), returned widened to fp32.  Uses the same decode as the
+ * FFN kernels (model card, pure-NumPy parity section: 16-entry non-linear
+ * lookup times one fp16 scale). */
+moe_status moe_dequant(const moe_config* cfg, const void* packed_expert_dev, int32_t matrix, int32_t precision,
+                       float* out_dev, hipStream_t stream);
+
+/* ---- the layer's steps ---------------------------------------------------- */
+
+/* Router (model card "Model and routing": sigmoid + ffn_exp_probs_b, top-K,
+ * sum normalisation, expert_weights_scale 2.0).
+ *   x_dev       bf16 [T][H] activations
+ *   gate_w_dev  fp32 [E][H] router weight
+ *   sel_bias_dev fp32 [E] selection bias, or NULL for none
+ *   topk_ids_dev int32 [T][K] out: slot k = k-th expert by
+ *               (sigmoid(logit) + bias) descending, expert index ascending
+ *   topk_w_dev  fp32 [T][K] out: routed_scale * s_k / (s_0 + ... + s_{K-1})
+ *               with s the unbiased sigmoid scores, sums left to right.
+ * Logits are fp32 dot products in one fixed order (64 partial sums of
+ * elements 256m+4j+c, fused multiply-adds over (m, c), then pairwise sums
+ * p[j] + p[j^s], s = 32..1); the sigmoid is evaluated in double by a fixed
+ * sequence of IEEE operations and rounded to fp32; so the outputs are
+ * bit-reproducible and equal to the CPU reference.  ws: >= moe_workspace_bytes. */
+moe_status moe_route(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
+                     const float* sel_bias_dev, int32_t* topk_ids_dev, float* topk_w_dev, void* ws_dev,
+                     size_t ws_bytes, hipStream_t stream);
+
+/* Token-to-expert bucketing (design record, section 4: routes sorted by
+ * expert so each output has one writer).  Route r = t*K + k.
+ *   counts_dev  int32 [E]     routes per expert
+ *   offsets_dev int32 [E+1]   exclusive prefix sum, offsets[E] = T*K
+ *   perm_dev    int32 [T*K]   routes grouped by expert (ascending), ascending r
+ *                             inside an expert
+ *   pos_dev     int32 [T*K]   inverse permutation, or NULL
+ * Bit-exact (integer).  Needs no workspace. */
+moe_status moe_bucket(const moe_config* cfg, int32_t T, const int32_t* topk_ids_dev, int32_t* counts_dev,
+                      int32_t* offsets_dev, int32_t* perm_dev, int32_t* pos_dev, hipStream_t stream);
+
+/* Expert FFN and combine for given routing:
+ *   out[t] = sum_{k=0..K-1} topk_w[t][k] * FFN_{topk_ids[t][k]}(x[t])
+ *            + FFN_shared(x[t])                     (if n_shared == 1)
+ *   x_dev        bf16 [T][H]
+ *   arena_dev    E experts, packed order (moe_pack_experts)
+ *   shared_dev   one packed expert, or NULL when n_shared == 0
+ *   out_dev      fp32 [T][H], fully overwritten
+ * Deterministic: the same inputs give the same bits on every run; the slot
+ * sum runs in slot order.  ws: >= moe_workspace_bytes(cfg, T). */
+moe_status moe_expert_forward(const moe_config* cfg, int32_t T, const void* x_dev, const int32_t* topk_ids_dev,
+                              const float* topk_w_dev, const void* arena_dev, const void* shared_dev,
+                              float* out_dev, void* ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* The whole layer: moe_route then moe_expert_forward.  topk_ids_out_dev and
+ * topk_w_out_dev receive the routing when non-NULL (else the workspace holds
+ * it).  ws: >= moe_workspace_bytes(cfg, T). */
+moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
+                             const float* sel_bias_dev, const void* arena_dev, const void* shared_dev,
+                             float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
+                             size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_MOE_H */

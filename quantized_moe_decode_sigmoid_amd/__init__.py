@@ -1,0 +1,199 @@
+"""Python binding of libmoe: one quantized MoE FFN layer on MI355X (gfx950).
+
+Argument marshalling only -- every step of the layer runs in the hand-written HIP
+kernels of ``libmoe.so`` (C ABI in ``include/moe.h``); torch provides device memory
+and the current HIP stream.  The functions carry the C names; each takes torch
+tensors, passes their device pointers and ``torch.cuda.current_stream()``, and raises
+``MoeError`` on a non-zero status.  There is no fallback: if the library is missing
+the import of this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3, -4, -5
+PREC_AUTO, PREC_FP32, PREC_BF16 = 0, 1, 2
+MATRIX_GATE, MATRIX_UP, MATRIX_DOWN = 0, 1, 2
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("routed_scale", ctypes.c_float),
+                ("precision", ctypes.c_int32)]
+
+
+def make_config(hidden: int, ffn: int, n_experts: int, top_k: int, n_shared: int = 1,
+                routed_scale: float = 2.0, precision: int = PREC_AUTO) -> moe_config:
+    return moe_config(hidden, ffn, n_experts, top_k, n_shared, routed_scale, precision)
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                      "python quantized_moe_decode_sigmoid_amd/build.py")
+
+# torch brings its own HIP runtime (soname libamdhip64.so.7, requested by its
+# libraries under another name).  Loading torch first makes libmoe bind to that
+# same runtime instead of pulling a second copy into the process.
+import torch  # noqa: E402,F401
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+_cfgp = ctypes.POINTER(moe_config)
+_SIGS = {
+    "moe_abi_version": ([], _i32),
+    "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "moe_check_config": ([_cfgp], _i32),
+    "moe_expert_bytes": ([_cfgp], _sz),
+    "moe_resolved_precision": ([_cfgp, _i32], _i32),
+    "moe_workspace_bytes": ([_cfgp, _i32], _sz),
+    "moe_pack_experts": ([_cfgp, _i32, _vp, _vp, _vp], _i32),
+    "moe_dequant": ([_cfgp, _vp, _i32, _i32, _vp, _vp], _i32),
+    "moe_route": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_bucket": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "moe_expert_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_layer_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+EXPORTED = tuple(_SIGS)
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL).  Raw integers pass through."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def status_string(status: int) -> str:
+    return _lib.moe_status_string(status).decode()
+
+
+def moe_abi_version() -> int:
+    return _lib.moe_abi_version()
+
+
+def moe_check_config(cfg: moe_config) -> int:
+    return _lib.moe_check_config(ctypes.byref(cfg))
+
+
+def moe_expert_bytes(cfg: moe_config) -> int:
+    return _lib.moe_expert_bytes(ctypes.byref(cfg))
+
+
+def moe_resolved_precision(cfg: moe_config, T: int) -> int:
+    return _lib.moe_resolved_precision(ctypes.byref(cfg), T)
+
+
+def moe_workspace_bytes(cfg: moe_config, T: int) -> int:
+    return _lib.moe_workspace_bytes(ctypes.byref(cfg), T)
+
+
+def moe_pack_experts(cfg, n_experts, src, dst, stream=None):
+    _check(_lib.moe_pack_experts(ctypes.byref(cfg), n_experts, _p(src), _p(dst), _stream(stream)), "moe_pack_experts")
+
+
+def moe_dequant(cfg, packed_expert, matrix, precision, out, stream=None):
+    _check(_lib.moe_dequant(ctypes.byref(cfg), _p(packed_expert), matrix, precision, _p(out), _stream(stream)),
+           "moe_dequant")
+
+
+def moe_route(cfg, T, x, gate_w, sel_bias, topk_ids, topk_w, ws, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.moe_route(ctypes.byref(cfg), T, _p(x), _p(gate_w), _p(sel_bias), _p(topk_ids), _p(topk_w), _p(ws),
+                          ws_bytes, _stream(stream)), "moe_route")
+
+
+def moe_bucket(cfg, T, topk_ids, counts, offsets, perm, pos=None, stream=None):
+    _check(_lib.moe_bucket(ctypes.byref(cfg), T, _p(topk_ids), _p(counts), _p(offsets), _p(perm), _p(pos),
+                           _stream(stream)), "moe_bucket")
+
+
+def moe_expert_forward(cfg, T, x, topk_ids, topk_w, arena, shared, out, ws, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.moe_expert_forward(ctypes.byref(cfg), T, _p(x), _p(topk_ids), _p(topk_w), _p(arena), _p(shared),
+                                   _p(out), _p(ws), ws_bytes, _stream(stream)), "moe_expert_forward")
+
+
+def moe_layer_forward(cfg, T, x, gate_w, sel_bias, arena, shared, out, topk_ids=None, topk_w=None, ws=None,
+                      ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check(_lib.moe_layer_forward(ctypes.byref(cfg), T, _p(x), _p(gate_w), _p(sel_bias), _p(arena), _p(shared),
+                                  _p(out), _p(topk_ids), _p(topk_w), _p(ws), ws_bytes, _stream(stream)),
+           "moe_layer_forward")
+
+
+class DeviceLayer:
+    """Device copies of one layer's weights, the expert arena packed by moe_pack_experts.
+
+    gate_w fp32 [E, H], bias fp32 [E] or None, arena / shared uint8 in GGUF block order
+    (numpy or torch).  ``forward`` allocates the outputs and workspace with torch and
+    calls moe_layer_forward.
+    """
+
+    def __init__(self, cfg: moe_config, gate_w, bias, arena, shared, device="cuda"):
+        import torch
+
+        def dev(a, dtype):
+            t = torch.as_tensor(a)
+            return t.to(device=device, dtype=dtype).contiguous()
+
+        self.cfg = cfg
+        self.device = device
+        self.gate_w = dev(gate_w, torch.float32)
+        self.bias = None if bias is None else dev(bias, torch.float32)
+        eb = moe_expert_bytes(cfg)
+        src = dev(arena, torch.uint8)
+        assert src.numel() == eb * cfg.n_experts
+        self.arena = torch.empty_like(src)
+        moe_pack_experts(cfg, cfg.n_experts, src, self.arena)
+        self.shared = None
+        if cfg.n_shared:
+            ssrc = dev(shared, torch.uint8)
+            assert ssrc.numel() == eb
+            self.shared = torch.empty_like(ssrc)
+            moe_pack_experts(cfg, 1, ssrc, self.shared)
+        self._ws = None
+
+    def workspace(self, T: int):
+        import torch
+        need = moe_workspace_bytes(self.cfg, T)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def forward(self, x, out=None, topk_ids=None, topk_w=None):
+        """x: bf16 [T, H] (torch.bfloat16 or int16/uint16 bit patterns) -> fp32 [T, H]."""
+        import torch
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, self.cfg.hidden), dtype=torch.float32, device=self.device)
+        ws = self.workspace(T)
+        moe_layer_forward(self.cfg, T, x, self.gate_w, self.bias, self.arena, self.shared, out, topk_ids, topk_w, ws)
+        return out

@@ -1,0 +1,266 @@
+// C ABI of libmoe (declared in include/moe.h): host-side validation, the
+// workspace plan, and the dispatch of the kernels onto the caller's stream.
+// Nothing here allocates device memory, synchronizes, or reads device memory.
+#include "moe.h"
+
+#include <math.h>
+#include <stdio.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxTokens = 65536;
+constexpr int kMaxHidden = 8192;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
+
+moe_status check_cfg(const moe_config* c) {
+  if (!c) return MOE_EINVAL;
+  if (c->hidden <= 0 || c->ffn <= 0 || c->n_experts <= 0 || c->top_k <= 0) return MOE_EINVAL;
+  if (c->n_shared != 0 && c->n_shared != 1) return MOE_EUNSUPPORTED;
+  if (c->hidden % 256 != 0 || c->hidden > kMaxHidden) return MOE_EUNSUPPORTED;
+  if (c->ffn % 128 != 0 || c->ffn > 65536) return MOE_EUNSUPPORTED;
+  if (c->n_experts > 256) return MOE_EUNSUPPORTED;
+  if (c->top_k > 8 || c->top_k > c->n_experts) return MOE_EUNSUPPORTED;
+  if (!isfinite(c->routed_scale)) return MOE_EINVAL;
+  if (c->precision < MOE_PREC_AUTO || c->precision > MOE_PREC_BF16) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int resolve_precision(const moe_config* c, int T) {
+  if (c->precision != MOE_PREC_AUTO) return c->precision;
+  return (int64_t)T * c->top_k <= 16 * (int64_t)c->n_experts ? MOE_PREC_FP32 : MOE_PREC_BF16;
+}
+
+int64_t expert_bytes(const moe_config* c) { return 3 * (int64_t)c->ffn * (c->hidden / 32) * 18; }
+
+int max_chunks(const moe_config* c, int T) {
+  const int64_t R = (int64_t)T * c->top_k;
+  const int64_t nonempty = R < c->n_experts ? R : c->n_experts;
+  return (int)(R / 16 + nonempty + (c->n_shared ? (T + 15) / 16 : 0));
+}
+
+// Workspace plan: 256-byte aligned sub-buffers.
+struct Plan {
+  size_t scores, ids, w;                       // router
+  size_t counts, offsets, perm, pos, chunks, n_chunks;  // bucketing
+  size_t h_hi, h_lo, y;                        // exact-weight FFN
+  size_t total;
+};
+
+Plan make_plan(const moe_config* c, int T) {
+  const size_t R = (size_t)T * c->top_k, E = c->n_experts, S = c->n_shared ? (size_t)T : 0;
+  const size_t H = c->hidden, F = c->ffn;
+  Plan p;
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t here = at;
+    at += align_up(bytes > 0 ? bytes : 1);
+    return here;
+  };
+  p.scores = take((size_t)T * E * 4);
+  p.ids = take(R * 4);
+  p.w = take(R * 4);
+  p.counts = take(E * 4);
+  p.offsets = take((E + 1) * 4);
+  p.perm = take(R * 4);
+  p.pos = take(R * 4);
+  p.chunks = take((size_t)max_chunks(c, T) * sizeof(qmoe::Chunk));
+  p.n_chunks = take(4);
+  p.h_hi = take((R + S) * F * 2);
+  p.h_lo = take((R + S) * F * 2);
+  p.y = take((R + S) * H * 4);
+  p.total = at;
+  return p;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+moe_status check_common(const moe_config* cfg, int32_t T) {
+  const moe_status s = check_cfg(cfg);
+  if (s != MOE_OK) return s;
+  if (T < 0 || T > kMaxTokens) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status need(const void* p) {
+  if (!p) return MOE_EINVAL;
+  if (!aligned16(p)) return MOE_EALIGN;
+  return MOE_OK;
+}
+
+moe_status optional_ptr(const void* p) { return (p && !aligned16(p)) ? MOE_EALIGN : MOE_OK; }
+
+#define TRY(expr)                          \
+  do {                                     \
+    const moe_status _s = (expr);          \
+    if (_s != MOE_OK) return _s;           \
+  } while (0)
+
+moe_status launched(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  fprintf(stderr, "libmoe: launch failed: %s\n", hipGetErrorString(e));
+  return MOE_ELAUNCH;
+}
+
+// Expert FFN + combine after validation; ids and w are device pointers.
+moe_status run_expert_forward(const moe_config* cfg, int32_t T, const void* x, const int32_t* ids, const float* w,
+                              const void* arena, const void* shared, float* out, void* ws, hipStream_t stream) {
+  if (T == 0) return MOE_OK;
+  const Plan p = make_plan(cfg, T);
+  const int H = cfg->hidden, F = cfg->ffn, E = cfg->n_experts, K = cfg->top_k;
+  TRY(launched(qmoe::launch_bucket(ids, T, K, E, cfg->n_shared, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
+                                   at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), at<qmoe::Chunk>(ws, p.chunks),
+                                   at<int32_t>(ws, p.n_chunks), stream)));
+  const int prec = resolve_precision(cfg, T);
+  if (prec != MOE_PREC_FP32) return MOE_EUNSUPPORTED;
+  return launched(qmoe::launch_ffn_exact(
+      static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, max_chunks(cfg, T),
+      static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
+      at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks), at<int32_t>(ws, p.n_chunks),
+      at<uint16_t>(ws, p.h_hi), at<uint16_t>(ws, p.h_lo), at<float>(ws, p.y), out, stream));
+}
+
+}  // namespace
+
+MOE_API int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+MOE_API const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument (null pointer, bad size or shape)";
+    case MOE_EALIGN: return "device pointer not 16-byte aligned";
+    case MOE_EWORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+    case MOE_EUNSUPPORTED: return "unsupported configuration";
+    case MOE_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+MOE_API moe_status moe_check_config(const moe_config* cfg) { return check_cfg(cfg); }
+
+MOE_API size_t moe_expert_bytes(const moe_config* cfg) {
+  return check_cfg(cfg) == MOE_OK ? (size_t)expert_bytes(cfg) : 0;
+}
+
+MOE_API int32_t moe_resolved_precision(const moe_config* cfg, int32_t T) {
+  return check_cfg(cfg) == MOE_OK ? resolve_precision(cfg, T) : 0;
+}
+
+MOE_API size_t moe_workspace_bytes(const moe_config* cfg, int32_t T) {
+  if (check_common(cfg, T) != MOE_OK) return 0;
+  return make_plan(cfg, T).total;
+}
+
+MOE_API moe_status moe_pack_experts(const moe_config* cfg, int32_t n_experts, const void* src_dev, void* dst_dev,
+                                    hipStream_t stream) {
+  TRY(check_cfg(cfg));
+  if (n_experts < 0) return MOE_EINVAL;
+  if (n_experts == 0) return MOE_OK;
+  TRY(need(src_dev));
+  TRY(need(dst_dev));
+  const char* s = static_cast<const char*>(src_dev);
+  const char* d = static_cast<const char*>(dst_dev);
+  const int64_t bytes = (int64_t)n_experts * expert_bytes(cfg);
+  if (s < d + bytes && d < s + bytes) return MOE_EINVAL;  // overlap
+  return launched(qmoe::launch_pack(static_cast<const uint8_t*>(src_dev), static_cast<uint8_t*>(dst_dev), n_experts,
+                                    cfg->hidden, cfg->ffn, stream));
+}
+
+MOE_API moe_status moe_dequant(const moe_config* cfg, const void* packed_expert_dev, int32_t matrix, int32_t precision,
+                               float* out_dev, hipStream_t stream) {
+  TRY(check_cfg(cfg));
+  if (matrix < 0 || matrix > 2) return MOE_EINVAL;
+  if (precision != MOE_PREC_FP32 && precision != MOE_PREC_BF16) return MOE_EINVAL;
+  TRY(need(packed_expert_dev));
+  TRY(need(out_dev));
+  const int64_t mat_bytes = expert_bytes(cfg) / 3;
+  const int rows = matrix < 2 ? cfg->ffn : cfg->hidden;
+  const int cols = matrix < 2 ? cfg->hidden : cfg->ffn;
+  return launched(qmoe::launch_dequant(static_cast<const uint8_t*>(packed_expert_dev) + matrix * mat_bytes, rows,
+                                       cols, precision == MOE_PREC_BF16 ? 1 : 0, out_dev, stream));
+}
+
+MOE_API moe_status moe_route(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
+                             const float* sel_bias_dev, int32_t* topk_ids_dev, float* topk_w_dev, void* ws_dev,
+                             size_t ws_bytes, hipStream_t stream) {
+  TRY(check_common(cfg, T));
+  if (T == 0) return MOE_OK;  // nothing to read or write
+  TRY(need(x_dev));
+  TRY(need(gate_w_dev));
+  TRY(optional_ptr(sel_bias_dev));
+  TRY(need(topk_ids_dev));
+  TRY(need(topk_w_dev));
+  TRY(need(ws_dev));
+  const Plan p = make_plan(cfg, T);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  return launched(qmoe::launch_router(static_cast<const uint16_t*>(x_dev), gate_w_dev, sel_bias_dev, T, cfg->hidden,
+                                      cfg->n_experts, cfg->top_k, cfg->routed_scale, at<float>(ws_dev, p.scores),
+                                      topk_ids_dev, topk_w_dev, stream));
+}
+
+MOE_API moe_status moe_bucket(const moe_config* cfg, int32_t T, const int32_t* topk_ids_dev, int32_t* counts_dev,
+                              int32_t* offsets_dev, int32_t* perm_dev, int32_t* pos_dev, hipStream_t stream) {
+  TRY(check_common(cfg, T));
+  TRY(need(counts_dev));
+  TRY(need(offsets_dev));
+  if (T > 0) {  // with no routes only the (all-zero) counts and offsets are written
+    TRY(need(topk_ids_dev));
+    TRY(need(perm_dev));
+    TRY(optional_ptr(pos_dev));
+  }
+  return launched(qmoe::launch_bucket(topk_ids_dev, T, cfg->top_k, cfg->n_experts, cfg->n_shared, counts_dev,
+                                      offsets_dev, perm_dev, pos_dev, nullptr, nullptr, stream));
+}
+
+MOE_API moe_status moe_expert_forward(const moe_config* cfg, int32_t T, const void* x_dev, const int32_t* topk_ids_dev,
+                                      const float* topk_w_dev, const void* arena_dev, const void* shared_dev,
+                                      float* out_dev, void* ws_dev, size_t ws_bytes, hipStream_t stream) {
+  TRY(check_common(cfg, T));
+  if (T == 0) return MOE_OK;  // nothing to read or write
+  TRY(need(x_dev));
+  TRY(need(topk_ids_dev));
+  TRY(need(topk_w_dev));
+  TRY(need(arena_dev));
+  if (cfg->n_shared) TRY(need(shared_dev));
+  TRY(need(out_dev));
+  TRY(need(ws_dev));
+  if (ws_bytes < make_plan(cfg, T).total) return MOE_EWORKSPACE;
+  return run_expert_forward(cfg, T, x_dev, topk_ids_dev, topk_w_dev, arena_dev, shared_dev, out_dev, ws_dev, stream);
+}
+
+MOE_API moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
+                                     const float* sel_bias_dev, const void* arena_dev, const void* shared_dev,
+                                     float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
+                                     size_t ws_bytes, hipStream_t stream) {
+  TRY(check_common(cfg, T));
+  if (T == 0) return MOE_OK;  // nothing to read or write
+  TRY(need(x_dev));
+  TRY(need(gate_w_dev));
+  TRY(optional_ptr(sel_bias_dev));
+  TRY(need(arena_dev));
+  if (cfg->n_shared) TRY(need(shared_dev));
+  TRY(need(out_dev));
+  TRY(optional_ptr(topk_ids_out_dev));
+  TRY(optional_ptr(topk_w_out_dev));
+  TRY(need(ws_dev));
+  const Plan p = make_plan(cfg, T);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  if (T == 0) return MOE_OK;
+  int32_t* ids = topk_ids_out_dev ? topk_ids_out_dev : at<int32_t>(ws_dev, p.ids);
+  float* w = topk_w_out_dev ? topk_w_out_dev : at<float>(ws_dev, p.w);
+  TRY(launched(qmoe::launch_router(static_cast<const uint16_t*>(x_dev), gate_w_dev, sel_bias_dev, T, cfg->hidden,
+                                   cfg->n_experts, cfg->top_k, cfg->routed_scale, at<float>(ws_dev, p.scores), ids, w,
+                                   stream)));
+  return run_expert_forward(cfg, T, x_dev, ids, w, arena_dev, shared_dev, out_dev, ws_dev, stream);
+}

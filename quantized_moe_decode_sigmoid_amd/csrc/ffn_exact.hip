@@ -1,0 +1,361 @@
+// Expert FFN with exact IQ4_NL weights (the decode / small-batch path).
+//
+// The FFN is the gated MLP y = W_down(silu(W_gate x) * (W_up x)) (zLLM
+// "Algorithm Layer", FFN section), silu(g) * u handed to the down projection
+// in fp32 and the routed + shared sum formed in fp32 (PocketLLM design record,
+// section 2).
+//
+// Work is a list of chunks, each up to 16 routes of one expert (or up to 16
+// tokens of the shared expert), produced by the bucketing pass: an expert's
+// weights are streamed once per chunk, not once per route.  Every 16x32
+// weight fragment (16 rows, one 32-weight block) is one v_mfma_f32_16x16x32_bf16
+// against the chunk's 16 activation columns:
+//   A = the block's levels (exact in bf16, decoded two at a time from LDS),
+//   B = the activations (bf16) -- or, for the down projection, the fp32
+//       product h split exactly enough as h_hi + h_lo (two bf16, two MFMAs),
+//   then acc += d * C with the block's fp16 scale d, in fp32.
+// So the weights are the exact values d*level; products of levels and bf16
+// activations are exact; only fp32 accumulation rounds.
+//
+// Memory: a packed tile (16 rows x 4 blocks, 1152 bytes) is read by one
+// wavefront with one 16-byte load per lane for the nibbles and two for the
+// scales, fully coalesced.  Each workgroup (4 waves) owns one (chunk, 16-row
+// tile) and splits the reduction dimension over its waves; partial results are
+// added in wave order through LDS, so results are deterministic.
+#include "device.h"
+#include "launch.h"
+
+namespace qmoe {
+
+constexpr int kFfnThreads = 256;
+
+// ---------------------------------------------------------------- packing
+
+// One thread per 16-byte lane slot of a tile.  src: GGUF order, rows of
+// NB = cols/32 blocks of 18 bytes.  Threads with slot < 16 also place the
+// four scales of (rows 4G..4G+3, block b), G = slot/4, b = slot%4.
+__global__ void k_pack(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n_tiles_total,
+                       int rows, int nb, int64_t matrix_bytes) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t tile = gid >> 6;
+  const int slot = (int)(gid & 63);
+  if (tile >= n_tiles_total) return;
+  const int nkg = nb >> 2;
+  const int64_t tiles_per_matrix = (int64_t)(rows >> 4) * nkg;
+  const int64_t mat = tile / tiles_per_matrix;
+  const int64_t tin = tile % tiles_per_matrix;
+  const int rt = (int)(tin / nkg), kg = (int)(tin % nkg);
+  const uint8_t* m_src = src + mat * matrix_bytes;
+  uint8_t* t_dst = dst + mat * matrix_bytes + tin * kTileBytes;
+  {
+    const int row = 16 * rt + (slot & 15), w = slot >> 4;
+    uint8_t out[16];
+    for (int b = 0; b < 4; b++) {
+      const uint8_t* blk = m_src + ((int64_t)row * nb + 4 * kg + b) * 18;
+      for (int i = 0; i < 4; i++) out[4 * b + i] = blk[2 + 4 * w + i];
+    }
+    uint4 v;
+    __builtin_memcpy(&v, out, 16);
+    *reinterpret_cast<uint4*>(t_dst + 16 * slot) = v;
+  }
+  if (slot < 16) {
+    const int G = slot >> 2, b = slot & 3;
+    uint8_t out[8];
+    for (int i = 0; i < 4; i++) {
+      const uint8_t* blk = m_src + ((int64_t)(16 * rt + 4 * G + i) * nb + 4 * kg + b) * 18;
+      out[2 * i] = blk[0];
+      out[2 * i + 1] = blk[1];
+    }
+    uint2 v;
+    __builtin_memcpy(&v, out, 8);
+    *reinterpret_cast<uint2*>(t_dst + kTileNibbleBytes + 32 * G + 8 * b) = v;
+  }
+}
+
+// ---------------------------------------------------------------- dequant
+
+// One wavefront per tile; writes the 16 x 128 weights of the tile.
+// bf16 = 0: exact d*level in fp32; bf16 = 1: that value rounded to bf16.
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat, int rows, int cols, int bf16,
+                                                 float* __restrict__ out) {
+  __shared__ uint32_t tbl[kPairTableWords];
+  build_pair_table(tbl);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int nkg = cols >> 7;
+  const int64_t tile = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= (int64_t)(rows >> 4) * nkg) return;
+  const int rt = (int)(tile / nkg), kg = (int)(tile % nkg);
+  const uint8_t* t = mat + tile * kTileBytes;
+  const uint4 nib = *reinterpret_cast<const uint4*>(t + 16 * lane);
+  const int r = lane & 15, w = lane >> 4;
+  const int row = 16 * rt + r;
+  const uint32_t words[4] = {nib.x, nib.y, nib.z, nib.w};
+  for (int b = 0; b < 4; b++) {
+    // the scale of (row, block 4kg+b): G = r/4, i = r%4
+    const uint16_t dh = *reinterpret_cast<const uint16_t*>(t + kTileNibbleBytes + 32 * (r >> 2) + 8 * b + 2 * (r & 3));
+    const float d = half_bits_to_float(dh);
+    union {
+      bf16x8 v;
+      uint32_t u[4];
+    } a;
+    a.v = decode_word(tbl, words[b], lane & 31);
+    float* o = out + (size_t)row * cols + 32 * (4 * kg + b);
+    for (int i = 0; i < 4; i++) {
+      float lo = d * bf16_bits_to_f32(a.u[i] & 0xffffu);
+      float hi = d * bf16_bits_to_f32(a.u[i] >> 16);
+      if (bf16) {
+        lo = bf16_bits_to_f32(f32_to_bf16_rne(lo));
+        hi = bf16_bits_to_f32(f32_to_bf16_rne(hi));
+      }
+      o[4 * w + i] = lo;
+      o[16 + 4 * w + i] = hi;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- shared pieces
+
+struct TileScales {
+  uint32_t s[8];  // fp16 pairs: block b -> s[2b] (rows 4G, 4G+1), s[2b+1] (rows 4G+2, 4G+3)
+};
+
+__device__ __forceinline__ TileScales load_scales(const uint8_t* tile, int G) {
+  const uint4 a = *reinterpret_cast<const uint4*>(tile + kTileNibbleBytes + 32 * G);
+  const uint4 b = *reinterpret_cast<const uint4*>(tile + kTileNibbleBytes + 32 * G + 16);
+  TileScales t;
+  t.s[0] = a.x;
+  t.s[1] = a.y;
+  t.s[2] = a.z;
+  t.s[3] = a.w;
+  t.s[4] = b.x;
+  t.s[5] = b.y;
+  t.s[6] = b.z;
+  t.s[7] = b.w;
+  return t;
+}
+
+// acc[i] += d(row 4G+i, block b) * c[i]
+__device__ __forceinline__ void scale_acc(f32x4& acc, const f32x4& c, const TileScales& sc, int b) {
+  const uint32_t p = sc.s[2 * b], q = sc.s[2 * b + 1];
+  acc[0] = __builtin_fmaf(half_bits_to_float(p), c[0], acc[0]);
+  acc[1] = __builtin_fmaf(half_bits_to_float(p >> 16), c[1], acc[1]);
+  acc[2] = __builtin_fmaf(half_bits_to_float(q), c[2], acc[2]);
+  acc[3] = __builtin_fmaf(half_bits_to_float(q >> 16), c[3], acc[3]);
+}
+
+__device__ __forceinline__ uint32_t uword(const uint4& v, int b) {
+  return b == 0 ? v.x : (b == 1 ? v.y : (b == 2 ? v.z : v.w));
+}
+
+// ---------------------------------------------------------------- gate / up
+
+// Workgroup = (chunk, 16-row tile of F).  Output: the product h = silu(g)*u of
+// route column c, row f, as two bf16 halves h_hi = bf16(h), h_lo = bf16(h -
+// h_hi), stored in the operand order of the down projection: element f of a
+// row sits at 32*(f/32) + 2*(f%16) + (f%32 >= 16).
+__global__ __launch_bounds__(kFfnThreads) void k_gate_up_exact(
+    const uint16_t* __restrict__ x, int H, int F, int K, int T, const uint8_t* __restrict__ arena,
+    const uint8_t* __restrict__ shared, int64_t expert_bytes, const int32_t* __restrict__ perm,
+    const Chunk* __restrict__ chunks, const int32_t* __restrict__ n_chunks, uint16_t* __restrict__ h_hi,
+    uint16_t* __restrict__ h_lo) {
+  __shared__ uint32_t tbl[kPairTableWords];
+  __shared__ f32x4 red[2][4][64];
+  const int n_rt = F >> 4;
+  const int chunk_id = blockIdx.x / n_rt;
+  const int rt = blockIdx.x % n_rt;
+  if (chunk_id >= *n_chunks) return;
+  build_pair_table(tbl);
+  const Chunk ch = chunks[chunk_id];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, G = lane >> 4;
+  const int64_t mat_bytes = expert_bytes / 3;
+  const uint8_t* ex = ch.expert >= 0 ? arena + (int64_t)ch.expert * expert_bytes : shared;
+  const int TK = T * K;
+  int tok = -1;
+  if (c < ch.count) tok = ch.expert >= 0 ? perm[ch.first + c] / K : ch.first + c;
+  const uint16_t* xr = x + (size_t)(tok >= 0 ? tok : 0) * H;
+  const int nkg = H >> 7;
+  const int kg0 = (wave * nkg) >> 2, kg1 = ((wave + 1) * nkg) >> 2;
+  const uint8_t* gate_t = ex + (int64_t)rt * nkg * kTileBytes;
+  const uint8_t* up_t = ex + mat_bytes + (int64_t)rt * nkg * kTileBytes;
+  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  for (int kg = kg0; kg < kg1; kg++) {
+    const uint8_t* tg = gate_t + (int64_t)kg * kTileBytes;
+    const uint8_t* tu = up_t + (int64_t)kg * kTileBytes;
+    const uint4 ng = *reinterpret_cast<const uint4*>(tg + 16 * lane);
+    const uint4 nu = *reinterpret_cast<const uint4*>(tu + 16 * lane);
+    const TileScales sg = load_scales(tg, G);
+    const TileScales su = load_scales(tu, G);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const bf16x8 xb = tok >= 0 ? load_x_operand(xr, 4 * kg + b, G) : zero_operand();
+      const f32x4 cg = mfma16x16x32(decode_word(tbl, uword(ng, b), lane & 31), xb, zero);
+      const f32x4 cu = mfma16x16x32(decode_word(tbl, uword(nu, b), lane & 31), xb, zero);
+      scale_acc(accg, cg, sg, b);
+      scale_acc(accu, cu, su, b);
+    }
+  }
+  red[0][wave][lane] = accg;
+  red[1][wave][lane] = accu;
+  __syncthreads();
+  if (wave != 0 || tok < 0) return;
+  f32x4 g = red[0][0][lane], u = red[1][0][lane];
+  for (int w = 1; w < 4; w++) {
+    g += red[0][w][lane];
+    u += red[1][w][lane];
+  }
+  const int64_t hrow = ch.expert >= 0 ? (int64_t)(ch.first + c) : (int64_t)TK + tok;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int f = 16 * rt + 4 * G + i;
+    const float gv = g[i];
+    const float h = gv / (1.0f + expf(-gv)) * u[i];
+    const uint32_t hb = f32_to_bf16_rne(h);
+    const uint32_t lb = f32_to_bf16_rne(h - bf16_bits_to_f32(hb));
+    const int64_t at = hrow * F + 32 * (f >> 5) + 2 * (f & 15) + ((f >> 4) & 1);
+    h_hi[at] = (uint16_t)hb;
+    h_lo[at] = (uint16_t)lb;
+  }
+}
+
+// ---------------------------------------------------------------- down
+
+// Workgroup = (chunk, 16-row tile of H).  y[hrow][n] = sum_f W_down[n][f] h[f]
+// in fp32, one row per route (bucketed position) or per shared-expert token.
+__global__ __launch_bounds__(kFfnThreads) void k_down_exact(
+    int H, int F, int K, int T, const uint8_t* __restrict__ arena, const uint8_t* __restrict__ shared,
+    int64_t expert_bytes, const Chunk* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
+    const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, float* __restrict__ y) {
+  __shared__ uint32_t tbl[kPairTableWords];
+  __shared__ f32x4 red[4][64];
+  const int n_rt = H >> 4;
+  const int chunk_id = blockIdx.x / n_rt;
+  const int rt = blockIdx.x % n_rt;
+  if (chunk_id >= *n_chunks) return;
+  build_pair_table(tbl);
+  const Chunk ch = chunks[chunk_id];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, G = lane >> 4;
+  const int64_t mat_bytes = expert_bytes / 3;
+  const uint8_t* ex = ch.expert >= 0 ? arena + (int64_t)ch.expert * expert_bytes : shared;
+  const int TK = T * K;
+  const bool live = c < ch.count;
+  const int64_t hrow = ch.expert >= 0 ? (int64_t)(ch.first + c) : (int64_t)TK + ch.first + c;
+  const uint16_t* hh = h_hi + (live ? hrow : 0) * F;
+  const uint16_t* hl = h_lo + (live ? hrow : 0) * F;
+  const int nkg = F >> 7;
+  const int kg0 = (wave * nkg) >> 2, kg1 = ((wave + 1) * nkg) >> 2;
+  const uint8_t* down_t = ex + 2 * mat_bytes + (int64_t)rt * nkg * kTileBytes;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  for (int kg = kg0; kg < kg1; kg++) {
+    const uint8_t* td = down_t + (int64_t)kg * kTileBytes;
+    const uint4 nd = *reinterpret_cast<const uint4*>(td + 16 * lane);
+    const TileScales sd = load_scales(td, G);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int blk = 4 * kg + b;
+      bf16x8 bh = zero_operand(), bl = zero_operand();
+      if (live) {
+        bh = *reinterpret_cast<const bf16x8*>(hh + 32 * blk + 8 * G);
+        bl = *reinterpret_cast<const bf16x8*>(hl + 32 * blk + 8 * G);
+      }
+      const bf16x8 a = decode_word(tbl, uword(nd, b), lane & 31);
+      f32x4 cc = mfma16x16x32(a, bh, zero);
+      cc = mfma16x16x32(a, bl, cc);
+      scale_acc(acc, cc, sd, b);
+    }
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave != 0 || !live) return;
+  f32x4 s = red[0][lane];
+  for (int w = 1; w < 4; w++) s += red[w][lane];
+  *reinterpret_cast<f32x4*>(y + hrow * H + 16 * rt + 4 * G) = s;
+}
+
+// ---------------------------------------------------------------- combine
+
+// out[t][n] = sum_k w[t][k] * y[pos[t*K+k]][n]  (slot order)  + y[TK + t][n]
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const int32_t* __restrict__ pos,
+                                                 const float* __restrict__ w, int T, int K, int H, int n_shared,
+                                                 float* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int n = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+  if (n >= H) return;
+  const int TK = T * K;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < K; k++) {
+    const float wk = w[(size_t)t * K + k];
+    const float4 v = *reinterpret_cast<const float4*>(y + (size_t)pos[(size_t)t * K + k] * H + n);
+    acc.x = __builtin_fmaf(wk, v.x, acc.x);
+    acc.y = __builtin_fmaf(wk, v.y, acc.y);
+    acc.z = __builtin_fmaf(wk, v.z, acc.z);
+    acc.w = __builtin_fmaf(wk, v.w, acc.w);
+  }
+  if (n_shared) {
+    const float4 v = *reinterpret_cast<const float4*>(y + ((size_t)TK + t) * H + n);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *reinterpret_cast<float4*>(out + (size_t)t * H + n) = acc;
+}
+
+// ---------------------------------------------------------------- launchers
+
+hipError_t launch_pack(const uint8_t* src, uint8_t* dst, int n_experts, int H, int F, hipStream_t stream) {
+  const int64_t mat_bytes = (int64_t)F * (H / 32) * 18;
+  // gate and up: F rows x H/32 blocks; down: H rows x F/32 blocks.  The two
+  // shapes differ, so launch per matrix kind with a matrix stride of 3.
+  for (int m = 0; m < 3; m++) {
+    const int rows = m < 2 ? F : H;
+    const int nb = m < 2 ? H / 32 : F / 32;
+    const int64_t tiles = (int64_t)(rows / 16) * (nb / 4);
+    for (int e = 0; e < n_experts; e++) {
+      const int64_t off = (int64_t)e * 3 * mat_bytes + m * mat_bytes;
+      const int64_t threads = tiles * 64;
+      clear_last_error();
+      hipLaunchKernelGGL(k_pack, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, src + off, dst + off,
+                         tiles, rows, nb, mat_bytes);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_dequant(const uint8_t* mat, int rows, int cols, int bf16, float* out, hipStream_t stream) {
+  const int64_t tiles = (int64_t)(rows / 16) * (cols / 128);
+  clear_last_error();
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, stream, mat, rows, cols, bf16, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_chunks,
+                            const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
+                            const int32_t* pos, const float* w, const Chunk* chunks, const int32_t* n_chunks,
+                            uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  clear_last_error();
+  hipLaunchKernelGGL(k_gate_up_exact, dim3((unsigned)(max_chunks * (F / 16))), dim3(kFfnThreads), 0, stream, x, H, F,
+                     K, T, arena, shared, expert_bytes, perm, chunks, n_chunks, h_hi, h_lo);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  clear_last_error();
+  hipLaunchKernelGGL(k_down_exact, dim3((unsigned)(max_chunks * (H / 16))), dim3(kFfnThreads), 0, stream, H, F, K, T,
+                     arena, shared, expert_bytes, chunks, n_chunks, h_hi, h_lo, y);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  clear_last_error();
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)T), dim3(256), 0, stream, y, pos, w, T,
+                     K, H, n_shared, out);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

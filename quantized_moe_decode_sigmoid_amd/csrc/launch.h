@@ -1,0 +1,26 @@
+// Host-side launchers of the libmoe kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.h"
+
+namespace qmoe {
+
+hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
+                         float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream);
+
+hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int n_shared, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, int32_t* pos, Chunk* chunks, int32_t* n_chunks, hipStream_t stream);
+
+hipError_t launch_pack(const uint8_t* src, uint8_t* dst, int n_experts, int H, int F, hipStream_t stream);
+
+hipError_t launch_dequant(const uint8_t* mat, int rows, int cols, int bf16, float* out, hipStream_t stream);
+
+hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_chunks,
+                            const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
+                            const int32_t* pos, const float* w, const Chunk* chunks, const int32_t* n_chunks,
+                            uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream);
+
+}  // namespace qmoe

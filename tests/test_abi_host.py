@@ -1,0 +1,144 @@
+"""Host-side checks of the C ABI (no GPU needed: validation runs before any launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_moe_decode_sigmoid_amd as qm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+XING4 = dict(hidden=3584, ffn=1024, n_experts=64, top_k=4, n_shared=1, routed_scale=2.0)
+A = 0x10000  # fake, 16-byte aligned device addresses: never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert names == sorted(qm.EXPORTED)
+    lib = ctypes.CDLL(qm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_exports_nothing_else():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", qm.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if l.split()[1] == "T"})
+    assert exported == declared_functions()
+
+
+def test_version_and_status_strings():
+    assert qm.moe_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(qm.status_string(s), str) and qm.status_string(s)
+
+
+def test_sizes_and_precision_rule():
+    cfg = qm.make_config(**XING4)
+    assert qm.moe_check_config(cfg) == 0
+    assert qm.moe_expert_bytes(cfg) == 6193152  # the model card's per-expert figure
+    assert qm.moe_resolved_precision(cfg, 1) == qm.PREC_FP32
+    assert qm.moe_resolved_precision(cfg, 128) == qm.PREC_FP32   # 512 routes <= 16 * 64
+    assert qm.moe_resolved_precision(cfg, 257) == qm.PREC_BF16
+    pre = qm.make_config(2048, 512, 256, 8)
+    assert qm.moe_expert_bytes(pre) == 1769472
+    assert qm.moe_resolved_precision(pre, 2048) == qm.PREC_BF16
+    assert qm.moe_workspace_bytes(cfg, 1) > 0
+    assert qm.moe_workspace_bytes(cfg, 128) > qm.moe_workspace_bytes(cfg, 1)
+    assert qm.moe_workspace_bytes(cfg, 0) > 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(hidden=3584 + 64), qm.MOE_EUNSUPPORTED),
+    (dict(hidden=0), qm.MOE_EINVAL),
+    (dict(ffn=1000), qm.MOE_EUNSUPPORTED),
+    (dict(n_experts=300), qm.MOE_EUNSUPPORTED),
+    (dict(top_k=9), qm.MOE_EUNSUPPORTED),
+    (dict(n_experts=2, top_k=3), qm.MOE_EUNSUPPORTED),
+    (dict(n_shared=2), qm.MOE_EUNSUPPORTED),
+    (dict(routed_scale=float("nan")), qm.MOE_EINVAL),
+    (dict(precision=5), qm.MOE_EINVAL),
+])
+def test_bad_configs_are_refused(bad, code):
+    cfg = qm.make_config(**{**XING4, **bad})
+    assert qm.moe_check_config(cfg) == code
+    assert qm.moe_expert_bytes(cfg) == 0
+    assert qm.moe_workspace_bytes(cfg, 1) == 0
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_route(cfg, 1, A, A, None, A, A, A, ws_bytes=1 << 30, stream=0)
+    assert ei.value.status == code
+
+
+def test_route_argument_errors():
+    cfg = qm.make_config(**XING4)
+    ws = qm.moe_workspace_bytes(cfg, 4)
+
+    def call(T=4, x=A, g=A, b=None, ids=A, w=A, wsp=A, wsb=ws):
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_route(cfg, T, x, g, b, ids, w, wsp, ws_bytes=wsb, stream=0)
+        return ei.value.status
+
+    assert call(T=-1) == qm.MOE_EUNSUPPORTED
+    assert call(T=70000) == qm.MOE_EUNSUPPORTED
+    assert call(x=None) == qm.MOE_EINVAL
+    assert call(g=None) == qm.MOE_EINVAL
+    assert call(ids=None) == qm.MOE_EINVAL
+    assert call(w=None) == qm.MOE_EINVAL
+    assert call(wsp=None) == qm.MOE_EINVAL
+    assert call(x=A + 2) == qm.MOE_EALIGN          # an offset view: the research log's float4 lesson
+    assert call(g=A + 4) == qm.MOE_EALIGN
+    assert call(b=A + 8) == qm.MOE_EALIGN
+    assert call(wsp=A + 8) == qm.MOE_EALIGN
+    assert call(wsb=ws - 1) == qm.MOE_EWORKSPACE
+
+
+def test_expert_forward_and_layer_argument_errors():
+    cfg = qm.make_config(**XING4)
+    ws = qm.moe_workspace_bytes(cfg, 3)
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_expert_forward(cfg, 3, A, A, A, A, None, A, A, ws_bytes=ws, stream=0)  # shared expert missing
+    assert ei.value.status == qm.MOE_EINVAL
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_expert_forward(cfg, 3, A, A, A, A + 1, A, A, A, ws_bytes=ws, stream=0)
+    assert ei.value.status == qm.MOE_EALIGN
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_expert_forward(cfg, 3, A, A, A, A, A, A, A, ws_bytes=16, stream=0)
+    assert ei.value.status == qm.MOE_EWORKSPACE
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_layer_forward(cfg, 3, A, A, None, A, A, A, A + 4, None, ws=A, ws_bytes=ws, stream=0)
+    assert ei.value.status == qm.MOE_EALIGN
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_layer_forward(cfg, 3, A, A, None, A, A, None, None, None, ws=A, ws_bytes=ws, stream=0)
+    assert ei.value.status == qm.MOE_EINVAL
+
+
+def test_bucket_pack_dequant_argument_errors():
+    cfg = qm.make_config(**XING4)
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_bucket(cfg, 2, A, A, A, None, stream=0)
+    assert ei.value.status == qm.MOE_EINVAL
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_pack_experts(cfg, 2, A, A + 1024, stream=0)  # overlapping ranges
+    assert ei.value.status == qm.MOE_EINVAL
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_pack_experts(cfg, -1, A, A, stream=0)
+    assert ei.value.status == qm.MOE_EINVAL
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_dequant(cfg, A, 3, qm.PREC_FP32, A, stream=0)
+    assert ei.value.status == qm.MOE_EINVAL
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_dequant(cfg, A, 0, qm.PREC_AUTO, A, stream=0)
+    assert ei.value.status == qm.MOE_EINVAL
+
+
+def test_zero_sized_calls_enqueue_nothing():
+    cfg = qm.make_config(**XING4)
+    qm.moe_pack_experts(cfg, 0, A, A + (1 << 24), stream=0)  # no work, no launch

@@ -1,0 +1,199 @@
+"""GPU parity: every step of the layer, run through the C ABI, against the CPU oracle.
+
+Integer work (routing ids, bucketing, the dequantized weights) must match bit for bit;
+the routing weights too (same fp32 operations in the same order); the FP output must
+match within max-abs 2e-2 and rel-L2 1e-3 of the oracle in the matching precision mode.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import assert_close, cfg_of, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+import quantized_moe_decode_sigmoid_amd as qm  # noqa: E402
+
+_CACHE = {}
+
+
+def workload(name, layer=0):
+    key = (name, layer)
+    if key not in _CACHE:
+        s = synth.WORKLOADS[name]
+        _CACHE[key] = (s, synth.layer_inputs(s, layer=layer))
+    return _CACHE[key]
+
+
+def device_layer(name, precision=qm.PREC_AUTO, bias=None):
+    s, inp = workload(name)
+    cfg = cfg_of(s, precision)
+    return s, inp, qm.DeviceLayer(cfg, inp["gate_w"], bias, inp["arena"], inp["shared"])
+
+
+def log(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------- dequant (bit-exact)
+
+@pytest.mark.parametrize("name", ["tiny", "xing4", "prefill"])
+@pytest.mark.parametrize("precision", [qm.PREC_FP32, qm.PREC_BF16])
+def test_dequant_bit_exact(name, precision):
+    s, inp, dl = device_layer(name)
+    eb = s.expert_bytes
+    mb = eb // 3
+    for e in (0, s.n_experts - 1):
+        for m, (rows, cols) in enumerate([(s.ffn, s.hidden), (s.ffn, s.hidden), (s.hidden, s.ffn)]):
+            log(f"dequant {name} expert={e} matrix={m} precision={precision}")
+            out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+            qm.moe_dequant(dl.cfg, dl.arena[e * eb:(e + 1) * eb], m, precision, out)
+            want = oracle.dequant(inp["arena"][e * eb + m * mb: e * eb + (m + 1) * mb],
+                                  oracle.BF16 if precision == qm.PREC_BF16 else oracle.FP32).reshape(rows, cols)
+            got = out.cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), (name, e, m)
+
+
+# ---------------------------------------------------------------- router (bit-exact)
+
+def run_route(dl, x_bits, bias_dev=None):
+    T = x_bits.shape[0]
+    cfg = dl.cfg
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    qm.moe_route(cfg, T, to_dev_bf16(x_bits), dl.gate_w, bias_dev, ids, w, ws)
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 1), ("xing4", 64), ("batch", 128), ("prefill", 300)])
+def test_route_bit_exact(name, T):
+    s, inp, dl = device_layer(name)
+    x = synth.tokens(s, T, first=1000)
+    log(f"route {name} T={T}")
+    ids, w = run_route(dl, x)
+    rid, rw, _, _ = oracle.route(x, inp["gate_w"], s.top_k, s.routed_scale)
+    assert np.array_equal(ids, rid)
+    assert np.array_equal(w.view(np.uint32), rw.view(np.uint32))
+
+
+def test_route_with_selection_bias_bit_exact():
+    s, inp, dl = device_layer("prefill")
+    bias = synth.zipf_bias(s, 0.05)
+    x = synth.tokens(s, 257, first=7)
+    log("route prefill with zipf bias T=257")
+    ids, w = run_route(dl, x, torch.from_numpy(bias).cuda())
+    rid, rw, _, _ = oracle.route(x, inp["gate_w"], s.top_k, s.routed_scale, bias)
+    assert np.array_equal(ids, rid)
+    assert np.array_equal(w.view(np.uint32), rw.view(np.uint32))
+
+
+# ---------------------------------------------------------------- bucketing (bit-exact)
+
+@pytest.mark.parametrize("T,K,E", [(4, 2, 8), (1, 4, 64), (128, 4, 64), (2048, 8, 256), (1000, 3, 5), (0, 4, 64)])
+def test_bucket_bit_exact(T, K, E):
+    rng = np.random.default_rng(T * 7 + K)
+    ids = np.array([rng.choice(E, K, replace=False) for _ in range(T)], np.int32).reshape(T, K)
+    cfg = qm.make_config(256, 128, E, K)
+    log(f"bucket T={T} K={K} E={E}")
+    dids = torch.from_numpy(ids).cuda()
+    counts = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + 1,), -1, dtype=torch.int32, device="cuda")
+    perm = torch.full((max(T * K, 1),), -1, dtype=torch.int32, device="cuda")
+    pos = torch.full((max(T * K, 1),), -1, dtype=torch.int32, device="cuda")
+    qm.moe_bucket(cfg, T, dids, counts, offsets, perm, pos)
+    rc, ro, rp, rpos = oracle.bucket(ids, E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy()[:T * K], rp)
+    assert np.array_equal(pos.cpu().numpy()[:T * K], rpos)
+
+
+# ---------------------------------------------------------------- the whole layer (FP tolerance)
+
+def layer_parity(name, T, first=0, sample=None, bias=None, precision=qm.PREC_AUTO):
+    s, inp, dl = device_layer(name, precision, bias)
+    x = synth.tokens(s, T, first=first)
+    cfg = dl.cfg
+    prec = qm.moe_resolved_precision(cfg, T)
+    log(f"layer {name} T={T} precision={prec}")
+    ids = torch.empty((T, s.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.top_k), dtype=torch.float32, device="cuda")
+    out = dl.forward(to_dev_bf16(x), topk_ids=ids, topk_w=w).cpu().numpy()
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    mode = oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32
+    ref, rid, rw = oracle.layer(x[rows], inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn,
+                                s.routed_scale, bias, mode)
+    assert np.array_equal(ids.cpu().numpy()[rows], rid)
+    assert np.array_equal(w.cpu().numpy()[rows].view(np.uint32), rw.view(np.uint32))
+    assert_close(out[rows], ref, f"{name} T={T} rows={len(rows)}")
+    return out
+
+
+def test_layer_tiny():
+    layer_parity("tiny", 4)
+
+
+def test_layer_tiny_ragged_and_single():
+    layer_parity("tiny", 1, first=11)
+    layer_parity("tiny", 37, first=20)
+
+
+def test_layer_xing4_decode_tokens():
+    for i in range(3):
+        layer_parity("xing4", 1, first=500 + i)
+
+
+def test_layer_xing4_small_batch():
+    layer_parity("xing4", 5, first=40)
+
+
+def test_layer_batch_128_sampled():
+    layer_parity("batch", 128, sample=[0, 1, 17, 63, 64, 100, 127])
+
+
+def test_layer_many_routes_on_one_expert():
+    """A selection bias that sends every token to experts 0..K-1: chunks of 16 per expert, ragged tail."""
+    s, _ = workload("tiny")
+    bias = np.zeros(s.n_experts, np.float32)
+    bias[:s.top_k] = 10.0
+    layer_parity("tiny", 45, first=3, bias=bias)
+
+
+def test_layer_zero_tokens_is_a_no_op():
+    s, inp, dl = device_layer("tiny")
+    log("layer tiny T=0")
+    out = torch.empty((0, s.hidden), dtype=torch.float32, device="cuda")
+    x = torch.empty((0, s.hidden), dtype=torch.bfloat16, device="cuda")
+    dl.forward(x, out=out)
+    torch.cuda.synchronize()
+
+
+def test_layer_is_deterministic_and_token_order_equivariant():
+    s, inp, dl = device_layer("xing4")
+    x = synth.tokens(s, 24, first=77)
+    log("determinism xing4 T=24")
+    a = dl.forward(to_dev_bf16(x)).cpu().numpy()
+    b = dl.forward(to_dev_bf16(x)).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    perm = np.random.default_rng(5).permutation(24)
+    c = dl.forward(to_dev_bf16(x[perm])).cpu().numpy()
+    assert np.array_equal(a[perm].view(np.uint32), c.view(np.uint32))
+
+
+def test_expert_forward_matches_layer_forward():
+    s, inp, dl = device_layer("tiny")
+    x = synth.tokens(s, 9, first=50)
+    log("expert_forward tiny T=9")
+    xd = to_dev_bf16(x)
+    rid, rw, _, _ = oracle.route(x, inp["gate_w"], s.top_k, s.routed_scale)
+    out = torch.empty((9, s.hidden), dtype=torch.float32, device="cuda")
+    qm.moe_expert_forward(dl.cfg, 9, xd, torch.from_numpy(rid).cuda(), torch.from_numpy(rw).cuda(), dl.arena,
+                          dl.shared, out, dl.workspace(9))
+    full = dl.forward(xd).cpu().numpy()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), full.view(np.uint32))
