@@ -25,6 +25,8 @@
  *     enqueued.  Every device pointer must be 16-byte aligned (MOE_EALIGN).
  *     A call with T == 0 tokens is a no-op that checks only cfg and T
  *     (except moe_bucket, which then writes all-zero counts and offsets).
+ *   - Workspaces are caller-owned scratch; no state is kept in them between
+ *     calls (beyond the status word, see moe_workspace_init).
  *   - Values that are only known on the device (expert ids outside [0, E),
  *     non-finite activations) are not checked: behaviour is undefined.
  *   - Row-major layouts.  bf16 is the upper half of an IEEE fp32, fp16 is
@@ -101,6 +103,13 @@ int32_t moe_resolved_precision(const moe_config* cfg, int32_t T);
  * T tokens (the maximum of the three).  0 if the configuration is invalid. */
 size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
 
+/* Zero the status word of a workspace (its first 4 bytes).  The decode path
+ * of moe_layer_forward (T = 1, K <= 4, H <= 4096, F <= 1024, FP32 contract)
+ * hands data between workgroups of one kernel and bounds every wait; a wait
+ * that gives up (which a correct launch never does) sets this word to 1.
+ * Workspaces need no other preparation. */
+moe_status moe_workspace_init(const moe_config* cfg, int32_t T, void* ws_dev, size_t ws_bytes, hipStream_t stream);
+
 /* ---- expert arena --------------------------------------------------------
  * GGUF order (input of moe_pack_experts): expert e starts at e*expert_bytes;
  * inside it W_gate [F rows][H/32 blocks], W_up [F][H/32], W_down [H][F/32],
@@ -108,16 +117,17 @@ size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
  * index of weight j in its low nibble and of weight j+16 in its high nibble
  * (the ggml IQ4_NL definition the model card's checker follows).
  *
- * Packed order (what the compute entry points read): the same bytes regrouped
- * per matrix into 1152-byte tiles of 16 rows x 4 blocks, so that a wavefront
- * streams each tile with one 16-byte load per lane: tile (rt, kg) covers rows
- * 16*rt..16*rt+15 and blocks 4*kg..4*kg+3 and sits at tile index
+ * Packed order (what the compute entry points read): the same information
+ * regrouped per matrix into 1152-byte tiles of 16 rows x 4 blocks, so that a
+ * wavefront streams each tile with one 16-byte load per lane: tile (rt, kg)
+ * covers rows 16*rt..16*rt+15 and blocks 4*kg..4*kg+3 and sits at tile index
  * rt*(NB/4) + kg (NB = blocks per row).  Bytes [0, 1024): lane slot s
- * (row 16*rt + s%16, nibble word w = s/16) holds nibble bytes 4w..4w+3 of
- * blocks 4kg+0..4kg+3 of that row, 4 bytes each.  Bytes [1024, 1152): the 64
- * fp16 scales, scale of (row 16*rt + 4*G + i, block 4*kg + b) at
- * 1024 + 32*G + 8*b + 2*i.  Packing is a permutation of bytes: an expert
- * keeps moe_expert_bytes() bytes and the same start offset. */
+ * (row 16*rt + s%16, word w = s/16) holds, for blocks 4kg+0..4kg+3 in turn,
+ * 4 bytes with the indices of weights 8w..8w+7 of that block: byte i holds
+ * weight 8w+2i in its low nibble and 8w+2i+1 in its high nibble.  Bytes
+ * [1024, 1152): the 64 fp16 scales, scale of (row 16*rt + 4*G + i,
+ * block 4*kg + b) at 1024 + 32*G + 8*b + 2*i.  An expert keeps
+ * moe_expert_bytes() bytes and the same start offset. */
 
 /* Repack n_experts consecutive experts from GGUF order (src_dev) into packed
  * order (dst_dev).  src and dst must not overlap.  Run once at load. */

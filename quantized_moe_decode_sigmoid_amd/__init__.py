@@ -56,6 +56,7 @@ _SIGS = {
     "moe_expert_bytes": ([_cfgp], _sz),
     "moe_resolved_precision": ([_cfgp, _i32], _i32),
     "moe_workspace_bytes": ([_cfgp, _i32], _sz),
+    "moe_workspace_init": ([_cfgp, _i32, _vp, _sz, _vp], _i32),
     "moe_pack_experts": ([_cfgp, _i32, _vp, _vp, _vp], _i32),
     "moe_dequant": ([_cfgp, _vp, _i32, _i32, _vp, _vp], _i32),
     "moe_route": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -113,6 +114,11 @@ def moe_resolved_precision(cfg: moe_config, T: int) -> int:
 
 def moe_workspace_bytes(cfg: moe_config, T: int) -> int:
     return _lib.moe_workspace_bytes(ctypes.byref(cfg), T)
+
+
+def moe_workspace_init(cfg, T, ws, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.moe_workspace_init(ctypes.byref(cfg), T, _p(ws), ws_bytes, _stream(stream)), "moe_workspace_init")
 
 
 def moe_pack_experts(cfg, n_experts, src, dst, stream=None):
@@ -186,6 +192,7 @@ class DeviceLayer:
         need = moe_workspace_bytes(self.cfg, T)
         if self._ws is None or self._ws.numel() < need:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            moe_workspace_init(self.cfg, T, self._ws)
         return self._ws
 
     def forward(self, x, out=None, topk_ids=None, topk_w=None):

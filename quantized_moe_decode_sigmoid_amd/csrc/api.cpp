@@ -47,8 +47,16 @@ int max_chunks(const moe_config* c, int T) {
   return (int)(R / 16 + nonempty + (c->n_shared ? (T + 15) / 16 : 0));
 }
 
+// The two-launch decode path covers one token with the exact-weight contract.
+bool decode_path(const moe_config* c, int T) {
+  return T == 1 && c->top_k <= qmoe::kMaxDecodeK && c->ffn <= qmoe::kMaxDecodeFfn &&
+         c->hidden <= qmoe::kMaxDecodeHidden && resolve_precision(c, T) == MOE_PREC_FP32;
+}
+
 // Workspace plan: 256-byte aligned sub-buffers.
 struct Plan {
+  size_t status;                               // error word of the decode path
+  size_t hw;                                   // decode path: h words of one token
   size_t scores, ids, w;                       // router
   size_t counts, offsets, perm, pos, chunks, n_chunks;  // bucketing
   size_t h_hi, h_lo, y;                        // exact-weight FFN
@@ -65,6 +73,8 @@ Plan make_plan(const moe_config* c, int T) {
     at += align_up(bytes > 0 ? bytes : 1);
     return here;
   };
+  p.status = take(4);
+  p.hw = take((size_t)(c->top_k + 1) * F * 4);
   p.scores = take((size_t)T * E * 4);
   p.ids = take(R * 4);
   p.w = take(R * 4);
@@ -72,7 +82,8 @@ Plan make_plan(const moe_config* c, int T) {
   p.offsets = take((E + 1) * 4);
   p.perm = take(R * 4);
   p.pos = take(R * 4);
-  p.chunks = take((size_t)max_chunks(c, T) * sizeof(qmoe::Chunk));
+  const size_t nch = (size_t)max_chunks(c, T);
+  p.chunks = take(nch * sizeof(qmoe::Chunk));
   p.n_chunks = take(4);
   p.h_hi = take((R + S) * F * 2);
   p.h_lo = take((R + S) * F * 2);
@@ -160,6 +171,15 @@ MOE_API int32_t moe_resolved_precision(const moe_config* cfg, int32_t T) {
 MOE_API size_t moe_workspace_bytes(const moe_config* cfg, int32_t T) {
   if (check_common(cfg, T) != MOE_OK) return 0;
   return make_plan(cfg, T).total;
+}
+
+MOE_API moe_status moe_workspace_init(const moe_config* cfg, int32_t T, void* ws_dev, size_t ws_bytes,
+                                      hipStream_t stream) {
+  TRY(check_common(cfg, T));
+  TRY(need(ws_dev));
+  const Plan p = make_plan(cfg, T);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  return launched(qmoe::launch_zero_words(at<uint32_t>(ws_dev, p.status), 1, stream));
 }
 
 MOE_API moe_status moe_pack_experts(const moe_config* cfg, int32_t n_experts, const void* src_dev, void* dst_dev,
@@ -259,6 +279,28 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const voi
   if (T == 0) return MOE_OK;
   int32_t* ids = topk_ids_out_dev ? topk_ids_out_dev : at<int32_t>(ws_dev, p.ids);
   float* w = topk_w_out_dev ? topk_w_out_dev : at<float>(ws_dev, p.w);
+  if (decode_path(cfg, T)) {
+    qmoe::DecodeArgs a;
+    a.x = static_cast<const uint16_t*>(x_dev);
+    a.wg = gate_w_dev;
+    a.bias = sel_bias_dev;
+    a.arena = static_cast<const uint8_t*>(arena_dev);
+    a.shared = static_cast<const uint8_t*>(shared_dev);
+    a.expert_bytes = expert_bytes(cfg);
+    a.H = cfg->hidden;
+    a.F = cfg->ffn;
+    a.E = cfg->n_experts;
+    a.K = cfg->top_k;
+    a.n_shared = cfg->n_shared;
+    a.scale = cfg->routed_scale;
+    a.scores = at<float>(ws_dev, p.scores);
+    a.ids = ids;
+    a.w = w;
+    a.hw = at<uint32_t>(ws_dev, p.hw);
+    a.out = out_dev;
+    a.err = at<uint32_t>(ws_dev, p.status);
+    return launched(qmoe::launch_layer_decode(a, stream));
+  }
   TRY(launched(qmoe::launch_router(static_cast<const uint16_t*>(x_dev), gate_w_dev, sel_bias_dev, T, cfg->hidden,
                                    cfg->n_experts, cfg->top_k, cfg->routed_scale, at<float>(ws_dev, p.scores), ids, w,
                                    stream)));

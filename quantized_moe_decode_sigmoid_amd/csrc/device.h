@@ -7,11 +7,14 @@
 // the fp32 block result (exact-weight contract), or round d*level to bf16
 // (bf16 contract).
 //
-// Nibble bytes are decoded two weights at a time through a 256-entry table in
-// LDS: entry v = bf16(level[v & 15]) | bf16(level[v >> 4]) << 16, i.e. the
-// pair (weight j, weight j+16) of a block, ready to be one dword of an MFMA
-// operand.  The table is replicated 32 times so that lane l always reads bank
-// l % 32: lookups never conflict.
+// In the packed arena (moe_pack_experts) the 4-bit indices of a block are
+// regrouped so that nibble word w (4 bytes) holds weights 8w..8w+7, byte i
+// holding weight 8w+2i in its low nibble and 8w+2i+1 in its high nibble.
+// Bytes are decoded two weights at a time through a 256-entry table in LDS:
+// entry v = bf16(level[v & 15]) | bf16(level[v >> 4]) << 16, i.e. one dword
+// of an MFMA operand with its two k slots in natural order.  The table is
+// replicated 32 times so that lane l always reads bank l % 32: lookups never
+// conflict.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,6 +24,10 @@ namespace qmoe {
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // a native 16-byte vector (not a struct)
+
+// 16-byte load into a native vector
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 constexpr int kTileBytes = 1152;       // 16 rows x 4 blocks of 18 bytes
 constexpr int kTileNibbleBytes = 1024; // 64 lane slots x 16 bytes
@@ -43,8 +50,8 @@ __device__ __forceinline__ void build_pair_table(uint32_t* tbl) {
   }
 }
 
-// One nibble word (bytes 4w..4w+3 of a block) -> the 4 dwords of an 8-slot
-// bf16 operand: dword i = (level of weight 4w+i, level of weight 16+4w+i).
+// One nibble word (weights 8w..8w+7 of a block) -> the 4 dwords of an 8-slot
+// bf16 operand: dword i = (level of weight 8w+2i, level of weight 8w+2i+1).
 __device__ __forceinline__ bf16x8 decode_word(const uint32_t* tbl, uint32_t word, uint32_t lane32) {
   union {
     uint32_t u[4];
@@ -71,19 +78,9 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // bf16 activations of one row for block b, in the operand slot order of
-// decode_word: dword i = (x[32b + 4w + i], x[32b + 16 + 4w + i]).
+// decode_word: elements 32b + 8w .. 32b + 8w + 7, one 16-byte load.
 __device__ __forceinline__ bf16x8 load_x_operand(const uint16_t* xrow, int b, int w) {
-  const uint2 a = *reinterpret_cast<const uint2*>(xrow + 32 * b + 4 * w);
-  const uint2 c = *reinterpret_cast<const uint2*>(xrow + 32 * b + 16 + 4 * w);
-  union {
-    uint32_t u[4];
-    bf16x8 v;
-  } r;
-  r.u[0] = (a.x & 0xffffu) | (c.x << 16);
-  r.u[1] = (a.x >> 16) | (c.x & 0xffff0000u);
-  r.u[2] = (a.y & 0xffffu) | (c.y << 16);
-  r.u[3] = (a.y >> 16) | (c.y & 0xffff0000u);
-  return r.v;
+  return *reinterpret_cast<const bf16x8*>(xrow + 32 * b + 8 * w);
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -94,6 +91,41 @@ __device__ __forceinline__ bf16x8 zero_operand() {
   bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
   return z;
 }
+
+// Scales of one packed tile as seen by MFMA C-register group G (rows 4G..4G+3).
+
+struct TileScales {
+  uint32_t s[8];  // fp16 pairs: block b -> s[2b] (rows 4G, 4G+1), s[2b+1] (rows 4G+2, 4G+3)
+};
+
+__device__ __forceinline__ TileScales load_scales(const uint8_t* tile, int G) {
+  const uint4 a = *reinterpret_cast<const uint4*>(tile + kTileNibbleBytes + 32 * G);
+  const uint4 b = *reinterpret_cast<const uint4*>(tile + kTileNibbleBytes + 32 * G + 16);
+  TileScales t;
+  t.s[0] = a.x;
+  t.s[1] = a.y;
+  t.s[2] = a.z;
+  t.s[3] = a.w;
+  t.s[4] = b.x;
+  t.s[5] = b.y;
+  t.s[6] = b.z;
+  t.s[7] = b.w;
+  return t;
+}
+
+// acc[i] += d(row 4G+i, block b) * c[i]
+__device__ __forceinline__ void scale_acc(f32x4& acc, const f32x4& c, const TileScales& sc, int b) {
+  const uint32_t p = sc.s[2 * b], q = sc.s[2 * b + 1];
+  acc[0] = __builtin_fmaf(half_bits_to_float(p), c[0], acc[0]);
+  acc[1] = __builtin_fmaf(half_bits_to_float(p >> 16), c[1], acc[1]);
+  acc[2] = __builtin_fmaf(half_bits_to_float(q), c[2], acc[2]);
+  acc[3] = __builtin_fmaf(half_bits_to_float(q >> 16), c[3], acc[3]);
+}
+
+__device__ __forceinline__ uint32_t uword(const uint4& v, int b) {
+  return b == 0 ? v.x : (b == 1 ? v.y : (b == 2 ? v.z : v.w));
+}
+__device__ __forceinline__ uint32_t uword(const u32x4& v, int b) { return v[b]; }
 
 // HIP keeps the last error of any runtime call per thread; clear it before a
 // launch so that the check after the launch reports that launch only.

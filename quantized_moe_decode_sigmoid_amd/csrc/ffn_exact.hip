@@ -32,8 +32,12 @@ constexpr int kFfnThreads = 256;
 // ---------------------------------------------------------------- packing
 
 // One thread per 16-byte lane slot of a tile.  src: GGUF order, rows of
-// NB = cols/32 blocks of 18 bytes.  Threads with slot < 16 also place the
-// four scales of (rows 4G..4G+3, block b), G = slot/4, b = slot%4.
+// NB = cols/32 blocks of 18 bytes, byte j of a block holding the index of
+// weight j (low nibble) and of weight j+16 (high nibble).  Lane slot s (row
+// s%16, word w = s/16) receives, per block, the indices of weights
+// 8w..8w+7 as 4 bytes (weight 8w+2i low, 8w+2i+1 high in byte i).  Threads
+// with slot < 16 also place the four scales of (rows 4G..4G+3, block b),
+// G = slot/4, b = slot%4.
 __global__ void k_pack(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t n_tiles_total,
                        int rows, int nb, int64_t matrix_bytes) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -52,7 +56,12 @@ __global__ void k_pack(const uint8_t* __restrict__ src, uint8_t* __restrict__ ds
     uint8_t out[16];
     for (int b = 0; b < 4; b++) {
       const uint8_t* blk = m_src + ((int64_t)row * nb + 4 * kg + b) * 18;
-      for (int i = 0; i < 4; i++) out[4 * b + i] = blk[2 + 4 * w + i];
+      for (int i = 0; i < 4; i++) {
+        const int k0 = 8 * w + 2 * i, k1 = k0 + 1;  // weight indices, 0..31
+        const int q0 = k0 < 16 ? (blk[2 + k0] & 15) : (blk[2 + k0 - 16] >> 4);
+        const int q1 = k1 < 16 ? (blk[2 + k1] & 15) : (blk[2 + k1 - 16] >> 4);
+        out[4 * b + i] = (uint8_t)(q0 | (q1 << 4));
+      }
     }
     uint4 v;
     __builtin_memcpy(&v, out, 16);
@@ -100,7 +109,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat
       uint32_t u[4];
     } a;
     a.v = decode_word(tbl, words[b], lane & 31);
-    float* o = out + (size_t)row * cols + 32 * (4 * kg + b);
+    float* o = out + (size_t)row * cols + 32 * (4 * kg + b) + 8 * w;
     for (int i = 0; i < 4; i++) {
       float lo = d * bf16_bits_to_f32(a.u[i] & 0xffffu);
       float hi = d * bf16_bits_to_f32(a.u[i] >> 16);
@@ -108,52 +117,17 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat
         lo = bf16_bits_to_f32(f32_to_bf16_rne(lo));
         hi = bf16_bits_to_f32(f32_to_bf16_rne(hi));
       }
-      o[4 * w + i] = lo;
-      o[16 + 4 * w + i] = hi;
+      o[2 * i] = lo;
+      o[2 * i + 1] = hi;
     }
   }
-}
-
-// ---------------------------------------------------------------- shared pieces
-
-struct TileScales {
-  uint32_t s[8];  // fp16 pairs: block b -> s[2b] (rows 4G, 4G+1), s[2b+1] (rows 4G+2, 4G+3)
-};
-
-__device__ __forceinline__ TileScales load_scales(const uint8_t* tile, int G) {
-  const uint4 a = *reinterpret_cast<const uint4*>(tile + kTileNibbleBytes + 32 * G);
-  const uint4 b = *reinterpret_cast<const uint4*>(tile + kTileNibbleBytes + 32 * G + 16);
-  TileScales t;
-  t.s[0] = a.x;
-  t.s[1] = a.y;
-  t.s[2] = a.z;
-  t.s[3] = a.w;
-  t.s[4] = b.x;
-  t.s[5] = b.y;
-  t.s[6] = b.z;
-  t.s[7] = b.w;
-  return t;
-}
-
-// acc[i] += d(row 4G+i, block b) * c[i]
-__device__ __forceinline__ void scale_acc(f32x4& acc, const f32x4& c, const TileScales& sc, int b) {
-  const uint32_t p = sc.s[2 * b], q = sc.s[2 * b + 1];
-  acc[0] = __builtin_fmaf(half_bits_to_float(p), c[0], acc[0]);
-  acc[1] = __builtin_fmaf(half_bits_to_float(p >> 16), c[1], acc[1]);
-  acc[2] = __builtin_fmaf(half_bits_to_float(q), c[2], acc[2]);
-  acc[3] = __builtin_fmaf(half_bits_to_float(q >> 16), c[3], acc[3]);
-}
-
-__device__ __forceinline__ uint32_t uword(const uint4& v, int b) {
-  return b == 0 ? v.x : (b == 1 ? v.y : (b == 2 ? v.z : v.w));
 }
 
 // ---------------------------------------------------------------- gate / up
 
 // Workgroup = (chunk, 16-row tile of F).  Output: the product h = silu(g)*u of
 // route column c, row f, as two bf16 halves h_hi = bf16(h), h_lo = bf16(h -
-// h_hi), stored in the operand order of the down projection: element f of a
-// row sits at 32*(f/32) + 2*(f%16) + (f%32 >= 16).
+// h_hi), row-major [route][F].
 __global__ __launch_bounds__(kFfnThreads) void k_gate_up_exact(
     const uint16_t* __restrict__ x, int H, int F, int K, int T, const uint8_t* __restrict__ arena,
     const uint8_t* __restrict__ shared, int64_t expert_bytes, const int32_t* __restrict__ perm,
@@ -215,9 +189,8 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up_exact(
     const float h = gv / (1.0f + expf(-gv)) * u[i];
     const uint32_t hb = f32_to_bf16_rne(h);
     const uint32_t lb = f32_to_bf16_rne(h - bf16_bits_to_f32(hb));
-    const int64_t at = hrow * F + 32 * (f >> 5) + 2 * (f & 15) + ((f >> 4) & 1);
-    h_hi[at] = (uint16_t)hb;
-    h_lo[at] = (uint16_t)lb;
+    h_hi[hrow * F + f] = (uint16_t)hb;
+    h_lo[hrow * F + f] = (uint16_t)lb;
   }
 }
 

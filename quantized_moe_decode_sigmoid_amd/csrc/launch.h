@@ -23,4 +23,32 @@ hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n
                             const int32_t* pos, const float* w, const Chunk* chunks, const int32_t* n_chunks,
                             uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream);
 
+// ---- one decode token in two launches (layer_decode.hip)
+
+constexpr int kMaxDecodeK = 4;          // experts per token
+constexpr int kMaxDecodeFfn = 1024;     // F
+constexpr int kMaxDecodeHidden = 4096;  // H
+
+struct DecodeArgs {
+  const uint16_t* x;   // [H] bf16
+  const float* wg;     // [E][H]
+  const float* bias;   // [E] or null
+  const uint8_t* arena;
+  const uint8_t* shared;
+  int64_t expert_bytes;
+  int H, F, E, K, n_shared;
+  float scale;
+  float* scores;       // [E] sigmoid scores (first kernel -> second)
+  int32_t* ids;        // [K] routing outputs
+  float* w;            // [K]
+  uint32_t* hw;        // [(K + 1) * F] h words: bf16(h) | bf16(h - bf16(h)) << 16
+  float* out;          // [H]
+  uint32_t* err;       // set to 1 if a wait gave up
+  int n_router, n_shared_wg, n_routed_wg, n_down_wg;  // grid partition (set by the launcher)
+};
+
+hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream);
+
+hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
+
 }  // namespace qmoe

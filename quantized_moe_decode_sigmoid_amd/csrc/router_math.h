@@ -1,0 +1,158 @@
+// Router arithmetic shared by the standalone router kernels and the fused
+// decode kernel: the fixed-order fp32 logit, the fixed-sequence sigmoid and
+// the wavefront top-K.  Every function disables fp contraction in its body so
+// that only the written fused multiply-adds fuse.
+//
+// Model card xing4_0-29b-IQ4_NL_EPQ, "Model and routing" table: sigmoid
+// gating with the selection bias ffn_exp_probs_b (noaux_tc), top-K, weights
+// normalised over the selected experts and scaled by expert_weights_scale.
+#pragma once
+
+#include "device.h"
+
+namespace qmoe {
+
+// exp(y) in double: y = n ln2 + r (Cody-Waite with a two-part ln 2 and fused
+// multiply-adds), Taylor polynomial of degree 13 for exp(r) in Horner form
+// (|r| <= ln2/2, truncation error below 1e-17), times 2^n.
+__device__ __forceinline__ double exp_fixed(double y) {
+#pragma clang fp contract(off)
+  constexpr double kLog2e = 0x1.71547652b82fep+0;  // nearest double to 1/ln 2
+  constexpr double kLn2Hi = 0x1.62e42fefa39efp-1;  // nearest double to ln 2
+  constexpr double kLn2Lo = 0x1.abc9e3b39803fp-56; // nearest double to (ln 2 - kLn2Hi)
+  if (y > 200.0) return __builtin_inf();
+  if (y < -200.0) return 0.0;
+  const double n = __builtin_rint(y * kLog2e);
+  double r = __builtin_fma(-n, kLn2Hi, y);
+  r = __builtin_fma(-n, kLn2Lo, r);
+  double inv_fact[14];
+  double fact = 1.0;
+#pragma unroll
+  for (int k = 0; k < 14; k++) {
+    if (k > 0) fact *= (double)k;
+    inv_fact[k] = 1.0 / fact;
+  }
+  double p = inv_fact[13];
+#pragma unroll
+  for (int k = 12; k >= 0; k--) p = __builtin_fma(p, r, inv_fact[k]);
+  return __builtin_ldexp(p, (int)n);
+}
+
+// Sigmoid evaluated in double and rounded once to fp32.
+__device__ __forceinline__ float sigmoid_fixed(float l) {
+#pragma clang fp contract(off)
+  return (float)(1.0 / (1.0 + exp_fixed(-(double)l)));
+}
+
+// The expert's router row in registers: lane j holds elements 256m + 4j + c.
+// Every load is issued (slots m >= H/256 repeat the last valid one and are
+// never used), so that no load sits behind a branch.
+template <int MMAX>
+__device__ __forceinline__ void load_router_row(const float* wrow, int H, int lane, float4 (&w)[MMAX]) {
+  const int M = H >> 8;
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    const int mm = m < M ? m : M - 1;
+    w[m] = *reinterpret_cast<const float4*>(wrow + 256 * mm + 4 * lane);
+  }
+}
+
+// fp32 logit in the fixed order: lane j accumulates its elements with fused
+// multiply-adds in (m, c) order, then p_j + p_{j xor s} for s = 32..1.  Every
+// lane returns the same value.
+template <int MMAX>
+__device__ __forceinline__ float router_logit(const uint16_t* xrow, int H, int lane, const float4 (&w)[MMAX]) {
+#pragma clang fp contract(off)
+  const int M = H >> 8;
+  uint2 xv[MMAX];
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    const int mm = m < M ? m : M - 1;
+    xv[m] = *reinterpret_cast<const uint2*>(xrow + 256 * mm + 4 * lane);
+  }
+  float p = 0.0f;
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    if (m < M) {
+      p = __builtin_fmaf(bf16_bits_to_f32(xv[m].x & 0xffffu), w[m].x, p);
+      p = __builtin_fmaf(bf16_bits_to_f32(xv[m].x >> 16), w[m].y, p);
+      p = __builtin_fmaf(bf16_bits_to_f32(xv[m].y & 0xffffu), w[m].z, p);
+      p = __builtin_fmaf(bf16_bits_to_f32(xv[m].y >> 16), w[m].w, p);
+    }
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_xor(p, s, 64);
+  return p;
+}
+
+// The (selection score, expert) order: a precedes b when its score is larger,
+// or equal with a smaller expert index.
+__device__ __forceinline__ bool sel_before(float sa, int ea, float sb, int eb) {
+  return sa > sb || (sa == sb && ea < eb);
+}
+
+// One wavefront selects the K experts of one token from its E sigmoid scores:
+// K rounds of a wave-wide arg-max under (selection score descending, expert
+// index ascending), selection score = s + bias.  Lane 0 writes the slots to
+// ids[0..K) and the weights scale * s_k / (((s_0 + s_1) + s_2) + ...) to w
+// (either may point to global or LDS memory).
+__device__ __forceinline__ void topk_wave(const float* scores, const float* bias, int E, int K, float scale,
+                                          int lane, int32_t* ids, float* wout) {
+#pragma clang fp contract(off)
+  float s[4], sel[4];
+  bool avail[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int e = lane + 64 * q;
+    avail[q] = e < E;
+    s[q] = avail[q] ? scores[e] : 0.0f;
+    sel[q] = avail[q] ? (bias ? s[q] + bias[e] : s[q]) : 0.0f;
+  }
+  int chosen[8];
+  float chosen_s[8];
+  for (int k = 0; k < K; k++) {
+    bool have = false;
+    float bs = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      if (avail[q] && (!have || sel[q] > bs)) {
+        have = true;
+        bs = sel[q];
+        be = lane + 64 * q;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float os = __shfl_xor(bs, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      const bool ohave = oe != 0x7fffffff;
+      if (ohave && (!have || os > bs || (os == bs && oe < be))) {
+        have = true;
+        bs = os;
+        be = oe;
+      }
+    }
+    float sw = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      if (lane + 64 * q == be) {
+        avail[q] = false;
+        sw = s[q];
+      }
+    }
+    sw = __shfl(sw, be & 63, 64);
+    chosen[k] = be;
+    chosen_s[k] = sw;
+  }
+  if (lane == 0) {
+    float S = 0.0f;
+    for (int k = 0; k < K; k++) S = S + chosen_s[k];
+    for (int k = 0; k < K; k++) {
+      ids[k] = chosen[k];
+      wout[k] = (chosen_s[k] / S) * scale;
+    }
+  }
+}
+
+}  // namespace qmoe

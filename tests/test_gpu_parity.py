@@ -197,3 +197,67 @@ def test_expert_forward_matches_layer_forward():
                           dl.shared, out, dl.workspace(9))
     full = dl.forward(xd).cpu().numpy()
     assert np.array_equal(out.cpu().numpy().view(np.uint32), full.view(np.uint32))
+
+
+# ---------------------------------------------------------------- single-launch decode path
+
+def multi_kernel_layer(dl, xd, T):
+    """moe_route + moe_expert_forward: the multi-kernel composition of the same layer."""
+    cfg = dl.cfg
+    ids = torch.empty((T, cfg.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, T), dtype=torch.uint8, device="cuda")
+    qm.moe_route(cfg, T, xd, dl.gate_w, dl.bias, ids, w, ws)
+    qm.moe_expert_forward(cfg, T, xd, ids, w, dl.arena, dl.shared, out, ws)
+    return out
+
+
+@pytest.mark.parametrize("name,T,first", [("xing4", 1, 300), ("xing4", 1, 301), ("tiny", 1, 300), ("tiny", 1, 7)])
+def test_decode_path_equals_multi_kernel_path(name, T, first):
+    s, inp, dl = device_layer(name)
+    x = synth.tokens(s, T, first=first)
+    xd = to_dev_bf16(x)
+    log(f"decode path vs multi-kernel {name} T={T}")
+    a = dl.forward(xd).cpu().numpy()
+    b = multi_kernel_layer(dl, xd, T).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    torch.cuda.synchronize()
+    status = dl.workspace(T)[:4].view(torch.int32).cpu().numpy()
+    assert status[0] == 0, "a wait of the decode path gave up"
+
+
+def test_decode_path_many_consecutive_calls_one_workspace():
+    s, inp, dl = device_layer("xing4")
+    x = synth.tokens(s, 64, first=900)
+    xd = to_dev_bf16(x)
+    log("decode path, 64 consecutive T=1 calls")
+    outs = [dl.forward(xd[i:i + 1]) for i in range(64)]
+    got = torch.cat(outs).cpu().numpy()
+    ref = multi_kernel_layer(dl, xd, 64).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def test_graph_replay_of_decode_calls():
+    """A captured sequence of T=1 calls replayed several times, with eager work between replays."""
+    s, inp, dl = device_layer("xing4")
+    x = synth.tokens(s, 16, first=1500)
+    xd = to_dev_bf16(x)
+    out = torch.empty((16, s.hidden), dtype=torch.float32, device="cuda")
+    ws = dl.workspace(1)
+    eager = torch.cat([dl.forward(xd[i:i + 1]) for i in range(16)]).cpu().numpy()
+    log("graph capture of 16 decode calls")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(16):
+                qm.moe_layer_forward(dl.cfg, 1, xd[i:i + 1], dl.gate_w, None, dl.arena, dl.shared,
+                                     out[i:i + 1], ws=ws)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        _ = dl.forward(xd[rep:rep + 1])  # eager work between replays
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.view(np.uint32)), rep
