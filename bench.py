@@ -32,6 +32,8 @@ PLACEMENTS = 32
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+                   help="decode: the headline T=1 line (default); prefill: one T=2048 layer call per step")
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--distinct-layers", type=int, default=4,
@@ -41,12 +43,122 @@ def parse():
     return p.parse_args()
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.workload == "prefill":
+        run_prefill(args)
+    else:
+        run_decode(args)
 
+
+def run_prefill(args):
+    """One prefill-sized layer call per step: T=2048, H=2048, 256 experts top-8 + 1 shared, ffn 512,
+    Zipf(1.0) expert popularity through the selection bias; bf16 grouped MFMA FFN."""
+    import torch
+
+    import quantized_moe_decode_sigmoid_amd as qm
+    import synth
+
+    shape = synth.WORKLOADS["prefill"]
+    T, H, E, K, F = shape.tokens, shape.hidden, shape.n_experts, shape.top_k, shape.ffn
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    lam = synth.zipf_lambda(shape)
+    inp = synth.layer_inputs(shape, lam=lam)
+    x_bits = synth.tokens(shape, T)
+    gen_s = time.time() - t0
+    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
+    prec = qm.moe_resolved_precision(cfg, T)
+    dl = qm.DeviceLayer(cfg, inp["gate_w"], inp["bias"], inp["arena"], inp["shared"])
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, K), dtype=torch.float32, device=dev)
+    ws = dl.workspace(T)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        def step():
+            qm.moe_layer_forward(cfg, T, x, dl.gate_w, dl.bias, dl.arena, dl.shared, out, ids, wts, ws)
+
+        t_first = time.time()
+        step()
+        torch.cuda.synchronize()
+        first_ms = (time.time() - t_first) * 1e3
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        layer_ms = ev0.elapsed_time(ev1) / args.steps
+        # the expert FFN alone (bucketing, gate/up, down, combine) on the routing just computed
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda._sleep(50_000_000)
+        for i in range(args.steps):
+            starts[i].record(stream)
+            qm.moe_expert_forward(cfg, T, x, ids, wts, dl.arena, dl.shared, out, ws)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+    ffn_us = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)])
+    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
+    flops = 2.0 * 3 * H * F * (T * K + T * shape.n_shared)
+    ffn_tflops = flops / (float(np.mean(ffn_us)) * 1e-6) / 1e12
+
+    cpu = None
+    if args.cpu_sample > 0:
+        import oracle
+        n = args.cpu_sample
+        c0 = time.time()
+        oracle.layer(x_bits[:n], inp["gate_w"], inp["arena"], inp["shared"], K, F, shape.routed_scale, inp["bias"],
+                     oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32)
+        cs = time.time() - c0
+        cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"the first {n} of the {T} tokens in one oracle.layer call, {cs:.1f} s"}
+
+    res = {
+        "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
+        "value": round(flops / (layer_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(layer_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if prec == qm.PREC_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill MoE layer, T=2048: hidden 2048, 256 experts top-8 + 1 shared, ffn 512, "
+                               "IQ4_NL experts, sigmoid router, scale 2.0, Zipf(1.0) expert popularity",
+                   "tokens_per_step": T, "zipf_lambda": lam},
+        "roofline": {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe_expert_forward bf16: k_bucket + k_gate_up_bf16 + k_down_bf16 + k_combine "
+                               "(events around the call)",
+                     "flops_per_launch": flops, "avg_us": round(float(np.mean(ffn_us)), 3)},
+        "cpu_baseline": cpu,
+        "tok_s": round(T / (layer_ms * 1e-3), 1),
+        "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
+                              "median": float(np.median(counts))},
+        "first_step_ms": round(first_ms, 3),
+        "setup_s": round(gen_s, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def run_decode(args):
     import torch
 
     import quantized_moe_decode_sigmoid_amd as qm

@@ -61,9 +61,10 @@ typedef enum {
 /* Arithmetic contract of the expert FFN.
  * FP32: weights are the exact IQ4_NL values d*level, the activation product
  *       silu(g)*u is kept in fp32, all sums in fp32 (decode-sized calls).
- * BF16: weights are rounded to bf16 (nearest even) in LDS and the product
- *       silu(g)*u is rounded to bf16 before the down projection; products run
- *       on bf16 MFMA with fp32 accumulation (batched / prefill calls).
+ * BF16: weights are the exact values rounded to bf16 (nearest even), the
+ *       product silu(g)*u is rounded to bf16 before the down projection;
+ *       products run on bf16 MFMA with fp32 accumulation (batched / prefill
+ *       calls: tiles of up to 128 routes of one expert).
  * AUTO: FP32 when T*K <= 16*E (at most 16 routes per expert on average),
  *       else BF16.  The router and the combine are fp32 in every mode. */
 typedef enum { MOE_PREC_AUTO = 0, MOE_PREC_FP32 = 1, MOE_PREC_BF16 = 2 } moe_precision;

@@ -41,11 +41,18 @@ int resolve_precision(const moe_config* c, int T) {
 
 int64_t expert_bytes(const moe_config* c) { return 3 * (int64_t)c->ffn * (c->hidden / 32) * 18; }
 
-int max_chunks(const moe_config* c, int T) {
+// Routes per work chunk of the FFN kernels of each contract.
+int chunk_rows(int precision) { return precision == MOE_PREC_BF16 ? qmoe::kBfRows : 16; }
+
+// Upper bound on the chunks of T tokens: at most one partial chunk per
+// non-empty expert beyond the full ones, plus the shared expert's.
+int max_chunks(const moe_config* c, int T, int rows) {
   const int64_t R = (int64_t)T * c->top_k;
   const int64_t nonempty = R < c->n_experts ? R : c->n_experts;
-  return (int)(R / 16 + nonempty + (c->n_shared ? (T + 15) / 16 : 0));
+  return (int)(R / rows + nonempty + (c->n_shared ? (T + rows - 1) / rows : 0));
 }
+
+int max_chunks(const moe_config* c, int T) { return max_chunks(c, T, chunk_rows(resolve_precision(c, T))); }
 
 // The two-launch decode path covers one token with the exact-weight contract.
 bool decode_path(const moe_config* c, int T) {
@@ -85,8 +92,8 @@ Plan make_plan(const moe_config* c, int T) {
   const size_t nch = (size_t)max_chunks(c, T);
   p.chunks = take(nch * sizeof(qmoe::Chunk));
   p.n_chunks = take(4);
-  p.h_hi = take((R + S) * F * 2);
-  p.h_lo = take((R + S) * F * 2);
+  p.h_hi = take((R + S) * F * 2);  // h (bf16 contract) or its high half (exact contract)
+  p.h_lo = take(resolve_precision(c, T) == MOE_PREC_BF16 ? 0 : (R + S) * F * 2);
   p.y = take((R + S) * H * 4);
   p.total = at;
   return p;
@@ -130,11 +137,16 @@ moe_status run_expert_forward(const moe_config* cfg, int32_t T, const void* x, c
   if (T == 0) return MOE_OK;
   const Plan p = make_plan(cfg, T);
   const int H = cfg->hidden, F = cfg->ffn, E = cfg->n_experts, K = cfg->top_k;
-  TRY(launched(qmoe::launch_bucket(ids, T, K, E, cfg->n_shared, at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets),
-                                   at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), at<qmoe::Chunk>(ws, p.chunks),
-                                   at<int32_t>(ws, p.n_chunks), stream)));
   const int prec = resolve_precision(cfg, T);
-  if (prec != MOE_PREC_FP32) return MOE_EUNSUPPORTED;
+  TRY(launched(qmoe::launch_bucket(ids, T, K, E, cfg->n_shared, chunk_rows(prec), at<int32_t>(ws, p.counts),
+                                   at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos),
+                                   at<qmoe::Chunk>(ws, p.chunks), at<int32_t>(ws, p.n_chunks), stream)));
+  if (prec == MOE_PREC_BF16)
+    return launched(qmoe::launch_ffn_bf16(
+        static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, max_chunks(cfg, T),
+        static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
+        at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks),
+        at<int32_t>(ws, p.n_chunks), at<uint16_t>(ws, p.h_hi), at<float>(ws, p.y), out, stream));
   return launched(qmoe::launch_ffn_exact(
       static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, max_chunks(cfg, T),
       static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
@@ -239,7 +251,7 @@ MOE_API moe_status moe_bucket(const moe_config* cfg, int32_t T, const int32_t* t
     TRY(need(perm_dev));
     TRY(optional_ptr(pos_dev));
   }
-  return launched(qmoe::launch_bucket(topk_ids_dev, T, cfg->top_k, cfg->n_experts, cfg->n_shared, counts_dev,
+  return launched(qmoe::launch_bucket(topk_ids_dev, T, cfg->top_k, cfg->n_experts, cfg->n_shared, 16, counts_dev,
                                       offsets_dev, perm_dev, pos_dev, nullptr, nullptr, stream));
 }
 

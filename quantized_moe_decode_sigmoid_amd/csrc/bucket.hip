@@ -13,9 +13,9 @@
 //      LDS give the offset of each wavefront; a running offset per expert
 //      carries across tiles.  Position = running + earlier waves + lane rank,
 //      which is exactly the stable order (ascending route id in an expert).
-// The same pass writes the work list of the exact-weight FFN kernels: chunks
-// of at most 16 routes of one expert, then chunks of 16 tokens of the shared
-// expert.
+// The same pass writes the work list of the FFN kernels: chunks of at most
+// chunk_rows routes of one expert, then chunks of chunk_rows tokens of the
+// shared expert (chunk_rows is a power of two).
 #include "device.h"
 #include "launch.h"
 
@@ -25,7 +25,7 @@ constexpr int kBucketThreads = 1024;
 constexpr int kBucketWaves = kBucketThreads / 64;
 
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int T, int K, int E,
-                                                           int n_shared, int32_t* __restrict__ counts,
+                                                           int n_shared, int chunk_shift, int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ pos, Chunk* __restrict__ chunks,
                                                            int32_t* __restrict__ n_chunks) {
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
       s_run[e] = run;
       s_chunk_first[e] = ch;
       run += s_cnt[e];
-      ch += (s_cnt[e] + 15) >> 4;
+      ch += (s_cnt[e] + (1 << chunk_shift) - 1) >> chunk_shift;
     }
     s_chunk_first[E] = ch;
   }
@@ -62,23 +62,24 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   // chunk list (independent of the permutation itself); optional
   const bool want_chunks = chunks != nullptr;
   for (int e = tid; want_chunks && e < E; e += kBucketThreads) {
-    const int c0 = s_chunk_first[e], nch = (s_cnt[e] + 15) >> 4;
+    const int rows = 1 << chunk_shift;
+    const int c0 = s_chunk_first[e], nch = (s_cnt[e] + rows - 1) >> chunk_shift;
     for (int j = 0; j < nch; j++) {
       Chunk c;
       c.expert = e;
-      c.first = s_run[e] + 16 * j;
-      c.count = min(16, s_cnt[e] - 16 * j);
+      c.first = s_run[e] + rows * j;
+      c.count = min(rows, s_cnt[e] - rows * j);
       c.pad = 0;
       chunks[c0 + j] = c;
     }
   }
   const int routed_chunks = s_chunk_first[E];
-  const int shared_chunks = n_shared ? (T + 15) >> 4 : 0;
+  const int shared_chunks = n_shared ? (T + (1 << chunk_shift) - 1) >> chunk_shift : 0;
   for (int j = tid; want_chunks && j < shared_chunks; j += kBucketThreads) {
     Chunk c;
     c.expert = -1;
-    c.first = 16 * j;
-    c.count = min(16, T - 16 * j);
+    c.first = j << chunk_shift;
+    c.count = min(1 << chunk_shift, T - (j << chunk_shift));
     c.pad = 0;
     chunks[routed_chunks + j] = c;
   }
@@ -118,11 +119,14 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   }
 }
 
-hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int n_shared, int32_t* counts, int32_t* offsets,
-                         int32_t* perm, int32_t* pos, Chunk* chunks, int32_t* n_chunks, hipStream_t stream) {
+hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int n_shared, int chunk_rows, int32_t* counts,
+                         int32_t* offsets, int32_t* perm, int32_t* pos, Chunk* chunks, int32_t* n_chunks,
+                         hipStream_t stream) {
+  int shift = 0;
+  while ((1 << shift) < chunk_rows) shift++;
   clear_last_error();
-  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, stream, ids, T, K, E, n_shared, counts, offsets, perm,
-                     pos, chunks, n_chunks);
+  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, stream, ids, T, K, E, n_shared, shift, counts,
+                     offsets, perm, pos, chunks, n_chunks);
   return hipGetLastError();
 }
 

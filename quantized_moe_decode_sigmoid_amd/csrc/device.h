@@ -77,6 +77,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two fp32 values -> one dword of bf16 (lo in bits 0..15), each rounded to
+// nearest even by the hardware conversion (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
 // bf16 activations of one row for block b, in the operand slot order of
 // decode_word: elements 32b + 8w .. 32b + 8w + 7, one 16-byte load.
 __device__ __forceinline__ bf16x8 load_x_operand(const uint16_t* xrow, int b, int w) {

@@ -1,0 +1,322 @@
+// Expert FFN with bf16 weights on MFMA: the batched / prefill path.
+//
+// Arithmetic (bf16 contract): every weight is the IQ4_NL value d*level
+// (model card xing4_0-29b-IQ4_NL_EPQ, pure-NumPy parity section) rounded to
+// bf16, nearest even; products run on v_mfma_f32_16x16x32_bf16 with fp32
+// accumulation; h = silu(g)*u (zLLM "Algorithm Layer", FFN section) is
+// rounded to bf16 before the down projection; y and the routed + shared sum
+// stay fp32 (PocketLLM design record, section 2).
+//
+// Work: tiles of up to 128 routes of one expert (bucketed order, design
+// record section 4) or 128 tokens of the shared expert.  A workgroup of 8
+// wavefronts owns one tile and one slab of output columns; wavefront w owns
+// 32 gate columns and the same 32 up columns (gate/up) or 64 output columns
+// (down), over all rows of the tile.  Per 128-wide step of the reduction:
+//   - the tile's activation rows (the A operand, the same for every
+//     wavefront) go from global memory straight into LDS (LDS DMA loads,
+//     double buffered, one step ahead): gathered rows of x for gate/up,
+//     consecutive rows of h for down;
+//   - each wavefront loads its packed weight tiles (one 16-byte word per lane
+//     per 16 columns) and dequantizes every word straight into its lane's
+//     bf16 B operand (levels from the LDS pair table, times the fp16 scale,
+//     rounded to bf16).  Each weight feeds exactly one wavefront, so the
+//     dequantized tile needs no trip through LDS; it is dequantized once per
+//     workgroup and reused by every 16-row sub-tile of the tile;
+//   - 16-row sub-tiles past the tile's last row are skipped (a branch that is
+//     uniform over the workgroup).
+#include "device.h"
+#include "launch.h"
+
+namespace qmoe {
+
+constexpr int kBfThreads = 512;
+constexpr int kBfWaves = kBfThreads / 64;
+constexpr int kBfSub = kBfRows / 16;        // 16-row MFMA sub-tiles per tile
+constexpr int kBfStep = 128;                // reduction elements per step (one packed tile)
+constexpr int kGuCols = 32;                 // gate (and up) columns per wavefront
+constexpr int kDnCols = 64;                 // down output columns per wavefront
+constexpr int kStageLoads = kBfRows / 4 / kBfWaves;  // 1 KB LDS DMA loads per wavefront and step
+
+// LDS: two buffers of activation rows, then the level pair table.  A buffer
+// row is 256 bytes (one step); its 16-byte slots are permuted by the row
+// index (slot = piece ^ (row % 16)), so that the 16 rows read by one A
+// operand fetch fall into distinct banks.  The buffers come first: the LDS
+// address of an LDS DMA load is taken from the low 16 bits of M0, so its
+// destinations must lie in the first 64 KB of the workgroup's LDS.
+struct BfLds {
+  uint16_t a[2][kBfRows * kBfStep];
+  uint32_t tbl[kPairTableWords];
+  int32_t src[kBfRows];  // source row of each tile row (x row or h row)
+};
+static_assert(sizeof(uint16_t) * 2 * kBfRows * kBfStep <= 65536, "LDS DMA destinations beyond 64 KB");
+
+// One nibble word -> the lane's 8-element bf16 operand, each weight
+// bf16(d * level) with the fp32 product exact before the rounding.
+__device__ __forceinline__ bf16x8 dequant_bf16(const uint32_t* tbl, uint32_t word, float d, uint32_t lane32) {
+  union {
+    uint32_t u[4];
+    bf16x8 v;
+  } r;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const uint32_t e = tbl[((word >> (8 * i)) & 0xffu) * 32u + lane32];
+    r.u[i] = pack_bf16x2(__uint_as_float(e << 16) * d, __uint_as_float(e & 0xffff0000u) * d);
+  }
+  return r.v;
+}
+
+// The packed tile of 16 columns that a lane reads: its nibble word and the
+// fp16 scales of its column (lane % 16) for the tile's 4 blocks.
+struct LaneTile {
+  u32x4 nib;
+  uint32_t sc[4];
+};
+
+__device__ __forceinline__ LaneTile load_lane_tile(const uint8_t* tile, int lane) {
+  LaneTile t;
+  t.nib = ld16(tile + 16 * lane);
+  const int n = lane & 15;
+  const uint16_t* sp = reinterpret_cast<const uint16_t*>(tile + kTileNibbleBytes + 32 * (n >> 2) + 2 * (n & 3));
+#pragma unroll
+  for (int b = 0; b < 4; b++) t.sc[b] = sp[4 * b];
+  return t;
+}
+
+__device__ __forceinline__ float lane_scale(const LaneTile& t, int b) { return half_bits_to_float(t.sc[b]); }
+
+// Activation rows of one step, global memory straight into LDS
+// (global_load_lds_dwordx4): load j of wavefront w fills rows 4q..4q+3,
+// q = j*8 + w, lane i writing slot i%16 of row 4q + i/16.  Loads of rows at
+// or past n_rows (16 x active sub-tiles) are not issued.
+__device__ __forceinline__ void stage_rows(uint16_t* a, const uint16_t* base, int64_t ld, const int32_t* src, int k0,
+                                           int n_rows, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < kStageLoads; j++) {
+    const int q = j * kBfWaves + wave;
+    if (4 * q < n_rows) {
+      const int row = 4 * q + (lane >> 4);
+      const int piece = (lane & 15) ^ (row & 15);
+      const uint16_t* g = base + (int64_t)src[row] * ld + k0 + 8 * piece;
+      __builtin_amdgcn_global_load_lds(g, a + 4 * kBfStep * q, 16, 0, 0);
+    }
+  }
+}
+
+// Every LDS DMA load and weight load of this wavefront has landed.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A operand of sub-tile s, block b: row 16s + lane%16, elements 32b + 8*(lane/16) .. +7.
+__device__ __forceinline__ bf16x8 a_operand(const uint16_t* a, int s, int b, int lane) {
+  const int r = lane & 15;
+  return *reinterpret_cast<const bf16x8*>(a + (16 * s + r) * kBfStep + 8 * ((4 * b + (lane >> 4)) ^ r));
+}
+
+// acc[s][c] += A(s) x B(c) over one step for the NC column tiles in wt.
+template <int NC>
+__device__ __forceinline__ void step_mfma(const BfLds& sh, const uint16_t* a, const LaneTile (&wt)[NC], int n_sub,
+                                          int lane, f32x4 (&acc)[kBfSub][NC]) {
+#pragma unroll
+  for (int b = 0; b < 4; b++) {
+    bf16x8 bop[NC];
+#pragma unroll
+    for (int c = 0; c < NC; c++) bop[c] = dequant_bf16(sh.tbl, wt[c].nib[b], lane_scale(wt[c], b), lane & 31);
+#pragma unroll
+    for (int s = 0; s < kBfSub; s++) {
+      if (s < n_sub) {
+        const bf16x8 aop = a_operand(a, s, b, lane);
+#pragma unroll
+        for (int c = 0; c < NC; c++) acc[s][c] = mfma16x16x32(aop, bop[c], acc[s][c]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- gate / up
+
+// Workgroup = (tile, slab of 256 gate columns).  h[hrow][f] = bf16(silu(g) * u)
+// for hrow = bucketed position (routed) or T*K + token (shared).
+__global__ __launch_bounds__(kBfThreads) void k_gate_up_bf16(
+    const uint16_t* __restrict__ x, int H, int F, int K, int T, const uint8_t* __restrict__ arena,
+    const uint8_t* __restrict__ shared, int64_t expert_bytes, const int32_t* __restrict__ perm,
+    const Chunk* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int max_tiles, uint16_t* __restrict__ h) {
+  __shared__ BfLds sh;
+  const int tile_id = blockIdx.x % max_tiles;
+  const int slab = blockIdx.x / max_tiles;
+  if (tile_id >= *n_tiles) return;
+  const Chunk ch = tiles[tile_id];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool routed = ch.expert >= 0;
+  if (threadIdx.x < kBfRows) {
+    const int i = min((int)threadIdx.x, ch.count - 1);
+    sh.src[threadIdx.x] = routed ? perm[ch.first + i] / K : ch.first + i;
+  }
+  build_pair_table(sh.tbl);
+  __syncthreads();
+
+  const int n_sub = (ch.count + 15) >> 4;
+  const int n_rows = 16 * n_sub;
+  const int col0 = slab * (kBfWaves * kGuCols) + wave * kGuCols;
+  const bool cols_on = col0 < F;
+  const int64_t mat_bytes = expert_bytes / 3;
+  const uint8_t* ex = routed ? arena + (int64_t)ch.expert * expert_bytes : shared;
+  const int nkg = H / kBfStep;
+  const int rt0 = (cols_on ? col0 : 0) >> 4;
+  // column tiles: 0, 1 = gate rows rt0, rt0+1; 2, 3 = up rows rt0, rt0+1
+  const uint8_t* wbase[4] = {ex + (int64_t)rt0 * nkg * kTileBytes, ex + (int64_t)(rt0 + 1) * nkg * kTileBytes,
+                             ex + mat_bytes + (int64_t)rt0 * nkg * kTileBytes,
+                             ex + mat_bytes + (int64_t)(rt0 + 1) * nkg * kTileBytes};
+
+  f32x4 acc[kBfSub][4];
+#pragma unroll
+  for (int s = 0; s < kBfSub; s++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  stage_rows(sh.a[0], x, H, sh.src, 0, n_rows, wave, lane);
+  LaneTile wt[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) wt[c] = load_lane_tile(wbase[c], lane);
+  wait_loads();
+  __syncthreads();
+
+  for (int kt = 0; kt < nkg; kt++) {
+    const bool more = kt + 1 < nkg;
+    LaneTile wn[4];
+    if (more) {
+      stage_rows(sh.a[(kt + 1) & 1], x, H, sh.src, (kt + 1) * kBfStep, n_rows, wave, lane);
+#pragma unroll
+      for (int c = 0; c < 4; c++) wn[c] = load_lane_tile(wbase[c] + (int64_t)(kt + 1) * kTileBytes, lane);
+    }
+    if (cols_on) step_mfma<4>(sh, sh.a[kt & 1], wt, n_sub, lane, acc);
+    if (more) {
+#pragma unroll
+      for (int c = 0; c < 4; c++) wt[c] = wn[c];
+    }
+    wait_loads();
+    __syncthreads();
+  }
+
+  if (!cols_on) return;
+  const int TK = T * K;
+#pragma unroll
+  for (int s = 0; s < kBfSub; s++) {
+    if (s < n_sub) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int m = 16 * s + 4 * (lane >> 4) + v;
+        if (m < ch.count) {
+          const int64_t hrow = routed ? (int64_t)ch.first + m : (int64_t)TK + ch.first + m;
+#pragma unroll
+          for (int c = 0; c < 2; c++) {
+            const float g = acc[s][c][v], u = acc[s][c + 2][v];
+            const float hv = g / (1.0f + expf(-g)) * u;
+            h[hrow * F + col0 + 16 * c + (lane & 15)] = __builtin_bit_cast(uint16_t, (__bf16)hv);
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- down
+
+// Workgroup = (tile, slab of 512 output columns).  y[hrow][n] = sum_f Wd[n][f] h[hrow][f].
+__global__ __launch_bounds__(kBfThreads) void k_down_bf16(
+    int H, int F, int K, int T, const uint8_t* __restrict__ arena, const uint8_t* __restrict__ shared,
+    int64_t expert_bytes, const Chunk* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int max_tiles,
+    const uint16_t* __restrict__ h, float* __restrict__ y) {
+  __shared__ BfLds sh;
+  const int tile_id = blockIdx.x % max_tiles;
+  const int slab = blockIdx.x / max_tiles;
+  if (tile_id >= *n_tiles) return;
+  const Chunk ch = tiles[tile_id];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool routed = ch.expert >= 0;
+  const int TK = T * K;
+  const int64_t row0 = routed ? (int64_t)ch.first : (int64_t)TK + ch.first;
+  if (threadIdx.x < kBfRows) sh.src[threadIdx.x] = (int32_t)(row0 + min((int)threadIdx.x, ch.count - 1));
+  build_pair_table(sh.tbl);
+  __syncthreads();
+
+  const int n_sub = (ch.count + 15) >> 4;
+  const int n_rows = 16 * n_sub;
+  const int col0 = slab * (kBfWaves * kDnCols) + wave * kDnCols;
+  const bool cols_on = col0 < H;
+  const int64_t mat_bytes = expert_bytes / 3;
+  const uint8_t* ex = (routed ? arena + (int64_t)ch.expert * expert_bytes : shared) + 2 * mat_bytes;
+  const int nkg = F / kBfStep;
+  const int rt0 = (cols_on ? col0 : 0) >> 4;
+  const uint8_t* wbase[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) wbase[c] = ex + (int64_t)(rt0 + c) * nkg * kTileBytes;
+
+  f32x4 acc[kBfSub][4];
+#pragma unroll
+  for (int s = 0; s < kBfSub; s++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  stage_rows(sh.a[0], h, F, sh.src, 0, n_rows, wave, lane);
+  LaneTile wt[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) wt[c] = load_lane_tile(wbase[c], lane);
+  wait_loads();
+  __syncthreads();
+
+  for (int kt = 0; kt < nkg; kt++) {
+    const bool more = kt + 1 < nkg;
+    LaneTile wn[4];
+    if (more) {
+      stage_rows(sh.a[(kt + 1) & 1], h, F, sh.src, (kt + 1) * kBfStep, n_rows, wave, lane);
+#pragma unroll
+      for (int c = 0; c < 4; c++) wn[c] = load_lane_tile(wbase[c] + (int64_t)(kt + 1) * kTileBytes, lane);
+    }
+    if (cols_on) step_mfma<4>(sh, sh.a[kt & 1], wt, n_sub, lane, acc);
+    if (more) {
+#pragma unroll
+      for (int c = 0; c < 4; c++) wt[c] = wn[c];
+    }
+    wait_loads();
+    __syncthreads();
+  }
+
+  if (!cols_on) return;
+#pragma unroll
+  for (int s = 0; s < kBfSub; s++) {
+    if (s < n_sub) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int m = 16 * s + 4 * (lane >> 4) + v;
+        if (m < ch.count) {
+          float* yr = y + (row0 + m) * H + col0 + (lane & 15);
+#pragma unroll
+          for (int c = 0; c < 4; c++) yr[16 * c] = acc[s][c][v];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launcher
+
+hipError_t launch_ffn_bf16(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_tiles,
+                           const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
+                           const int32_t* pos, const float* w, const Chunk* tiles, const int32_t* n_tiles,
+                           uint16_t* h, float* y, float* out, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int gu_slabs = (F + kBfWaves * kGuCols - 1) / (kBfWaves * kGuCols);
+  const int dn_slabs = (H + kBfWaves * kDnCols - 1) / (kBfWaves * kDnCols);
+  clear_last_error();
+  hipLaunchKernelGGL(k_gate_up_bf16, dim3((unsigned)(max_tiles * gu_slabs)), dim3(kBfThreads), 0, stream, x, H, F, K,
+                     T, arena, shared, expert_bytes, perm, tiles, n_tiles, max_tiles, h);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  clear_last_error();
+  hipLaunchKernelGGL(k_down_bf16, dim3((unsigned)(max_tiles * dn_slabs)), dim3(kBfThreads), 0, stream, H, F, K, T,
+                     arena, shared, expert_bytes, tiles, n_tiles, max_tiles, h, y);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_combine(y, pos, w, T, K, H, n_shared, out, stream);
+}
+
+}  // namespace qmoe

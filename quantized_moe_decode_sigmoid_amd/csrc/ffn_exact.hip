@@ -113,9 +113,10 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat
     for (int i = 0; i < 4; i++) {
       float lo = d * bf16_bits_to_f32(a.u[i] & 0xffffu);
       float hi = d * bf16_bits_to_f32(a.u[i] >> 16);
-      if (bf16) {
-        lo = bf16_bits_to_f32(f32_to_bf16_rne(lo));
-        hi = bf16_bits_to_f32(f32_to_bf16_rne(hi));
+      if (bf16) {  // the conversion the bf16-contract FFN kernels use
+        const uint32_t pk = pack_bf16x2(lo, hi);
+        lo = bf16_bits_to_f32(pk & 0xffffu);
+        hi = bf16_bits_to_f32(pk >> 16);
       }
       o[2 * i] = lo;
       o[2 * i + 1] = hi;
@@ -325,6 +326,11 @@ hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n
                      arena, shared, expert_bytes, chunks, n_chunks, h_hi, h_lo, y);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  return launch_combine(y, pos, w, T, K, H, n_shared, out, stream);
+}
+
+hipError_t launch_combine(const float* y, const int32_t* pos, const float* w, int T, int K, int H, int n_shared,
+                          float* out, hipStream_t stream) {
   clear_last_error();
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)T), dim3(256), 0, stream, y, pos, w, T,
                      K, H, n_shared, out);

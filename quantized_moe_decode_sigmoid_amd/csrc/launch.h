@@ -11,12 +11,26 @@ namespace qmoe {
 hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
                          float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream);
 
-hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int n_shared, int32_t* counts, int32_t* offsets,
-                         int32_t* perm, int32_t* pos, Chunk* chunks, int32_t* n_chunks, hipStream_t stream);
+// chunk_rows: routes per work chunk (16 for the exact-weight kernels, kBfRows for the bf16 kernels)
+hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int n_shared, int chunk_rows, int32_t* counts,
+                         int32_t* offsets, int32_t* perm, int32_t* pos, Chunk* chunks, int32_t* n_chunks,
+                         hipStream_t stream);
 
 hipError_t launch_pack(const uint8_t* src, uint8_t* dst, int n_experts, int H, int F, hipStream_t stream);
 
 hipError_t launch_dequant(const uint8_t* mat, int rows, int cols, int bf16, float* out, hipStream_t stream);
+
+hipError_t launch_combine(const float* y, const int32_t* pos, const float* w, int T, int K, int H, int n_shared,
+                          float* out, hipStream_t stream);
+
+// ---- bf16 grouped MFMA path (ffn_bf16.hip)
+
+constexpr int kBfRows = 128;  // routes per tile
+
+hipError_t launch_ffn_bf16(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_tiles,
+                           const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
+                           const int32_t* pos, const float* w, const Chunk* tiles, const int32_t* n_tiles,
+                           uint16_t* h, float* y, float* out, hipStream_t stream);
 
 hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_chunks,
                             const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,

@@ -182,6 +182,17 @@ def zipf_bias(shape: Shape, lam: float, layer: int = 0, seed: int | None = None)
     return (-lam * shape.zipf_s * np.log(rank.astype(np.float64))).astype(np.float32)
 
 
+ZIPF_LAMBDA_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden",
+                                "zipf_lambda.json")
+
+
+def zipf_lambda(shape: Shape) -> float:
+    """The bias strength calibrated for a skewed workload (tests/golden/make_zipf_lambda.py)."""
+    import json
+    with open(ZIPF_LAMBDA_FILE) as f:
+        return float(json.load(f)[shape.name]["lam"])
+
+
 def layer_inputs(shape: Shape, layer: int = 0, seed: int | None = None, lam: float = 0.0) -> dict:
     """Everything one layer consumes except the activations."""
     bias = zipf_bias(shape, lam, layer, seed) if shape.zipf_s and lam else None

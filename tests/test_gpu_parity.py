@@ -261,3 +261,64 @@ def test_graph_replay_of_decode_calls():
         _ = dl.forward(xd[rep:rep + 1])  # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.view(np.uint32)), rep
+
+
+# ---------------------------------------------------------------- bf16 grouped MFMA path
+
+def test_layer_tiny_bf16():
+    layer_parity("tiny", 4, precision=qm.PREC_BF16)
+    layer_parity("tiny", 1, first=5, precision=qm.PREC_BF16)
+    layer_parity("tiny", 37, first=20, precision=qm.PREC_BF16)
+
+
+def test_layer_bf16_tiles_past_128_rows():
+    """Every token on experts 0..K-1: 300 routes per expert and 300 shared rows = tiles of 128, 128, 44."""
+    s, _ = workload("tiny")
+    bias = np.zeros(s.n_experts, np.float32)
+    bias[:s.top_k] = 10.0
+    layer_parity("tiny", 300, first=3, bias=bias, precision=qm.PREC_BF16)
+
+
+def test_layer_batch_128_bf16_sampled():
+    layer_parity("batch", 128, sample=[0, 1, 17, 63, 64, 100, 127], precision=qm.PREC_BF16)
+
+
+def prefill_bias():
+    s, _ = workload("prefill")
+    return synth.zipf_bias(s, synth.zipf_lambda(s))
+
+
+def test_layer_prefill_full_size_sampled():
+    """T=2048, H=2048, 256 experts top-8 + shared, ffn 512, Zipf(1.0) popularity (AUTO -> bf16)."""
+    s, _ = workload("prefill")
+    rng = np.random.default_rng(11)
+    rows = sorted(set([0, 1, 127, 128, 1023, 2047] + rng.choice(2048, 18, replace=False).tolist()))
+    out = layer_parity("prefill", 2048, first=0, sample=rows, bias=prefill_bias())
+    assert np.all(np.isfinite(out))
+
+
+def test_layer_prefill_deterministic_and_order_equivariant():
+    s, inp, dl = device_layer("prefill", bias=prefill_bias())
+    x = synth.tokens(s, 2048, first=4096)
+    log("determinism prefill T=2048")
+    a = dl.forward(to_dev_bf16(x)).cpu().numpy()
+    b = dl.forward(to_dev_bf16(x)).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    perm = np.random.default_rng(6).permutation(2048)
+    c = dl.forward(to_dev_bf16(x[perm])).cpu().numpy()
+    assert np.array_equal(a[perm].view(np.uint32), c.view(np.uint32))
+
+
+def test_bf16_and_fp32_contracts_agree_on_a_batch():
+    """The two FFN contracts differ only by the bf16 roundings of weights and h."""
+    s, inp = workload("batch")
+    x = synth.tokens(s, 32, first=300)
+    outs = {}
+    for prec in (qm.PREC_FP32, qm.PREC_BF16):
+        _, _, dl = device_layer("batch", prec)
+        log(f"batch T=32 precision={prec}")
+        outs[prec] = dl.forward(to_dev_bf16(x)).cpu().numpy()
+    a, b = outs[qm.PREC_FP32].astype(np.float64), outs[qm.PREC_BF16].astype(np.float64)
+    r = np.linalg.norm(a - b) / np.linalg.norm(a)
+    print(f"[parity] fp32 vs bf16 contract rel_l2={r:.3e}", flush=True)
+    assert 0 < r < 2e-2
