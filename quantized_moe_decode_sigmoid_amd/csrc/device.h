@@ -34,19 +34,36 @@ constexpr int kTileNibbleBytes = 1024; // 64 lane slots x 16 bytes
 constexpr int kPairTableWords = 256 * 32;
 
 // The IQ4_NL levels (ggml definition of the format).
+constexpr int kIq4nlLevels[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
+
+// Levels 4w..4w+3 as signed bytes of one word.
+constexpr uint32_t iq4nl_level_word(int w) {
+  return (uint32_t)(uint8_t)kIq4nlLevels[4 * w] | ((uint32_t)(uint8_t)kIq4nlLevels[4 * w + 1] << 8) |
+         ((uint32_t)(uint8_t)kIq4nlLevels[4 * w + 2] << 16) | ((uint32_t)(uint8_t)kIq4nlLevels[4 * w + 3] << 24);
+}
+
+// Level of index q, selected from immediate words: no memory access (a table
+// in memory would make every table build wait behind the weight loads that
+// are already in flight).
 __device__ __forceinline__ int iq4nl_level(int q) {
-  constexpr int kLevels[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
-  return kLevels[q & 15];
+  const uint32_t lo = (q & 4) ? iq4nl_level_word(1) : iq4nl_level_word(0);
+  const uint32_t hi = (q & 4) ? iq4nl_level_word(3) : iq4nl_level_word(2);
+  const uint32_t w = (q & 8) ? hi : lo;
+  return (int)(int8_t)(uint8_t)(w >> (8 * (q & 3)));
 }
 
 // bf16 bits of a small integer (exact: at most 8 significant bits).
 __device__ __forceinline__ uint32_t small_int_bf16(int v) { return __float_as_uint((float)v) >> 16; }
 
-// Fill the replicated pair table; every thread of the block takes part.
+// Fill the replicated pair table; every thread of the block takes part.  Each
+// step computes one entry and writes 4 of its 32 copies with one 16-byte
+// store.
 __device__ __forceinline__ void build_pair_table(uint32_t* tbl) {
-  for (int i = threadIdx.x; i < kPairTableWords; i += blockDim.x) {
-    const int v = i >> 5;
-    tbl[i] = small_int_bf16(iq4nl_level(v & 15)) | (small_int_bf16(iq4nl_level(v >> 4)) << 16);
+  for (int i = threadIdx.x; i < kPairTableWords / 4; i += blockDim.x) {
+    const int v = i >> 3;
+    const uint32_t e = small_int_bf16(iq4nl_level(v & 15)) | (small_int_bf16(iq4nl_level(v >> 4)) << 16);
+    uint32_t __attribute__((ext_vector_type(4))) q = {e, e, e, e};
+    *reinterpret_cast<decltype(q)*>(tbl + 4 * i) = q;
   }
 }
 

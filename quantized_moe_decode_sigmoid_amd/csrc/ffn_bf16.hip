@@ -45,7 +45,7 @@ constexpr int kStageLoads = kBfRows / 4 / kBfWaves;  // 1 KB LDS DMA loads per w
 // destinations must lie in the first 64 KB of the workgroup's LDS.
 struct BfLds {
   uint16_t a[2][kBfRows * kBfStep];
-  uint32_t tbl[kPairTableWords];
+  __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
   int32_t src[kBfRows];  // source row of each tile row (x row or h row)
 };
 static_assert(sizeof(uint16_t) * 2 * kBfRows * kBfStep <= 65536, "LDS DMA destinations beyond 64 KB");

@@ -87,7 +87,7 @@ __global__ void k_pack(const uint8_t* __restrict__ src, uint8_t* __restrict__ ds
 // bf16 = 0: exact d*level in fp32; bf16 = 1: that value rounded to bf16.
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat, int rows, int cols, int bf16,
                                                  float* __restrict__ out) {
-  __shared__ uint32_t tbl[kPairTableWords];
+  __shared__ __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
   build_pair_table(tbl);
   __syncthreads();
   const int lane = threadIdx.x & 63;
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up_exact(
     const uint8_t* __restrict__ shared, int64_t expert_bytes, const int32_t* __restrict__ perm,
     const Chunk* __restrict__ chunks, const int32_t* __restrict__ n_chunks, uint16_t* __restrict__ h_hi,
     uint16_t* __restrict__ h_lo) {
-  __shared__ uint32_t tbl[kPairTableWords];
+  __shared__ __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
   __shared__ f32x4 red[2][4][64];
   const int n_rt = F >> 4;
   const int chunk_id = blockIdx.x / n_rt;
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kFfnThreads) void k_down_exact(
     int H, int F, int K, int T, const uint8_t* __restrict__ arena, const uint8_t* __restrict__ shared,
     int64_t expert_bytes, const Chunk* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, float* __restrict__ y) {
-  __shared__ uint32_t tbl[kPairTableWords];
+  __shared__ __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
   __shared__ f32x4 red[4][64];
   const int n_rt = H >> 4;
   const int chunk_id = blockIdx.x / n_rt;

