@@ -39,10 +39,13 @@ namespace qmoe {
 constexpr int kDecThreads = 1024;
 constexpr int kDecWaves = kDecThreads / 64;
 constexpr int kGuSplit = kDecWaves / 2;  // waves per matrix in gate/up: each takes 1/kGuSplit of H
-constexpr int kDnSplit = kDecWaves / 2;  // waves per row tile in down: each takes 1/kDnSplit of F
+// Down: two 16-row tiles of H per workgroup; wave w takes row tile w & 1 and
+// packed tile kg = w >> 1 of the F/128 tiles of a row.
+constexpr int kDnWavesPerRowTile = kDecWaves / 2;
+static_assert(kMaxDecodeFfn / 128 <= kDnWavesPerRowTile, "one packed tile per wave in down");
 static_assert(kDecWaves == 16, "the LDS DMA staging assigns its loads to 16 wavefronts");
 constexpr int kGuMaxKg = (kMaxDecodeHidden / 128 + kGuSplit - 1) / kGuSplit;  // gate/up tiles per wave
-constexpr int kDnMaxKg = (kMaxDecodeFfn / 128 + kDnSplit - 1) / kDnSplit;     // down tiles per wave and expert
+
 constexpr int kDnSlots = kMaxDecodeK + 1;             // routed slots + shared
 constexpr uint32_t kNotReady = 0xffffffffu;           // an h word before it is written
 constexpr uint32_t kPollLimit = 1u << 20;
@@ -77,6 +80,14 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 // Every load of this wavefront (LDS DMA included) has landed.
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Every load of this wavefront but the last N (vector loads complete in
+// order) has landed: the LDS DMA issued before N register loads.
+template <int N>
+__device__ __forceinline__ void wait_dma_before() {
+  static_assert(N >= 0 && N <= 15, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ bool ready(uint4 v) {
   return v.x != kNotReady && v.y != kNotReady && v.z != kNotReady && v.w != kNotReady;
 }
@@ -93,17 +104,19 @@ struct RouteLds {
   int32_t ids[kMaxDecodeK];
 };
 
+constexpr int kGuMaxRowTiles = 1;  // row tiles of F per gate/up workgroup
+
 struct GateUpLds {
-  uint16_t x[kMaxDecodeHidden];                             // the token's activations
-  uint32_t scales[2][kMaxDecodeHidden / 128][kScaleWords];  // [gate/up][kg] of this row tile
-  f32x4 red[kDecWaves][64];
+  uint16_t x[kMaxDecodeHidden];                                                // the token's activations
+  uint32_t scales[kGuMaxRowTiles][2][kMaxDecodeHidden / 128][kScaleWords];  // [row tile][gate/up][kg]
+  f32x4 red[kGuMaxRowTiles][kDecWaves][4];                                  // column 0 of each wave's acc
 };
 
 struct DownLds {
-  uint32_t scales[kDnSlots][2][kMaxDecodeFfn / 128][kScaleWords];  // [slot][rtl][kg]
+  uint32_t scales[kDnSlots][2][kMaxDecodeFfn / 128][kScaleWords];  // [slot][row tile][kg]
   uint16_t hh[kDnSlots][kMaxDecodeFfn];                            // bf16(h)
   uint16_t hl[kDnSlots][kMaxDecodeFfn];                            // bf16(h - bf16(h))
-  float part[kDecWaves][kDnSlots][16];                             // column 0 of each wave's partial
+  float part[kDecWaves][kDnSlots][16];                             // column 0 + 1 of each wave's partial
   float y[kDnSlots][32];
 };
 
@@ -187,7 +200,9 @@ __device__ __forceinline__ void route_local(const DecodeArgs& a, RouteLds& r) { 
 
 // waves 0-3: W_gate over quarters of the blocks of H; waves 4-7: W_up.
 // h of (row 16rt + 4G + i) is written to hw[slot][...] as bf16 hi | lo << 16.
-__device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, int rt, ExpertsLds& sh) {
+template <int NRT>
+__device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, int rt0, ExpertsLds& sh) {
+  static_assert(NRT >= 1 && NRT <= kGuMaxRowTiles, "row tiles per workgroup");
   GateUpLds& g = sh.u.g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, G = lane >> 4;
@@ -195,35 +210,45 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
   const int nkg = a.H >> 7;
   const int q = wave % kGuSplit, mat = wave / kGuSplit;
   const int kg0 = q * nkg / kGuSplit, nk = (q + 1) * nkg / kGuSplit - kg0;
-  const uint8_t* rowtiles = ex + (int64_t)rt * nkg * kTileBytes;  // gate; up is mat_bytes further
+  const int64_t rt_bytes = (int64_t)nkg * kTileBytes;
+  const uint8_t* rowtiles = ex + rt0 * rt_bytes;  // gate of row tile rt0; up is mat_bytes further
 
-  // 1. this wave's nibble words, the row tile's scales, the activations: all requested now
-  u32x4 nib[kGuMaxKg];
+  // 1. the row tiles' scales (16-byte piece p = 64 j + lane of [matrix][kg][8]
+  //    of row tile t, for j = 0..7) and x (piece p of the row) by LDS DMA,
+  //    one wave load each, pieces past the matrix repeating a valid one (never
+  //    read); then this wave's nibble words.  Only the DMA is waited for
+  //    before the MFMAs: each tile's MFMAs start when its words have landed.
+  for (int j = wave; j < 8 * NRT + 8; j += kDecWaves) {
+    if (j < 8 * NRT) {
+      const int t = j >> 3, p = 64 * (j & 7) + lane, m = p >> 8, kg = min((p >> 3) & 31, nkg - 1);
+      dma16(rowtiles + t * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
+            &g.scales[t][0][0][0] + 256 * (j & 7));
+    } else {
+      const int p = 64 * (j - 8 * NRT) + lane;
+      dma16(a.x + 8 * min(p, (a.H >> 3) - 1), &g.x[512 * (j - 8 * NRT)]);
+    }
+  }
+  asm volatile("" ::: "memory");  // keep the nibble loads after the DMA
+  u32x4 nib[NRT][kGuMaxKg];
 #pragma unroll
-  for (int i = 0; i < kGuMaxKg; i++) {
-    const int kg = min(kg0 + i, nkg - 1);
-    nib[i] = ld16(rowtiles + mat * mat_bytes + (int64_t)kg * kTileBytes + 16 * lane);
-  }
-  // scales (waves 0-7: 16-byte piece p = 64 wave + lane of [matrix][kg][8]) and
-  // x (waves 8-15: piece p of the row) by LDS DMA; pieces past the matrix
-  // repeat a valid one and are never read
-  if (wave < 8) {
-    const int p = 64 * wave + lane, m = p >> 8, kg = min((p >> 3) & 31, nkg - 1);
-    dma16(rowtiles + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
-          &g.scales[0][0][0] + 256 * wave);
-  } else {
-    const int p = 64 * (wave - 8) + lane;
-    dma16(a.x + 8 * min(p, (a.H >> 3) - 1), &g.x[512 * (wave - 8)]);
-  }
+  for (int t = 0; t < NRT; t++)
+#pragma unroll
+    for (int i = 0; i < kGuMaxKg; i++) {
+      const int kg = min(kg0 + i, nkg - 1);
+      nib[t][i] = ld16(rowtiles + t * rt_bytes + mat * mat_bytes + (int64_t)kg * kTileBytes + 16 * lane);
+    }
   build_pair_table(sh.tbl);
-  wait_loads();
+  wait_dma_before<NRT * kGuMaxKg>();
   __syncthreads();
 
   // 2. MFMAs: every column carries the token (a broadcast operand), column 0
-  //    is kept; acc[i] (row 4G+i) += d * (levels . x).  Tiles past this
-  //    wave's range are skipped (a branch uniform over the wavefront).
+  //    is kept; acc[t][i] (row 4G+i of row tile t) += d * (levels . x).
+  //    Tiles past this wave's range are skipped (a branch uniform over the
+  //    wavefront).
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc = zero;
+  f32x4 acc[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; t++) acc[t] = zero;
 #pragma unroll
   for (int i = 0; i < kGuMaxKg; i++) {
     if (i >= nk) continue;
@@ -231,24 +256,31 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
 #pragma unroll
     for (int b = 0; b < 4; b++) {
       const bf16x8 xb = *reinterpret_cast<const bf16x8*>(&g.x[32 * (4 * kg + b) + 8 * G]);
-      const bf16x8 wa = decode_word(sh.tbl, uword(nib[i], b), lane & 31);
-      const uint32_t s01 = g.scales[mat][kg][8 * G + 2 * b];
-      const uint32_t s23 = g.scales[mat][kg][8 * G + 2 * b + 1];
-      const f32x4 cc = mfma16x16x32(wa, xb, zero);
-      acc[0] = __builtin_fmaf(half_bits_to_float(s01), cc[0], acc[0]);
-      acc[1] = __builtin_fmaf(half_bits_to_float(s01 >> 16), cc[1], acc[1]);
-      acc[2] = __builtin_fmaf(half_bits_to_float(s23), cc[2], acc[2]);
-      acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), cc[3], acc[3]);
+#pragma unroll
+      for (int t = 0; t < NRT; t++) {
+        const bf16x8 wa = decode_word(sh.tbl, uword(nib[t][i], b), lane & 31);
+        const uint32_t s01 = g.scales[t][mat][kg][8 * G + 2 * b];
+        const uint32_t s23 = g.scales[t][mat][kg][8 * G + 2 * b + 1];
+        const f32x4 cc = mfma16x16x32(wa, xb, zero);
+        acc[t][0] = __builtin_fmaf(half_bits_to_float(s01), cc[0], acc[t][0]);
+        acc[t][1] = __builtin_fmaf(half_bits_to_float(s01 >> 16), cc[1], acc[t][1]);
+        acc[t][2] = __builtin_fmaf(half_bits_to_float(s23), cc[2], acc[t][2]);
+        acc[t][3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), cc[3], acc[t][3]);
+      }
     }
   }
-  g.red[wave][lane] = acc;
+  if (c == 0)
+#pragma unroll
+    for (int t = 0; t < NRT; t++) g.red[t][wave][G] = acc[t];
   __syncthreads();
-  // 3. wave 0, column 0: g and u summed in wave order, h = silu(g) * u
-  if (wave == 0 && c == 0) {
-    f32x4 gs = g.red[0][lane], us = g.red[kGuSplit][lane];
+  // 3. wave t, column 0: g and u of row tile t summed in wave order,
+  //    h = silu(g) * u
+  if (wave < NRT && c == 0) {
+    const int t = wave;
+    f32x4 gs = g.red[t][0][G], us = g.red[t][kGuSplit][G];
     for (int w = 1; w < kGuSplit; w++) {
-      gs += g.red[w][lane];
-      us += g.red[kGuSplit + w][lane];
+      gs += g.red[t][w][G];
+      us += g.red[t][kGuSplit + w][G];
     }
     uint32_t hw4[4];
 #pragma unroll
@@ -259,32 +291,29 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
       const uint32_t lb = f32_to_bf16_rne(h - bf16_bits_to_f32(hb));
       hw4[i] = hb | (lb << 16);
     }
-    const int off = (int)(((int64_t)slot * a.F + 16 * rt + 4 * G) * 4);
+    const int off = (int)(((int64_t)slot * a.F + 16 * (rt0 + t) + 4 * G) * 4);
     st_dev_x4(buffer_of(a.hw), off, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
   }
 }
 
 // ---------------------------------------------------------------- down role
 
-// the down tiles of routed slot S (S >= K repeats slot 0; those values are not used)
+// this wave's down tile (row tile rt, tile kg) of routed slot S (S >= K
+// repeats slot 0; those values are not used)
 template <int S>
-__device__ __forceinline__ void load_routed_slots(const DecodeArgs& a, const RouteLds& r, u32x4 (&nib)[kDnSlots][kDnMaxKg],
-                                                  int rt, int kg0, int nkg) {
+__device__ __forceinline__ void load_routed_slots(const DecodeArgs& a, const RouteLds& r, u32x4 (&nib)[kDnSlots], int rt,
+                                                  int kg, int nkg) {
   if constexpr (S < kMaxDecodeK) {
     const int64_t mat_bytes = a.expert_bytes / 3;
     const uint8_t* down = a.arena + (int64_t)r.ids[S < a.K ? S : 0] * a.expert_bytes + 2 * mat_bytes;
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int i = 0; i < kDnMaxKg; i++)
-      nib[S][i] = ld16(down + ((int64_t)rt * nkg + min(kg0 + i, nkg - 1)) * kTileBytes + 16 * lane);
-    load_routed_slots<S + 1>(a, r, nib, rt, kg0, nkg);
+    nib[S] = ld16(down + ((int64_t)rt * nkg + kg) * kTileBytes + 16 * (threadIdx.x & 63));
+    load_routed_slots<S + 1>(a, r, nib, rt, kg, nkg);
   }
 }
 
 // The scale pieces of one expert's two row tiles (2 x 8 kg x 8 pieces of 16
-// bytes) into d.scales[slot] by LDS DMA, half per wavefront: call from the
-// two wavefronts with half = 0, 1.  Pieces of kg >= nkg repeat a valid one
-// and are never read.
+// bytes) into d.scales[slot] by LDS DMA, half per wavefront (half = 0, 1).
+// Pieces of kg >= nkg repeat a valid one and are never read.
 __device__ __forceinline__ void dma_slot_scales(DownLds& d, const uint8_t* down_rows, int nkg, int slot, int half) {
   const int p = 64 * half + (threadIdx.x & 63);
   const int rtl = p >> 6, kg = min((p >> 3) & 7, nkg - 1);
@@ -292,135 +321,128 @@ __device__ __forceinline__ void dma_slot_scales(DownLds& d, const uint8_t* down_
         &d.scales[slot][0][0][0] + 256 * half);
 }
 
-// MFMAs of slot S for this wave's quarter of F (column 0 kept; every column
-// carries the same broadcast h operand); the partial goes to d.part.
+// MFMAs of slot S over this wave's tile.  Column 0 of the B operand carries
+// bf16(h), column 1 bf16(h - bf16(h)) (the other columns repeat column 0 and
+// are not used): one MFMA per block gives both products, each lane
+// accumulates d * C of its column, and column 0 + column 1 of the C rows is
+// this wave's partial, written to d.part.
 template <int S>
-__device__ __forceinline__ void down_slots(const DecodeArgs& a, ExpertsLds& sh, const u32x4 (&nib)[kDnSlots][kDnMaxKg],
-                                           int kg0, int nk, int nkg) {
-  if constexpr (S < kDnSlots) {
-    DownLds& d = sh.u.d;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int c = lane & 15, G = lane >> 4, rtl = wave & 1;
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    f32x4 acc = zero;
+__device__ __forceinline__ void down_slot(ExpertsLds& sh, const u32x4 (&nib)[kDnSlots], int rtl, int kg) {
+  DownLds& d = sh.u.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, G = lane >> 4;
+  const uint16_t* hp = c == 1 ? d.hl[S] : d.hh[S];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kDnMaxKg; i++) {
-      if (i >= nk) continue;
-      const int kg = min(kg0 + i, nkg - 1);
-#pragma unroll
-      for (int b = 0; b < 4; b++) {
-        const int b32 = 4 * kg + b;
-        // elements 32 b32 + 8G .. + 7 of both halves
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&d.hh[S][32 * b32 + 8 * G]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&d.hl[S][32 * b32 + 8 * G]);
-        const bf16x8 wa = decode_word(sh.tbl, uword(nib[S][i], b), lane & 31);
-        const uint32_t s01 = d.scales[S][rtl][kg][8 * G + 2 * b];
-        const uint32_t s23 = d.scales[S][rtl][kg][8 * G + 2 * b + 1];
-        f32x4 cc = mfma16x16x32(wa, bh, zero);
-        cc = mfma16x16x32(wa, bl, cc);
-        acc[0] = __builtin_fmaf(half_bits_to_float(s01), cc[0], acc[0]);
-        acc[1] = __builtin_fmaf(half_bits_to_float(s01 >> 16), cc[1], acc[1]);
-        acc[2] = __builtin_fmaf(half_bits_to_float(s23), cc[2], acc[2]);
-        acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), cc[3], acc[3]);
-      }
-    }
-    if (c == 0) *reinterpret_cast<f32x4*>(&d.part[wave][S][4 * G]) = acc;
-    down_slots<S + 1>(a, sh, nib, kg0, nk, nkg);
+  for (int b = 0; b < 4; b++) {
+    const bf16x8 bop = *reinterpret_cast<const bf16x8*>(hp + 32 * (4 * kg + b) + 8 * G);
+    const bf16x8 wa = decode_word(sh.tbl, uword(nib[S], b), lane & 31);
+    const uint32_t s01 = d.scales[S][rtl][kg][8 * G + 2 * b];
+    const uint32_t s23 = d.scales[S][rtl][kg][8 * G + 2 * b + 1];
+    const f32x4 cc = mfma16x16x32(wa, bop, zero);
+    acc[0] = __builtin_fmaf(half_bits_to_float(s01), cc[0], acc[0]);
+    acc[1] = __builtin_fmaf(half_bits_to_float(s01 >> 16), cc[1], acc[1]);
+    acc[2] = __builtin_fmaf(half_bits_to_float(s23), cc[2], acc[2]);
+    acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), cc[3], acc[3]);
   }
+#pragma unroll
+  for (int j = 0; j < 4; j++) acc[j] += __shfl_down(acc[j], 1, 64);
+  if (c == 0) *reinterpret_cast<f32x4*>(&d.part[wave][S][4 * G]) = acc;
+}
+
+// Routed slots S.. in order (slots >= K are skipped).
+template <int S>
+__device__ __forceinline__ void down_routed_slots(const DecodeArgs& a, ExpertsLds& sh, const u32x4 (&nib)[kDnSlots],
+                                                  int rtl, int kg) {
+  if constexpr (S < kMaxDecodeK) {
+    if (S < a.K) down_slot<S>(sh, nib, rtl, kg);
+    down_routed_slots<S + 1>(a, sh, nib, rtl, kg);
+  }
+}
+
+// Rows first .. first+n-1 of the h words (row r = slot r; row K = the shared
+// expert, kept in LDS slot kMaxDecodeK), read until complete -- each thread
+// one 16-byte piece, all requested together, re-read while one shows the
+// "not ready" pattern -- and split into the two bf16 planes.
+__device__ __forceinline__ void poll_h_rows(const DecodeArgs& a, DownLds& d, int first, int n) {
+  const __amdgpu_buffer_rsrc_t rh = buffer_of(a.hw);
+  const int row_pieces = a.F >> 2;
+  const int p = threadIdx.x;
+  if (p >= n * row_pieces) return;
+  const int row = first + p / row_pieces, e0 = 4 * (p % row_pieces);
+  const int off = (row * a.F + e0) * 4;
+  uint4 v = ld_dev_x4(rh, off);
+  uint32_t it = 0;
+  while (!ready(v)) {
+    if (++it > kPollLimit) {
+      a.err[0] = 1u;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_dev_x4(rh, off);
+  }
+  const int slot = row < a.K ? row : kMaxDecodeK;
+  *reinterpret_cast<uint2*>(&d.hh[slot][e0]) =
+      make_uint2((v.x & 0xffffu) | (v.y << 16), (v.z & 0xffffu) | (v.w << 16));
+  *reinterpret_cast<uint2*>(&d.hl[slot][e0]) =
+      make_uint2((v.x >> 16) | (v.y & 0xffff0000u), (v.z >> 16) | (v.w & 0xffff0000u));
 }
 
 __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   DownLds& d = sh.u.d;
   RouteLds& r = sh.route;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, G = lane >> 4;
-  const int rtl = wave & 1, q = wave >> 1;  // q: which 1/kDnSplit of F
-  const int rt = 2 * blk + rtl;
-  (void)rtl;
+  const int rtl = wave & 1, kg = wave >> 1;
+  const int rt = 2 * blk + rtl;  // this wave's 16 rows of H
   const int nkg = a.F >> 7;
-  const int kg0 = q * nkg / kDnSplit, nk = (q + 1) * nkg / kDnSplit - kg0;
+  const bool has_tile = kg < nkg;
+  const int kgc = has_tile ? kg : nkg - 1;
   const int64_t mat_bytes = a.expert_bytes / 3;
-  const int n_rows = a.K + a.n_shared;  // h rows: routed slots 0..K-1, then the shared expert at K
 
   auto down_tiles = [&](const uint8_t* ex, int rtile) {
     return ex + 2 * mat_bytes + (int64_t)rtile * nkg * kTileBytes;
   };
-  u32x4 nib[kDnSlots][kDnMaxKg];
+  u32x4 nib[kDnSlots];
   // 1. the router scores, then the shared expert's tiles (they need no routing)
   const RouteIn rin = route_fetch(a);
   const uint8_t* shx = a.n_shared ? a.shared : a.arena;
-#pragma unroll
-  for (int i = 0; i < kDnMaxKg; i++)
-    nib[kMaxDecodeK][i] = ld16(down_tiles(shx, rt) + (int64_t)min(kg0 + i, nkg - 1) * kTileBytes + 16 * lane);
+  nib[kMaxDecodeK] = ld16(down_tiles(shx, rt) + (int64_t)kgc * kTileBytes + 16 * lane);
   if (wave < 2) dma_slot_scales(d, down_tiles(shx, 2 * blk), nkg, kMaxDecodeK, wave);
   build_pair_table(sh.tbl);
   // 2. routing, then the routed experts' tiles
   route_rank(a, r, rin);
-  load_routed_slots<0>(a, r, nib, rt, kg0, nkg);
+  load_routed_slots<0>(a, r, nib, rt, kgc, nkg);
   if (wave >= 2 && wave < 2 + 2 * a.K) {
     const int slot = (wave - 2) >> 1;
     dma_slot_scales(d, down_tiles(a.arena + (int64_t)r.ids[slot] * a.expert_bytes, 2 * blk), nkg, slot, wave & 1);
   }
-  // 3. h of every slot, read until complete: each thread requests all its
-  //    pieces, then re-reads the ones still "not ready"
-  {
-    const __amdgpu_buffer_rsrc_t rh = buffer_of(a.hw);
-    const int row_pieces = a.F >> 2;  // 16-byte pieces per row
-    const int n_total = n_rows * row_pieces;
-    constexpr int kMaxPieces = (kDnSlots * kMaxDecodeFfn / 4 + kDecThreads - 1) / kDecThreads;
-    uint4 v[kMaxPieces];
-    int boff[kMaxPieces];
-#pragma unroll
-    for (int j = 0; j < kMaxPieces; j++) {
-      const int p = min((int)threadIdx.x + j * kDecThreads, n_total - 1);
-      boff[j] = (p / row_pieces * a.F + 4 * (p % row_pieces)) * 4;
-      v[j] = ld_dev_x4(rh, boff[j]);
-    }
-    uint32_t it = 0;
-    bool all = false;
-    while (!all) {
-      all = true;
-#pragma unroll
-      for (int j = 0; j < kMaxPieces; j++) all = all && ready(v[j]);
-      if (all) break;
-      if (++it > kPollLimit) {
-        a.err[0] = 1u;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int j = 0; j < kMaxPieces; j++)
-        if (!ready(v[j])) v[j] = ld_dev_x4(rh, boff[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < kMaxPieces; j++) {
-      const int p = (int)threadIdx.x + j * kDecThreads;
-      if (p < n_total) {
-        const int row = p / row_pieces, slot = row < a.K ? row : kMaxDecodeK, e0 = 4 * (p % row_pieces);
-        // split the words into the two bf16 planes
-        *reinterpret_cast<uint2*>(&d.hh[slot][e0]) =
-            make_uint2((v[j].x & 0xffffu) | (v[j].y << 16), (v[j].z & 0xffffu) | (v[j].w << 16));
-        *reinterpret_cast<uint2*>(&d.hl[slot][e0]) =
-            make_uint2((v[j].x >> 16) | (v[j].y & 0xffff0000u), (v[j].z >> 16) | (v[j].w & 0xffff0000u));
-      }
-    }
-  }
-  wait_loads();  // the scale pieces (LDS DMA)
-  __syncthreads();
-  // 4. every slot's MFMAs, then the kDnSplit parts of each (row tile, slot)
-  //    added in order
-  {
-    down_slots<0>(a, sh, nib, kg0, nk, nkg);
+  // 3. h of the shared expert (made first) and its MFMAs, while the routed
+  //    experts' h is still being made
+  static_assert(kMaxDecodeK * (kMaxDecodeFfn / 4) <= kDecThreads, "one h piece per thread");
+  if (a.n_shared) {
+    poll_h_rows(a, d, a.K, 1);
+    wait_loads();  // this wave's tiles and scale pieces (LDS DMA)
     __syncthreads();
-    for (int i = threadIdx.x; i < kDnSlots * 32; i += kDecThreads) {
-      const int s2 = i >> 5, row = i & 31, rt2 = row >> 4, r16 = row & 15;
-      float t = d.part[rt2][s2][r16];
-      for (int qq = 1; qq < kDnSplit; qq++) t += d.part[rt2 + 2 * qq][s2][r16];
+    if (has_tile) down_slot<kMaxDecodeK>(sh, nib, rtl, kg);
+  }
+  // 4. h of the routed slots and their MFMAs
+  poll_h_rows(a, d, 0, a.K);
+  wait_loads();
+  __syncthreads();
+  if (has_tile) down_routed_slots<0>(a, sh, nib, rtl, kg);
+  __syncthreads();
+  // 5. the wave parts of each (row tile, slot) added in order
+  for (int i = threadIdx.x; i < kDnSlots * 32; i += kDecThreads) {
+    const int s2 = i >> 5, row = i & 31, rt2 = row >> 4, r16 = row & 15;
+    if (s2 < a.K || (s2 == kMaxDecodeK && a.n_shared)) {
+      float t = 0.0f;
+      for (int q = 0; q < nkg; q++) t += d.part[rt2 + 2 * q][s2][r16];
       d.y[s2][row] = t;
     }
-    __syncthreads();
   }
-  // 5. slot-order combine of these 32 rows
+  __syncthreads();
+  // 6. slot-order combine of these 32 rows
   if (threadIdx.x < 32) {
     const int row = threadIdx.x;
     float acc = 0.0f;
@@ -441,14 +463,20 @@ __global__ __launch_bounds__(kDecThreads, 8) void k_decode_experts(DecodeArgs a)
   __shared__ ExpertsLds sh;
   int blk = blockIdx.x;
   const int n_rt_f = a.F >> 4;
-  if (blk < a.n_shared_wg) {
-    gate_up_role(a, a.shared, a.K, blk, sh);
-  } else if ((blk -= a.n_shared_wg) < a.n_routed_wg) {
+  // Block order: routed gate/up, shared gate/up, down.  Every producer of an
+  // h word has a lower block index than every workgroup that waits for it,
+  // so the kernel completes whatever number of workgroups is resident.
+  // Workgroups are placed in block order, one per CU first: the routed ones,
+  // whose first request is the router scores, get a CU of their own, so that
+  // request does not queue behind another workgroup's weight tiles.
+  if (blk < a.n_routed_wg) {
     const int slot = blk / n_rt_f, rt = blk % n_rt_f;
     route_local(a, sh.route);
-    gate_up_role(a, a.arena + (int64_t)sh.route.ids[slot] * a.expert_bytes, slot, rt, sh);
+    gate_up_role<1>(a, a.arena + (int64_t)sh.route.ids[slot] * a.expert_bytes, slot, rt, sh);
+  } else if ((blk -= a.n_routed_wg) < a.n_shared_wg) {
+    gate_up_role<1>(a, a.shared, a.K, blk, sh);
   } else {
-    down_role(a, blk - a.n_routed_wg, sh);
+    down_role(a, blk - a.n_shared_wg, sh);
   }
 }
 
