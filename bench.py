@@ -40,10 +40,41 @@ def parse():
                    help="distinct seeded layers generated; placements reuse them at distinct addresses")
     p.add_argument("--cpu-sample", type=int, default=24, help="tokens the CPU oracle runs (0: skip)")
     p.add_argument("--no-graph", action="store_true", help="replay eagerly instead of through a HIP graph")
+    p.add_argument("--copy-mb", type=int, default=0,
+                   help="first run one plain device copy of this many MiB (a kernel of known traffic, to scale "
+                        "the HBM byte counters of a profiler run)")
     return p.parse_args()
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+
+
+def measured_traffic(record):
+    """HBM bytes per launch from the committed counter summary, or None when the counted kernel source
+    has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", record)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, rec["kernel_source"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+            return None
+    return int(rec["bytes_per_call"])
+
+
+def copy_calibration(mib):
+    """One elementwise copy kernel that reads and writes exactly mib MiB."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def main():
@@ -51,6 +82,8 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_mb > 0:
+        copy_calibration(args.copy_mb)
     if args.workload == "prefill":
         run_prefill(args)
     else:
@@ -288,7 +321,7 @@ def run_decode(args):
                                f"{PLACEMENTS} placements of {distinct} distinct seeded layers",
                    "tokens_per_step": N_TOKENS, "graph": graph is not None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode_traffic.json"),
                      "kernel": "moe_layer_forward T=1: k_decode_scores + k_decode_experts (events around the call)",
                      "bytes_per_launch": layer_bytes, "avg_us": round(float(np.mean(ffn_us)), 3),
                      "median_us": round(float(np.median(ffn_us)), 3)},
