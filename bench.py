@@ -32,8 +32,12 @@ PLACEMENTS = 32
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--workload", choices=["decode", "prefill"], default="decode",
-                   help="decode: the headline T=1 line (default); prefill: one T=2048 layer call per step")
+    p.add_argument("--workload", choices=["decode", "prefill", "stack"], default="decode",
+                   help="decode: the headline T=1 line (default); prefill: one T=2048 layer call per step; "
+                        "stack: 38 chained layers per step, T=1")
+    p.add_argument("--stack-layers", type=int, default=38, help="layers of the stack workload")
+    p.add_argument("--stack-tokens", type=int, default=20,
+                   help="distinct tokens captured in the stack graph (steps per replay)")
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--distinct-layers", type=int, default=4,
@@ -86,6 +90,8 @@ def main():
         copy_calibration(args.copy_mb)
     if args.workload == "prefill":
         run_prefill(args)
+    elif args.workload == "stack":
+        run_stack(args)
     else:
         run_decode(args)
 
@@ -186,6 +192,128 @@ def run_prefill(args):
         "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
                               "median": float(np.median(counts))},
         "first_step_ms": round(first_ms, 3),
+        "setup_s": round(gen_s, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def chain(torch, x, out):
+    """Next layer's input: bf16(rmsnorm(x + out)), eps 1e-6, no weight (harness glue standing in for the
+    rest of a decoder block; not part of the MoE layer)."""
+    h = x.float() + out
+    return torch.nn.functional.rms_norm(h, (h.shape[-1],), eps=1e-6).to(torch.bfloat16)
+
+
+def run_stack(args):
+    """38 MoE layers of the Xing4 shape resident in HBM, one token per step (T=1) through all of them,
+    each layer's input chained from the previous layer's output; Zipf(1.1) expert popularity."""
+    import torch
+
+    import quantized_moe_decode_sigmoid_amd as qm
+    import synth
+
+    shape = synth.WORKLOADS["stack"]
+    H, E, K, F = shape.hidden, shape.n_experts, shape.top_k, shape.ffn
+    nl = args.stack_layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lam = synth.zipf_lambda(shape)
+    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
+    t0 = time.time()
+    layers = []
+    for l in range(nl):
+        inp = synth.layer_inputs(shape, layer=l, lam=lam)
+        layers.append(qm.DeviceLayer(cfg, inp["gate_w"], inp["bias"], inp["arena"], inp["shared"]))
+        del inp
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    S = args.stack_tokens
+    x_bits = synth.tokens(shape, S, first=7000)
+    x0 = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    ws = layers[0].workspace(1)
+    outs = [torch.empty((1, H), dtype=torch.float32, device=dev) for _ in range(nl)]
+    ids = torch.empty((S, nl, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((S, nl, K), dtype=torch.float32, device=dev)
+
+    def steps():
+        for i in range(S):
+            x = x0[i:i + 1]
+            for l, dl in enumerate(layers):
+                qm.moe_layer_forward(cfg, 1, x, dl.gate_w, dl.bias, dl.arena, dl.shared, outs[l], ids[i, l],
+                                     wts[i, l], ws)
+                x = chain(torch, x, outs[l])
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        steps()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            steps()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        # the MoE layer calls alone: events around each call of one eager pass over the S tokens, the
+        # queue kept busy by a spin kernel so that host launch gaps do not enter
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
+        torch.cuda._sleep(200_000_000)
+        for i in range(S):
+            x = x0[i:i + 1]
+            for l, dl in enumerate(layers):
+                starts[i * nl + l].record(stream)
+                qm.moe_layer_forward(cfg, 1, x, dl.gate_w, dl.bias, dl.arena, dl.shared, outs[l], ids[i, l],
+                                     wts[i, l], ws)
+                ends[i * nl + l].record(stream)
+                x = chain(torch, x, outs[l])
+        torch.cuda.synchronize()
+    ms_per_token = ev0.elapsed_time(ev1) / (args.steps * S)
+    moe_ms_per_token = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / S
+    eb = qm.moe_expert_bytes(cfg)
+    expert_bytes = nl * (K + shape.n_shared) * eb
+    router_bytes = nl * E * H * 4
+    # rank-frequency: each layer's expert counts sorted (layers rank their experts differently), summed by rank
+    ids_h = ids.cpu().numpy()
+    by_rank = np.zeros(E, np.int64)
+    for l in range(nl):
+        by_rank += np.sort(np.bincount(ids_h[:, l, :].reshape(-1), minlength=E))[::-1]
+    counts = by_rank
+    c = by_rank.astype(np.float64)
+    c = c[c > 0]
+    slope = float(np.polyfit(np.log(np.arange(1, c.size + 1)), np.log(c), 1)[0]) if c.size > 1 else None
+    gbs = (expert_bytes + router_bytes) / (ms_per_token * 1e-3) / 1e9
+    res = {
+        "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
+        "value": round(1e3 / ms_per_token, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps * S,
+        "warmup": args.warmup * S,
+        "ms_per_step": round(ms_per_token, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{nl}-layer MoE stack decode, T=1: each layer hidden 3584, 64 experts top-4 + 1 "
+                               "shared, ffn 1024, IQ4_NL, sigmoid router, scale 2.0; layer input = bf16(rmsnorm("
+                               "previous input + previous output)); Zipf(1.1) expert popularity",
+                   "layers": nl, "distinct_tokens": S, "zipf_lambda": lam, "graph": True},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole step: per layer k_decode_scores + k_decode_experts + the torch chaining ops",
+                     "bytes_per_token": expert_bytes + router_bytes},
+        "expert_bytes_per_token": expert_bytes,
+        "moe_calls_ms_per_token": round(moe_ms_per_token, 4),
+        "moe_calls_gbs": round((expert_bytes + router_bytes) / (moe_ms_per_token * 1e-3) / 1e9, 1),
+        "popularity": {"rank_frequency_slope": slope, "routes_by_rank": [int(v) for v in by_rank[:16]],
+                       "routes": int(by_rank.sum())},
         "setup_s": round(gen_s, 1),
     }
     print(json.dumps(res), flush=True)

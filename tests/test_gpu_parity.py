@@ -330,3 +330,30 @@ def test_bf16_and_fp32_contracts_agree_on_a_batch():
     r = np.linalg.norm(a - b) / np.linalg.norm(a)
     print(f"[parity] fp32 vs bf16 contract rel_l2={r:.3e}", flush=True)
     assert 0 < r < 2e-2
+
+
+# ---------------------------------------------------------------- the 38-layer stack workload
+
+def test_stack_layers_chained_with_zipf_bias():
+    """Three layers of the stack workload (Zipf(1.1) selection bias), each fed bf16(rmsnorm(x + out)) of the
+    previous one as in bench.py: every layer's routing is bit-exact and its output within tolerance of the
+    oracle on the same input."""
+    s = synth.WORKLOADS["stack"]
+    lam = synth.zipf_lambda(s)
+    cfg = cfg_of(s)
+    x = to_dev_bf16(synth.tokens(s, 1, first=123))
+    for layer in range(3):
+        inp = synth.layer_inputs(s, layer=layer, lam=lam)
+        dl = qm.DeviceLayer(cfg, inp["gate_w"], inp["bias"], inp["arena"], inp["shared"])
+        log(f"stack layer {layer}")
+        ids = torch.empty((1, s.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, s.top_k), dtype=torch.float32, device="cuda")
+        out = dl.forward(x, topk_ids=ids, topk_w=w)
+        xb = x.view(torch.int16).cpu().numpy().view(np.uint16)
+        ref, rid, rw = oracle.layer(xb, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn,
+                                    s.routed_scale, inp["bias"])
+        assert np.array_equal(ids.cpu().numpy(), rid)
+        assert np.array_equal(w.cpu().numpy().view(np.uint32), rw.view(np.uint32))
+        assert_close(out.cpu().numpy(), ref, f"stack layer {layer}")
+        h = x.float() + out
+        x = torch.nn.functional.rms_norm(h, (s.hidden,), eps=1e-6).to(torch.bfloat16)
