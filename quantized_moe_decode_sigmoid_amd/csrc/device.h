@@ -67,6 +67,18 @@ __device__ __forceinline__ void build_pair_table(uint32_t* tbl) {
   }
 }
 
+// The same table with fp16 levels (also exact), for the kernels that scale
+// each weight: a half of an entry feeds v_fma_mix_f32 directly.
+__device__ __forceinline__ void build_pair_table_f16(uint32_t* tbl) {
+  for (int i = threadIdx.x; i < kPairTableWords / 4; i += blockDim.x) {
+    const int v = i >> 3;
+    const uint32_t e = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)iq4nl_level(v & 15)) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)iq4nl_level(v >> 4)) << 16);
+    uint32_t __attribute__((ext_vector_type(4))) q = {e, e, e, e};
+    *reinterpret_cast<decltype(q)*>(tbl + 4 * i) = q;
+  }
+}
+
 // One nibble word (weights 8w..8w+7 of a block) -> the 4 dwords of an 8-slot
 // bf16 operand: dword i = (level of weight 8w+2i, level of weight 8w+2i+1).
 __device__ __forceinline__ bf16x8 decode_word(const uint32_t* tbl, uint32_t word, uint32_t lane32) {

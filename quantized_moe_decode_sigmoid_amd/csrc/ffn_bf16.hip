@@ -50,9 +50,15 @@ struct BfLds {
 };
 static_assert(sizeof(uint16_t) * 2 * kBfRows * kBfStep <= 65536, "LDS DMA destinations beyond 64 KB");
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
 // One nibble word -> the lane's 8-element bf16 operand, each weight
-// bf16(d * level) with the fp32 product exact before the rounding.
-__device__ __forceinline__ bf16x8 dequant_bf16(const uint32_t* tbl, uint32_t word, float d, uint32_t lane32) {
+// bf16(d * level): the fp16 level pair from the LDS table times the fp16
+// scale in fp32 (v_fma_mix_f32 with addend +0: the product is exact; a zero
+// product comes out +0 whatever its sign, which no sum can tell apart), both
+// rounded to nearest even by one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ bf16x8 dequant_bf16(const uint32_t* tbl, uint32_t word, _Float16 d, uint32_t lane32) {
   union {
     uint32_t u[4];
     bf16x8 v;
@@ -60,7 +66,10 @@ __device__ __forceinline__ bf16x8 dequant_bf16(const uint32_t* tbl, uint32_t wor
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const uint32_t e = tbl[((word >> (8 * i)) & 0xffu) * 32u + lane32];
-    r.u[i] = pack_bf16x2(__uint_as_float(e << 16) * d, __uint_as_float(e & 0xffff0000u) * d);
+    const _Float16 l0 = __builtin_bit_cast(_Float16, (uint16_t)(e & 0xffffu));
+    const _Float16 l1 = __builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
+    const f32x2 w = {__builtin_fmaf((float)l0, (float)d, 0.0f), __builtin_fmaf((float)l1, (float)d, 0.0f)};
+    r.u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(w, bf16x2v));
   }
   return r.v;
 }
@@ -82,7 +91,9 @@ __device__ __forceinline__ LaneTile load_lane_tile(const uint8_t* tile, int lane
   return t;
 }
 
-__device__ __forceinline__ float lane_scale(const LaneTile& t, int b) { return half_bits_to_float(t.sc[b]); }
+__device__ __forceinline__ _Float16 lane_scale(const LaneTile& t, int b) {
+  return __builtin_bit_cast(_Float16, (uint16_t)(t.sc[b] & 0xffffu));
+}
 
 // Activation rows of one step, global memory straight into LDS
 // (global_load_lds_dwordx4): load j of wavefront w fills rows 4q..4q+3,
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(kBfThreads) void k_gate_up_bf16(
     const int i = min((int)threadIdx.x, ch.count - 1);
     sh.src[threadIdx.x] = routed ? perm[ch.first + i] / K : ch.first + i;
   }
-  build_pair_table(sh.tbl);
+  build_pair_table_f16(sh.tbl);
   __syncthreads();
 
   const int n_sub = (ch.count + 15) >> 4;
@@ -235,7 +246,7 @@ __global__ __launch_bounds__(kBfThreads) void k_down_bf16(
   const int TK = T * K;
   const int64_t row0 = routed ? (int64_t)ch.first : (int64_t)TK + ch.first;
   if (threadIdx.x < kBfRows) sh.src[threadIdx.x] = (int32_t)(row0 + min((int)threadIdx.x, ch.count - 1));
-  build_pair_table(sh.tbl);
+  build_pair_table_f16(sh.tbl);
   __syncthreads();
 
   const int n_sub = (ch.count + 15) >> 4;
