@@ -4,15 +4,21 @@
 // exactly one writer and the top-k can be summed in slot order afterwards).
 //
 // One workgroup of 1024 threads (16 wavefronts).  Integer work only, so the
-// result is bit-exact whatever the scheduling:
-//   1. counts by LDS atomic increments (the totals do not depend on order);
-//   2. exclusive scan over the (at most 256) experts;
-//   3. routes taken 1024 at a time in route order; inside a wavefront, the
+// result is bit-exact whatever the scheduling.  The routes are cut into 16
+// contiguous segments, one per wavefront, in route order:
+//   1. each wavefront counts its segment per expert (LDS atomics; a count does
+//      not depend on order);
+//   2. per expert, a scan over the 16 segment counts gives each wavefront the
+//      number of earlier routes of that expert in earlier segments; a scan
+//      over the experts gives the expert offsets and the first chunk of each
+//      expert;
+//   3. each wavefront walks its own segment 64 routes at a time, in order:
 //      lanes holding the same expert find each other with 8 ballots (one per
-//      bit of the expert id) and rank themselves by lane; per-wave counts in
-//      LDS give the offset of each wavefront; a running offset per expert
-//      carries across tiles.  Position = running + earlier waves + lane rank,
-//      which is exactly the stable order (ascending route id in an expert).
+//      bit of the expert id) and rank themselves by lane; the wavefront's
+//      running count per expert carries across steps.  Position = expert
+//      offset + earlier segments + running count + lane rank, which is
+//      exactly the stable order (ascending route id in an expert).
+// No step after the scans needs a workgroup barrier.
 // The same pass writes the work list of the FFN kernels: chunks of at most
 // chunk_rows routes of one expert, then chunks of chunk_rows tokens of the
 // shared expert (chunk_rows is a power of two).
@@ -24,71 +30,111 @@ namespace qmoe {
 constexpr int kBucketThreads = 1024;
 constexpr int kBucketWaves = kBucketThreads / 64;
 
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int T, int K, int E,
                                                            int n_shared, int chunk_shift, int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ pos, Chunk* __restrict__ chunks,
                                                            int32_t* __restrict__ n_chunks) {
+  __shared__ int32_t s_seg[kBucketWaves][256];  // per segment: count, then routes before it, then running
   __shared__ int32_t s_cnt[256];
-  __shared__ int32_t s_run[256];
-  __shared__ int32_t s_wave[kBucketWaves][256];
+  __shared__ int32_t s_off[256];
   __shared__ int32_t s_chunk_first[257];
+  __shared__ int32_t s_part[2][4];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int R = T * K;
+  const int seg = (R + kBucketWaves - 1) / kBucketWaves;
+  const int r0 = min(R, wave * seg), r1 = min(R, r0 + seg);
 
-  for (int e = tid; e < 256; e += kBucketThreads) s_cnt[e] = 0;
+  for (int i = tid; i < kBucketWaves * 256; i += kBucketThreads) (&s_seg[0][0])[i] = 0;
   __syncthreads();
-  for (int r = tid; r < R; r += kBucketThreads) atomicAdd(&s_cnt[ids[r]], 1);
+  for (int r = r0 + lane; r < r1; r += 64) atomicAdd(&s_seg[wave][ids[r]], 1);
   __syncthreads();
-  if (tid == 0) {
-    int run = 0, ch = 0;
-    for (int e = 0; e < E; e++) {
-      s_run[e] = run;
-      s_chunk_first[e] = ch;
-      run += s_cnt[e];
-      ch += (s_cnt[e] + (1 << chunk_shift) - 1) >> chunk_shift;
+
+  // per expert: exclusive scan over the segments, total count, chunk count
+  const int rows = 1 << chunk_shift;
+  int cnt = 0, nch = 0;
+  if (tid < 256) {
+#pragma unroll
+    for (int w = 0; w < kBucketWaves; w++) {
+      const int c = s_seg[w][tid];
+      s_seg[w][tid] = cnt;
+      cnt += c;
     }
-    s_chunk_first[E] = ch;
+    if (tid >= E) cnt = 0;
+    nch = (cnt + rows - 1) >> chunk_shift;
+    s_cnt[tid] = cnt;
+  }
+  // exclusive scan over the experts (four wavefronts of 64 experts)
+  int inc_c = 0, inc_n = 0;
+  if (tid < 256) {
+    inc_c = wave_inclusive_scan(cnt, lane);
+    inc_n = wave_inclusive_scan(nch, lane);
+    if (lane == 63) {
+      s_part[0][wave] = inc_c;
+      s_part[1][wave] = inc_n;
+    }
+  }
+  __syncthreads();
+  if (tid < 256) {
+    int pc = 0, pn = 0;
+    for (int w = 0; w < wave; w++) {
+      pc += s_part[0][w];
+      pn += s_part[1][w];
+    }
+    s_off[tid] = pc + inc_c - cnt;
+    s_chunk_first[tid] = pn + inc_n - nch;
+    if (tid == 255) s_chunk_first[256] = pn + inc_n;
   }
   __syncthreads();
   for (int e = tid; e < E; e += kBucketThreads) {
     counts[e] = s_cnt[e];
-    offsets[e] = s_run[e];
+    offsets[e] = s_off[e];
   }
   if (tid == 0) offsets[E] = R;
 
   // chunk list (independent of the permutation itself); optional
   const bool want_chunks = chunks != nullptr;
-  for (int e = tid; want_chunks && e < E; e += kBucketThreads) {
-    const int rows = 1 << chunk_shift;
-    const int c0 = s_chunk_first[e], nch = (s_cnt[e] + rows - 1) >> chunk_shift;
+  const int routed_chunks = s_chunk_first[256];
+  if (want_chunks && tid < E) {
+    const int c0 = s_chunk_first[tid];
     for (int j = 0; j < nch; j++) {
       Chunk c;
-      c.expert = e;
-      c.first = s_run[e] + rows * j;
-      c.count = min(rows, s_cnt[e] - rows * j);
+      c.expert = tid;
+      c.first = s_off[tid] + rows * j;
+      c.count = min(rows, cnt - rows * j);
       c.pad = 0;
       chunks[c0 + j] = c;
     }
   }
-  const int routed_chunks = s_chunk_first[E];
-  const int shared_chunks = n_shared ? (T + (1 << chunk_shift) - 1) >> chunk_shift : 0;
+  const int shared_chunks = n_shared ? (T + rows - 1) >> chunk_shift : 0;
   for (int j = tid; want_chunks && j < shared_chunks; j += kBucketThreads) {
     Chunk c;
     c.expert = -1;
     c.first = j << chunk_shift;
-    c.count = min(1 << chunk_shift, T - (j << chunk_shift));
+    c.count = min(rows, T - (j << chunk_shift));
     c.pad = 0;
     chunks[routed_chunks + j] = c;
   }
   if (tid == 0 && want_chunks) *n_chunks = routed_chunks + shared_chunks;
 
-  // stable scatter
-  for (int base = 0; base < R; base += kBucketThreads) {
-    const int r = base + tid;
-    const bool valid = r < R;
+  // stable scatter, each wavefront over its own segment in route order
+  int32_t* run = s_seg[wave];
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = r0; base < r1; base += 64) {
+    const int r = base + lane;
+    const bool valid = r < r1;
     const int key = valid ? ids[r] : 0;
     uint64_t peers = __ballot(valid);
 #pragma unroll
@@ -96,26 +142,16 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
       const uint64_t b = __ballot(valid && ((key >> bit) & 1));
       peers &= ((key >> bit) & 1) ? b : ~b;
     }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     const int rank = __popcll(peers & below);
-    for (int i = tid; i < kBucketWaves * 256; i += kBucketThreads) (&s_wave[0][0])[i] = 0;
-    __syncthreads();
-    if (valid && rank == 0) s_wave[wave][key] = __popcll(peers);
-    __syncthreads();
+    const int before = run[key];
     if (valid) {
-      int before = 0;
-      for (int w = 0; w < wave; w++) before += s_wave[w][key];
-      const int at = s_run[key] + before + rank;
+      const int at = s_off[key] + before + rank;
       perm[at] = r;
       if (pos) pos[r] = at;
     }
-    __syncthreads();
-    for (int e = tid; e < E; e += kBucketThreads) {
-      int tot = 0;
-      for (int w = 0; w < kBucketWaves; w++) tot += s_wave[w][e];
-      s_run[e] += tot;
-    }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) run[key] = before + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
   }
 }
 

@@ -40,6 +40,91 @@ __global__ __launch_bounds__(256) void k_router_scores(const uint16_t* __restric
   }
 }
 
+// Batched calls: one workgroup per 16 tokens x 16 experts, four wavefronts of
+// 8 x 8.  Lane j keeps the partial sum p_j of all 64 (token, expert) pairs of
+// its wave in registers, each walking the same elements 256m + 4j + c in the
+// same (m, c) order as the single-row logit, so every partial is the one the
+// per-row form computes.  The 64 lane partials of each pair then go through
+// LDS and one lane per pair adds them in the butterfly's tree: level s pairs
+// index j with j + s for s = 32, 16, ..., 1 (fp32 addition commutes, so this
+// is exactly the value every lane of the shuffle butterfly ends with).
+constexpr int kRtTok = 8, kRtExp = 8, kRtStride = 68;
+
+__global__ __launch_bounds__(256, 2) void k_router_scores_tiled(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ wg, int T, int H, int E,
+                                                              float* __restrict__ scores) {
+#pragma clang fp contract(off)
+  __shared__ __attribute__((aligned(16))) float part[4][kRtTok * kRtExp * kRtStride];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 16 + (wave >> 1) * kRtTok;
+  const int e0 = blockIdx.y * 16 + (wave & 1) * kRtExp;
+  const uint16_t* xr[kRtTok];
+  const float* wr[kRtExp];
+#pragma unroll
+  for (int i = 0; i < kRtTok; i++) xr[i] = x + (size_t)min(t0 + i, T - 1) * H + 4 * lane;
+#pragma unroll
+  for (int i = 0; i < kRtExp; i++) wr[i] = wg + (size_t)min(e0 + i, E - 1) * H + 4 * lane;
+  float acc[kRtTok][kRtExp];
+#pragma unroll
+  for (int a = 0; a < kRtTok; a++)
+#pragma unroll
+    for (int b = 0; b < kRtExp; b++) acc[a][b] = 0.0f;
+  uint2 xv[kRtTok];
+  float4 wv[kRtExp];
+#pragma unroll
+  for (int i = 0; i < kRtTok; i++) xv[i] = *reinterpret_cast<const uint2*>(xr[i]);
+#pragma unroll
+  for (int i = 0; i < kRtExp; i++) wv[i] = *reinterpret_cast<const float4*>(wr[i]);
+  const int M = H >> 8;
+  for (int m = 0; m < M; m++) {
+    const int mn = (m + 1 < M ? m + 1 : m) * 256;
+    uint2 xn[kRtTok];
+    float4 wn[kRtExp];
+#pragma unroll
+    for (int i = 0; i < kRtTok; i++) xn[i] = *reinterpret_cast<const uint2*>(xr[i] + mn);
+#pragma unroll
+    for (int i = 0; i < kRtExp; i++) wn[i] = *reinterpret_cast<const float4*>(wr[i] + mn);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+#pragma unroll
+      for (int a = 0; a < kRtTok; a++) {
+        const uint32_t word = c < 2 ? xv[a].x : xv[a].y;
+        const float xf = bf16_bits_to_f32((c & 1) ? word >> 16 : word & 0xffffu);
+#pragma unroll
+        for (int b = 0; b < kRtExp; b++) {
+          const float wf = c == 0 ? wv[b].x : c == 1 ? wv[b].y : c == 2 ? wv[b].z : wv[b].w;
+          acc[a][b] = __builtin_fmaf(xf, wf, acc[a][b]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kRtTok; i++) xv[i] = xn[i];
+#pragma unroll
+    for (int i = 0; i < kRtExp; i++) wv[i] = wn[i];
+  }
+  float* pw = part[wave];
+#pragma unroll
+  for (int a = 0; a < kRtTok; a++)
+#pragma unroll
+    for (int b = 0; b < kRtExp; b++) pw[(a * kRtExp + b) * kRtStride + lane] = acc[a][b];
+  __syncthreads();
+  float p[64];
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float4 q = *reinterpret_cast<const float4*>(pw + lane * kRtStride + 4 * i);
+    p[4 * i] = q.x;
+    p[4 * i + 1] = q.y;
+    p[4 * i + 2] = q.z;
+    p[4 * i + 3] = q.w;
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1)
+#pragma unroll
+    for (int j = 0; j < s; j++) p[j] = p[j] + p[j + s];
+  const int t = t0 + lane / kRtExp, e = e0 + lane % kRtExp;
+  if (t < T && e < E) scores[(size_t)t * E + e] = sigmoid_fixed(p[0]);
+}
+
 // One wavefront per token.
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, const float* __restrict__ bias, int T,
                                               int E, int K, float scale, int32_t* __restrict__ ids,
@@ -50,6 +135,10 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, 
   topk_wave(scores + (size_t)t * E, bias, E, K, scale, lane, ids + (size_t)t * K, wout + (size_t)t * K);
 }
 
+// Below this many tokens a wavefront per (expert, run of tokens) has more
+// workgroups to spread over the chip than 16 x 16 tiles.
+constexpr int kRouterTiledMinTokens = 64;
+
 hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
                          float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream) {
   if (T == 0) return hipSuccess;
@@ -58,7 +147,10 @@ hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, 
   const int64_t waves = (int64_t)E * ((T + tpw - 1) / tpw);
   const int blocks = (int)((waves + 3) / 4);
   clear_last_error();
-  if (H <= 16 * 256)
+  if (T >= kRouterTiledMinTokens)
+    hipLaunchKernelGGL(k_router_scores_tiled, dim3((T + 15) / 16, (E + 15) / 16), dim3(256), 0, stream, x, wg, T, H,
+                       E, scores_ws);
+  else if (H <= 16 * 256)
     hipLaunchKernelGGL(k_router_scores<16>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores_ws);
   else
     hipLaunchKernelGGL(k_router_scores<32>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores_ws);

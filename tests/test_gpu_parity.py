@@ -71,7 +71,8 @@ def run_route(dl, x_bits, bias_dev=None):
     return ids.cpu().numpy(), w.cpu().numpy()
 
 
-@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 1), ("xing4", 64), ("batch", 128), ("prefill", 300)])
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 1), ("tiny", 100), ("xing4", 64), ("batch", 128),
+                                     ("prefill", 300), ("prefill", 2048)])
 def test_route_bit_exact(name, T):
     s, inp, dl = device_layer(name)
     x = synth.tokens(s, T, first=1000)
