@@ -200,7 +200,7 @@ def test_expert_forward_matches_layer_forward():
     assert np.array_equal(out.cpu().numpy().view(np.uint32), full.view(np.uint32))
 
 
-# ---------------------------------------------------------------- two-launch decode path
+# ---------------------------------------------------------------- one-launch decode path
 
 def assert_paths_agree(a, b, what):
     """Decode path vs multi-kernel path: same contract, fp32 sums split differently."""
@@ -245,6 +245,79 @@ def test_decode_path_many_consecutive_calls_one_workspace():
     got = torch.cat(outs).cpu().numpy()
     ref = multi_kernel_layer(dl, xd, 64).cpu().numpy()
     assert_paths_agree(got, ref, "64 consecutive decode calls")
+
+
+def decode_route(dl, x_bits):
+    """The decode path's routing outputs for one token (T = 1)."""
+    cfg = dl.cfg
+    ids = torch.empty((1, cfg.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, cfg.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((1, cfg.hidden), dtype=torch.float32, device="cuda")
+    qm.moe_layer_forward(cfg, 1, to_dev_bf16(x_bits), dl.gate_w, dl.bias, dl.arena, dl.shared, out, ids, w,
+                         ws=dl.workspace(1))
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("with_bias", [False, True])
+def test_decode_route_bit_exact(with_bias):
+    s, inp = workload("xing4")
+    bias = synth.zipf_bias(s, 0.08) if with_bias else None
+    _, _, dl = device_layer("xing4", bias=None if bias is None else torch.from_numpy(bias).cuda())
+    x = synth.tokens(s, 24, first=5100)
+    log(f"decode route xing4 bias={with_bias}")
+    rid, rw, _, _ = oracle.route(x, inp["gate_w"], s.top_k, s.routed_scale, bias)
+    for t in range(24):
+        ids, w = decode_route(dl, x[t:t + 1])
+        assert np.array_equal(ids[0], rid[t]), t
+        assert np.array_equal(w[0].view(np.uint32), rw[t].view(np.uint32)), t
+
+
+@pytest.mark.parametrize("path", ["decode", "multi-kernel"])
+def test_route_ties_break_by_lower_expert_index(path):
+    """Experts 1, 4 and 6 share one router row, so their scores tie exactly; tokens on which that row
+    wins must pick them in index order (K = 2 of 8 on the tiny shape: experts 1 and 4)."""
+    s, inp = workload("tiny")
+    gw = inp["gate_w"].copy()
+    gw[4] = gw[1]
+    gw[6] = gw[1]
+    x = synth.tokens(s, 64, first=900)
+    rid, rw, _, _ = oracle.route(x, gw, s.top_k, s.routed_scale)
+    tied = [t for t in range(64) if rid[t, 0] == 1]
+    assert len(tied) >= 3 and all(rid[t, 1] == 4 for t in tied)
+    dl = qm.DeviceLayer(cfg_of(s, qm.PREC_FP32), gw, None, inp["arena"], inp["shared"])
+    log(f"route ties {path} on {len(tied)} tokens")
+    for t in tied:
+        if path == "decode":
+            ids, w = decode_route(dl, x[t:t + 1])
+        else:
+            ids, w = run_route(dl, x[t:t + 1])
+        assert np.array_equal(ids[0], rid[t]), t
+        assert np.array_equal(w[0].view(np.uint32), rw[t].view(np.uint32)), t
+
+
+def test_decode_state_survives_batched_calls_on_the_same_workspace():
+    """Decode calls interleaved with batched calls (FP32 and BF16 contracts) on one workspace: the
+    decode path's words at the start of the workspace are not disturbed by the batched calls."""
+    s, inp, dl = device_layer("xing4")
+    cfg = dl.cfg
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, 300), dtype=torch.uint8, device="cuda")
+    qm.moe_workspace_init(cfg, 300, ws)
+    assert qm.moe_resolved_precision(cfg, 300) == qm.PREC_BF16
+    x = synth.tokens(s, 300, first=4200)
+    xd = to_dev_bf16(x)
+    ref = multi_kernel_layer(dl, xd[:8], 8).cpu().numpy()
+    log("decode calls around batched calls on one workspace")
+    got = []
+    for i in range(8):
+        out = torch.empty((1, s.hidden), dtype=torch.float32, device="cuda")
+        qm.moe_layer_forward(cfg, 1, xd[i:i + 1], dl.gate_w, None, dl.arena, dl.shared, out, ws=ws)
+        got.append(out)
+        T = 3 if i % 2 == 0 else 300  # FP32 then BF16 contract in between
+        big = torch.empty((T, s.hidden), dtype=torch.float32, device="cuda")
+        qm.moe_layer_forward(cfg, T, xd[:T], dl.gate_w, None, dl.arena, dl.shared, big, ws=ws)
+    assert_paths_agree(torch.cat(got).cpu().numpy(), ref, "decode calls between batched calls")
+    torch.cuda.synchronize()
+    assert ws[:4].view(torch.int32).cpu().numpy()[0] == 0, "a wait of the decode path gave up"
 
 
 def test_graph_replay_of_decode_calls():
