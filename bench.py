@@ -154,6 +154,11 @@ def run_prefill(args):
     counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
     flops = 2.0 * 3 * H * F * (T * K + T * shape.n_shared)
     ffn_tflops = flops / (float(np.mean(ffn_us)) * 1e-6) / 1e12
+    # algorithmic bytes of one moe_expert_forward call: every expert once (routed + shared), x, the
+    # routing (ids + weights), the fp32 output
+    ebytes = 3 * F * (H // 32) * 18
+    ffn_bytes = (E + shape.n_shared) * ebytes + T * H * 2 + T * K * 8 + T * H * 4
+    ffn_gbs = ffn_bytes / (float(np.mean(ffn_us)) * 1e-6) / 1e9
 
     cpu = None
     if args.cpu_sample > 0:
@@ -182,11 +187,18 @@ def run_prefill(args):
         "config": {"workload": "prefill MoE layer, T=2048: hidden 2048, 256 experts top-8 + 1 shared, ffn 512, "
                                "IQ4_NL experts, sigmoid router, scale 2.0, Zipf(1.0) expert popularity",
                    "tokens_per_step": T, "zipf_lambda": lam},
-        "roofline": {"bound": "mfma", "achieved": round(ffn_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+        # The FFN needs every expert's weights once (more bytes than the 256 MB last-level cache), so its
+        # HBM floor (bytes / 8 TB/s) is above its MFMA floor (flops / 2.5 PFLOP/s): it is HBM-bound.
+        "roofline": {"bound": "hbm" if ffn_bytes / HBM_PEAK_GBS > flops / 1e3 / MFMA_BF16_PEAK_TFLOPS else "mfma",
+                     "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "moe_expert_forward bf16: k_bucket + k_gate_up_bf16 + k_down_bf16 + k_combine "
                                "(events around the call)",
-                     "flops_per_launch": flops, "avg_us": round(float(np.mean(ffn_us)), 3)},
+                     "bytes_per_launch": ffn_bytes, "flops_per_launch": flops,
+                     "mfma_tflops": round(ffn_tflops, 2), "mfma_frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "hbm_floor_us": round(ffn_bytes / HBM_PEAK_GBS / 1e3, 2),
+                     "mfma_floor_us": round(flops / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
+                     "avg_us": round(float(np.mean(ffn_us)), 3)},
         "cpu_baseline": cpu,
         "tok_s": round(T / (layer_ms * 1e-3), 1),
         "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
