@@ -22,8 +22,10 @@
 //     rounded to bf16).  Each weight feeds exactly one wavefront, so the
 //     dequantized tile needs no trip through LDS; it is dequantized once per
 //     workgroup and reused by every 16-row sub-tile of the tile;
-//   - 16-row sub-tiles past the tile's last row are skipped (a branch that is
-//     uniform over the workgroup).
+//   - 16-row sub-tiles past the tile's last row are skipped: the k-loop is
+//     instantiated for each count of active sub-tiles (1 .. 8) and the tile
+//     picks its instance once, so that the loop body has no per-sub-tile
+//     branch and its LDS reads and MFMAs can be scheduled together.
 #include "device.h"
 #include "launch.h"
 
@@ -49,6 +51,7 @@ struct BfLds {
   int32_t src[kBfRows];  // source row of each tile row (x row or h row)
 };
 static_assert(sizeof(uint16_t) * 2 * kBfRows * kBfStep <= 65536, "LDS DMA destinations beyond 64 KB");
+static_assert(kBfSub == 8, "the k-loop is instantiated for 1 .. 8 sub-tiles");
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
@@ -122,23 +125,23 @@ __device__ __forceinline__ bf16x8 a_operand(const uint16_t* a, int s, int b, int
   return *reinterpret_cast<const bf16x8*>(a + (16 * s + r) * kBfStep + 8 * ((4 * b + (lane >> 4)) ^ r));
 }
 
-// acc[s][c] += A(s) x B(c) over one step for the NC column tiles in wt.
-template <int NC>
-__device__ __forceinline__ void step_mfma(const BfLds& sh, const uint16_t* a, const LaneTile (&wt)[NC], int n_sub,
-                                          int lane, f32x4 (&acc)[kBfSub][NC]) {
+// acc[s][c] += A(s) x B(c) over one step for the NS active sub-tiles and the
+// NC column tiles in wt.
+template <int NS, int NC>
+__device__ __forceinline__ void step_mfma(const BfLds& sh, const uint16_t* a, const LaneTile (&wt)[NC], int lane,
+                                          f32x4 (&acc)[NS][NC]) {
 #pragma unroll
   for (int b = 0; b < 4; b++) {
     bf16x8 bop[NC];
 #pragma unroll
     for (int c = 0; c < NC; c++) bop[c] = dequant_bf16(sh.tbl, wt[c].nib[b], lane_scale(wt[c], b), lane & 31);
+    bf16x8 aop[NS];
 #pragma unroll
-    for (int s = 0; s < kBfSub; s++) {
-      if (s < n_sub) {
-        const bf16x8 aop = a_operand(a, s, b, lane);
+    for (int s = 0; s < NS; s++) aop[s] = a_operand(a, s, b, lane);
 #pragma unroll
-        for (int c = 0; c < NC; c++) acc[s][c] = mfma16x16x32(aop, bop[c], acc[s][c]);
-      }
-    }
+    for (int s = 0; s < NS; s++)
+#pragma unroll
+      for (int c = 0; c < NC; c++) acc[s][c] = mfma16x16x32(aop[s], bop[c], acc[s][c]);
   }
 }
 
@@ -146,30 +149,12 @@ __device__ __forceinline__ void step_mfma(const BfLds& sh, const uint16_t* a, co
 
 // Workgroup = (tile, slab of 256 gate columns).  h[hrow][f] = bf16(silu(g) * u)
 // for hrow = bucketed position (routed) or T*K + token (shared).
-__global__ __launch_bounds__(kBfThreads) void k_gate_up_bf16(
-    const uint16_t* __restrict__ x, int H, int F, int K, int T, const uint8_t* __restrict__ arena,
-    const uint8_t* __restrict__ shared, int64_t expert_bytes, const int32_t* __restrict__ perm,
-    const Chunk* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int max_tiles, uint16_t* __restrict__ h) {
-  __shared__ BfLds sh;
-  const int tile_id = blockIdx.x % max_tiles;
-  const int slab = blockIdx.x / max_tiles;
-  if (tile_id >= *n_tiles) return;
-  const Chunk ch = tiles[tile_id];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool routed = ch.expert >= 0;
-  if (threadIdx.x < kBfRows) {
-    const int i = min((int)threadIdx.x, ch.count - 1);
-    sh.src[threadIdx.x] = routed ? perm[ch.first + i] / K : ch.first + i;
-  }
-  build_pair_table_f16(sh.tbl);
-  __syncthreads();
-
-  const int n_sub = (ch.count + 15) >> 4;
-  const int n_rows = 16 * n_sub;
-  const int col0 = slab * (kBfWaves * kGuCols) + wave * kGuCols;
+template <int NS>
+__device__ void gate_up_tile(BfLds& sh, const Chunk& ch, const uint16_t* __restrict__ x, int H, int F, int K, int T,
+                             const uint8_t* ex, int64_t mat_bytes, int col0, bool routed, int lane, int wave,
+                             uint16_t* __restrict__ h) {
+  const int n_rows = 16 * NS;
   const bool cols_on = col0 < F;
-  const int64_t mat_bytes = expert_bytes / 3;
-  const uint8_t* ex = routed ? arena + (int64_t)ch.expert * expert_bytes : shared;
   const int nkg = H / kBfStep;
   const int rt0 = (cols_on ? col0 : 0) >> 4;
   // column tiles: 0, 1 = gate rows rt0, rt0+1; 2, 3 = up rows rt0, rt0+1
@@ -177,9 +162,9 @@ __global__ __launch_bounds__(kBfThreads) void k_gate_up_bf16(
                              ex + mat_bytes + (int64_t)rt0 * nkg * kTileBytes,
                              ex + mat_bytes + (int64_t)(rt0 + 1) * nkg * kTileBytes};
 
-  f32x4 acc[kBfSub][4];
+  f32x4 acc[NS][4];
 #pragma unroll
-  for (int s = 0; s < kBfSub; s++)
+  for (int s = 0; s < NS; s++)
 #pragma unroll
     for (int c = 0; c < 4; c++) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -198,7 +183,7 @@ __global__ __launch_bounds__(kBfThreads) void k_gate_up_bf16(
 #pragma unroll
       for (int c = 0; c < 4; c++) wn[c] = load_lane_tile(wbase[c] + (int64_t)(kt + 1) * kTileBytes, lane);
     }
-    if (cols_on) step_mfma<4>(sh, sh.a[kt & 1], wt, n_sub, lane, acc);
+    if (cols_on) step_mfma<NS, 4>(sh, sh.a[kt & 1], wt, lane, acc);
     if (more) {
 #pragma unroll
       for (int c = 0; c < 4; c++) wt[c] = wn[c];
@@ -210,32 +195,27 @@ __global__ __launch_bounds__(kBfThreads) void k_gate_up_bf16(
   if (!cols_on) return;
   const int TK = T * K;
 #pragma unroll
-  for (int s = 0; s < kBfSub; s++) {
-    if (s < n_sub) {
+  for (int s = 0; s < NS; s++) {
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int m = 16 * s + 4 * (lane >> 4) + v;
-        if (m < ch.count) {
-          const int64_t hrow = routed ? (int64_t)ch.first + m : (int64_t)TK + ch.first + m;
+    for (int v = 0; v < 4; v++) {
+      const int m = 16 * s + 4 * (lane >> 4) + v;
+      if (m < ch.count) {
+        const int64_t hrow = routed ? (int64_t)ch.first + m : (int64_t)TK + ch.first + m;
 #pragma unroll
-          for (int c = 0; c < 2; c++) {
-            const float g = acc[s][c][v], u = acc[s][c + 2][v];
-            const float hv = g / (1.0f + expf(-g)) * u;
-            h[hrow * F + col0 + 16 * c + (lane & 15)] = __builtin_bit_cast(uint16_t, (__bf16)hv);
-          }
+        for (int c = 0; c < 2; c++) {
+          const float g = acc[s][c][v], u = acc[s][c + 2][v];
+          const float hv = g / (1.0f + expf(-g)) * u;
+          h[hrow * F + col0 + 16 * c + (lane & 15)] = __builtin_bit_cast(uint16_t, (__bf16)hv);
         }
       }
     }
   }
 }
 
-// ---------------------------------------------------------------- down
-
-// Workgroup = (tile, slab of 512 output columns).  y[hrow][n] = sum_f Wd[n][f] h[hrow][f].
-__global__ __launch_bounds__(kBfThreads) void k_down_bf16(
-    int H, int F, int K, int T, const uint8_t* __restrict__ arena, const uint8_t* __restrict__ shared,
-    int64_t expert_bytes, const Chunk* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int max_tiles,
-    const uint16_t* __restrict__ h, float* __restrict__ y) {
+__global__ __launch_bounds__(kBfThreads) void k_gate_up_bf16(
+    const uint16_t* __restrict__ x, int H, int F, int K, int T, const uint8_t* __restrict__ arena,
+    const uint8_t* __restrict__ shared, int64_t expert_bytes, const int32_t* __restrict__ perm,
+    const Chunk* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int max_tiles, uint16_t* __restrict__ h) {
   __shared__ BfLds sh;
   const int tile_id = blockIdx.x % max_tiles;
   const int slab = blockIdx.x / max_tiles;
@@ -243,27 +223,42 @@ __global__ __launch_bounds__(kBfThreads) void k_down_bf16(
   const Chunk ch = tiles[tile_id];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const bool routed = ch.expert >= 0;
-  const int TK = T * K;
-  const int64_t row0 = routed ? (int64_t)ch.first : (int64_t)TK + ch.first;
-  if (threadIdx.x < kBfRows) sh.src[threadIdx.x] = (int32_t)(row0 + min((int)threadIdx.x, ch.count - 1));
+  if (threadIdx.x < kBfRows) {
+    const int i = min((int)threadIdx.x, ch.count - 1);
+    sh.src[threadIdx.x] = routed ? perm[ch.first + i] / K : ch.first + i;
+  }
   build_pair_table_f16(sh.tbl);
   __syncthreads();
-
-  const int n_sub = (ch.count + 15) >> 4;
-  const int n_rows = 16 * n_sub;
-  const int col0 = slab * (kBfWaves * kDnCols) + wave * kDnCols;
-  const bool cols_on = col0 < H;
+  const int col0 = slab * (kBfWaves * kGuCols) + wave * kGuCols;
   const int64_t mat_bytes = expert_bytes / 3;
-  const uint8_t* ex = (routed ? arena + (int64_t)ch.expert * expert_bytes : shared) + 2 * mat_bytes;
+  const uint8_t* ex = routed ? arena + (int64_t)ch.expert * expert_bytes : shared;
+  switch ((ch.count + 15) >> 4) {
+#define QMOE_GU_CASE(n) \
+  case n: gate_up_tile<n>(sh, ch, x, H, F, K, T, ex, mat_bytes, col0, routed, lane, wave, h); break;
+    QMOE_GU_CASE(1) QMOE_GU_CASE(2) QMOE_GU_CASE(3) QMOE_GU_CASE(4)
+    QMOE_GU_CASE(5) QMOE_GU_CASE(6) QMOE_GU_CASE(7) QMOE_GU_CASE(8)
+#undef QMOE_GU_CASE
+    default: break;
+  }
+}
+
+// ---------------------------------------------------------------- down
+
+// Workgroup = (tile, slab of 512 output columns).  y[hrow][n] = sum_f Wd[n][f] h[hrow][f].
+template <int NS>
+__device__ void down_tile(BfLds& sh, const Chunk& ch, int H, int F, const uint8_t* ex, int64_t row0, int col0,
+                          int lane, int wave, const uint16_t* __restrict__ h, float* __restrict__ y) {
+  const int n_rows = 16 * NS;
+  const bool cols_on = col0 < H;
   const int nkg = F / kBfStep;
   const int rt0 = (cols_on ? col0 : 0) >> 4;
   const uint8_t* wbase[4];
 #pragma unroll
   for (int c = 0; c < 4; c++) wbase[c] = ex + (int64_t)(rt0 + c) * nkg * kTileBytes;
 
-  f32x4 acc[kBfSub][4];
+  f32x4 acc[NS][4];
 #pragma unroll
-  for (int s = 0; s < kBfSub; s++)
+  for (int s = 0; s < NS; s++)
 #pragma unroll
     for (int c = 0; c < 4; c++) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -282,7 +277,7 @@ __global__ __launch_bounds__(kBfThreads) void k_down_bf16(
 #pragma unroll
       for (int c = 0; c < 4; c++) wn[c] = load_lane_tile(wbase[c] + (int64_t)(kt + 1) * kTileBytes, lane);
     }
-    if (cols_on) step_mfma<4>(sh, sh.a[kt & 1], wt, n_sub, lane, acc);
+    if (cols_on) step_mfma<NS, 4>(sh, sh.a[kt & 1], wt, lane, acc);
     if (more) {
 #pragma unroll
       for (int c = 0; c < 4; c++) wt[c] = wn[c];
@@ -293,18 +288,45 @@ __global__ __launch_bounds__(kBfThreads) void k_down_bf16(
 
   if (!cols_on) return;
 #pragma unroll
-  for (int s = 0; s < kBfSub; s++) {
-    if (s < n_sub) {
+  for (int s = 0; s < NS; s++) {
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int m = 16 * s + 4 * (lane >> 4) + v;
-        if (m < ch.count) {
-          float* yr = y + (row0 + m) * H + col0 + (lane & 15);
+    for (int v = 0; v < 4; v++) {
+      const int m = 16 * s + 4 * (lane >> 4) + v;
+      if (m < ch.count) {
+        float* yr = y + (row0 + m) * H + col0 + (lane & 15);
 #pragma unroll
-          for (int c = 0; c < 4; c++) yr[16 * c] = acc[s][c][v];
-        }
+        for (int c = 0; c < 4; c++) yr[16 * c] = acc[s][c][v];
       }
     }
+  }
+}
+
+__global__ __launch_bounds__(kBfThreads) void k_down_bf16(
+    int H, int F, int K, int T, const uint8_t* __restrict__ arena, const uint8_t* __restrict__ shared,
+    int64_t expert_bytes, const Chunk* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int max_tiles,
+    const uint16_t* __restrict__ h, float* __restrict__ y) {
+  __shared__ BfLds sh;
+  const int tile_id = blockIdx.x % max_tiles;
+  const int slab = blockIdx.x / max_tiles;
+  if (tile_id >= *n_tiles) return;
+  const Chunk ch = tiles[tile_id];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool routed = ch.expert >= 0;
+  const int TK = T * K;
+  const int64_t row0 = routed ? (int64_t)ch.first : (int64_t)TK + ch.first;
+  if (threadIdx.x < kBfRows) sh.src[threadIdx.x] = (int32_t)(row0 + min((int)threadIdx.x, ch.count - 1));
+  build_pair_table_f16(sh.tbl);
+  __syncthreads();
+  const int col0 = slab * (kBfWaves * kDnCols) + wave * kDnCols;
+  const int64_t mat_bytes = expert_bytes / 3;
+  const uint8_t* ex = (routed ? arena + (int64_t)ch.expert * expert_bytes : shared) + 2 * mat_bytes;
+  switch ((ch.count + 15) >> 4) {
+#define QMOE_DN_CASE(n) \
+  case n: down_tile<n>(sh, ch, H, F, ex, row0, col0, lane, wave, h, y); break;
+    QMOE_DN_CASE(1) QMOE_DN_CASE(2) QMOE_DN_CASE(3) QMOE_DN_CASE(4)
+    QMOE_DN_CASE(5) QMOE_DN_CASE(6) QMOE_DN_CASE(7) QMOE_DN_CASE(8)
+#undef QMOE_DN_CASE
+    default: break;
   }
 }
 
