@@ -31,12 +31,14 @@
 
 namespace qmoe {
 
-constexpr int kBfThreads = 512;
+constexpr int kBfThreads = 1024;
 constexpr int kBfWaves = kBfThreads / 64;
 constexpr int kBfSub = kBfRows / 16;        // 16-row MFMA sub-tiles per tile
 constexpr int kBfStep = 128;                // reduction elements per step (one packed tile)
-constexpr int kGuCols = 32;                 // gate (and up) columns per wavefront
-constexpr int kDnCols = 64;                 // down output columns per wavefront
+constexpr int kGuCols = 16;                 // gate (and up) columns per wavefront
+constexpr int kDnCols = 32;                 // down output columns per wavefront
+constexpr int kGuTiles = kGuCols / 16;      // gate tiles per wavefront (as many up tiles)
+constexpr int kDnTiles = kDnCols / 16;      // down tiles per wavefront
 constexpr int kStageLoads = kBfRows / 4 / kBfWaves;  // 1 KB LDS DMA loads per wavefront and step
 
 // LDS: two buffers of activation rows, then the level pair table.  A buffer
@@ -135,13 +137,12 @@ __device__ __forceinline__ void step_mfma(const BfLds& sh, const uint16_t* a, co
     bf16x8 bop[NC];
 #pragma unroll
     for (int c = 0; c < NC; c++) bop[c] = dequant_bf16(sh.tbl, wt[c].nib[b], lane_scale(wt[c], b), lane & 31);
-    bf16x8 aop[NS];
 #pragma unroll
-    for (int s = 0; s < NS; s++) aop[s] = a_operand(a, s, b, lane);
+    for (int s = 0; s < NS; s++) {
+      const bf16x8 aop = a_operand(a, s, b, lane);
 #pragma unroll
-    for (int s = 0; s < NS; s++)
-#pragma unroll
-      for (int c = 0; c < NC; c++) acc[s][c] = mfma16x16x32(aop[s], bop[c], acc[s][c]);
+      for (int c = 0; c < NC; c++) acc[s][c] = mfma16x16x32(aop, bop[c], acc[s][c]);
+    }
   }
 }
 
@@ -157,36 +158,40 @@ __device__ void gate_up_tile(BfLds& sh, const Chunk& ch, const uint16_t* __restr
   const bool cols_on = col0 < F;
   const int nkg = H / kBfStep;
   const int rt0 = (cols_on ? col0 : 0) >> 4;
-  // column tiles: 0, 1 = gate rows rt0, rt0+1; 2, 3 = up rows rt0, rt0+1
-  const uint8_t* wbase[4] = {ex + (int64_t)rt0 * nkg * kTileBytes, ex + (int64_t)(rt0 + 1) * nkg * kTileBytes,
-                             ex + mat_bytes + (int64_t)rt0 * nkg * kTileBytes,
-                             ex + mat_bytes + (int64_t)(rt0 + 1) * nkg * kTileBytes};
+  // column tiles: c < kGuTiles = gate rows rt0 + c; kGuTiles + c = up rows rt0 + c
+  constexpr int NC = 2 * kGuTiles;
+  const uint8_t* wbase[NC];
+#pragma unroll
+  for (int c = 0; c < kGuTiles; c++) {
+    wbase[c] = ex + (int64_t)(rt0 + c) * nkg * kTileBytes;
+    wbase[kGuTiles + c] = ex + mat_bytes + (int64_t)(rt0 + c) * nkg * kTileBytes;
+  }
 
-  f32x4 acc[NS][4];
+  f32x4 acc[NS][NC];
 #pragma unroll
   for (int s = 0; s < NS; s++)
 #pragma unroll
-    for (int c = 0; c < 4; c++) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; c++) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   stage_rows(sh.a[0], x, H, sh.src, 0, n_rows, wave, lane);
-  LaneTile wt[4];
+  LaneTile wt[NC];
 #pragma unroll
-  for (int c = 0; c < 4; c++) wt[c] = load_lane_tile(wbase[c], lane);
+  for (int c = 0; c < NC; c++) wt[c] = load_lane_tile(wbase[c], lane);
   wait_loads();
   __syncthreads();
 
   for (int kt = 0; kt < nkg; kt++) {
     const bool more = kt + 1 < nkg;
-    LaneTile wn[4];
+    LaneTile wn[NC];
     if (more) {
       stage_rows(sh.a[(kt + 1) & 1], x, H, sh.src, (kt + 1) * kBfStep, n_rows, wave, lane);
 #pragma unroll
-      for (int c = 0; c < 4; c++) wn[c] = load_lane_tile(wbase[c] + (int64_t)(kt + 1) * kTileBytes, lane);
+      for (int c = 0; c < NC; c++) wn[c] = load_lane_tile(wbase[c] + (int64_t)(kt + 1) * kTileBytes, lane);
     }
-    if (cols_on) step_mfma<NS, 4>(sh, sh.a[kt & 1], wt, lane, acc);
+    if (cols_on) step_mfma<NS, NC>(sh, sh.a[kt & 1], wt, lane, acc);
     if (more) {
 #pragma unroll
-      for (int c = 0; c < 4; c++) wt[c] = wn[c];
+      for (int c = 0; c < NC; c++) wt[c] = wn[c];
     }
     wait_loads();
     __syncthreads();
@@ -202,8 +207,8 @@ __device__ void gate_up_tile(BfLds& sh, const Chunk& ch, const uint16_t* __restr
       if (m < ch.count) {
         const int64_t hrow = routed ? (int64_t)ch.first + m : (int64_t)TK + ch.first + m;
 #pragma unroll
-        for (int c = 0; c < 2; c++) {
-          const float g = acc[s][c][v], u = acc[s][c + 2][v];
+        for (int c = 0; c < kGuTiles; c++) {
+          const float g = acc[s][c][v], u = acc[s][c + kGuTiles][v];
           const float hv = g / (1.0f + expf(-g)) * u;
           h[hrow * F + col0 + 16 * c + (lane & 15)] = __builtin_bit_cast(uint16_t, (__bf16)hv);
         }
@@ -252,35 +257,36 @@ __device__ void down_tile(BfLds& sh, const Chunk& ch, int H, int F, const uint8_
   const bool cols_on = col0 < H;
   const int nkg = F / kBfStep;
   const int rt0 = (cols_on ? col0 : 0) >> 4;
-  const uint8_t* wbase[4];
+  constexpr int NC = kDnTiles;
+  const uint8_t* wbase[NC];
 #pragma unroll
-  for (int c = 0; c < 4; c++) wbase[c] = ex + (int64_t)(rt0 + c) * nkg * kTileBytes;
+  for (int c = 0; c < NC; c++) wbase[c] = ex + (int64_t)(rt0 + c) * nkg * kTileBytes;
 
-  f32x4 acc[NS][4];
+  f32x4 acc[NS][NC];
 #pragma unroll
   for (int s = 0; s < NS; s++)
 #pragma unroll
-    for (int c = 0; c < 4; c++) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; c++) acc[s][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   stage_rows(sh.a[0], h, F, sh.src, 0, n_rows, wave, lane);
-  LaneTile wt[4];
+  LaneTile wt[NC];
 #pragma unroll
-  for (int c = 0; c < 4; c++) wt[c] = load_lane_tile(wbase[c], lane);
+  for (int c = 0; c < NC; c++) wt[c] = load_lane_tile(wbase[c], lane);
   wait_loads();
   __syncthreads();
 
   for (int kt = 0; kt < nkg; kt++) {
     const bool more = kt + 1 < nkg;
-    LaneTile wn[4];
+    LaneTile wn[NC];
     if (more) {
       stage_rows(sh.a[(kt + 1) & 1], h, F, sh.src, (kt + 1) * kBfStep, n_rows, wave, lane);
 #pragma unroll
-      for (int c = 0; c < 4; c++) wn[c] = load_lane_tile(wbase[c] + (int64_t)(kt + 1) * kTileBytes, lane);
+      for (int c = 0; c < NC; c++) wn[c] = load_lane_tile(wbase[c] + (int64_t)(kt + 1) * kTileBytes, lane);
     }
-    if (cols_on) step_mfma<NS, 4>(sh, sh.a[kt & 1], wt, lane, acc);
+    if (cols_on) step_mfma<NS, NC>(sh, sh.a[kt & 1], wt, lane, acc);
     if (more) {
 #pragma unroll
-      for (int c = 0; c < 4; c++) wt[c] = wn[c];
+      for (int c = 0; c < NC; c++) wt[c] = wn[c];
     }
     wait_loads();
     __syncthreads();
@@ -295,7 +301,7 @@ __device__ void down_tile(BfLds& sh, const Chunk& ch, int H, int F, const uint8_
       if (m < ch.count) {
         float* yr = y + (row0 + m) * H + col0 + (lane & 15);
 #pragma unroll
-        for (int c = 0; c < 4; c++) yr[16 * c] = acc[s][c][v];
+        for (int c = 0; c < NC; c++) yr[16 * c] = acc[s][c][v];
       }
     }
   }
