@@ -62,10 +62,12 @@ def measured_traffic(record):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, rec["kernel_source"])
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
-            return None
+    sources = rec["kernel_sources"] if "kernel_sources" in rec else [rec["kernel_source"]]
+    hashes = rec["sha256"] if isinstance(rec["sha256"], list) else [rec["sha256"]]
+    for src, sha in zip(sources, hashes):
+        with open(os.path.join(ROOT, src), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != sha:
+                return None
     return int(rec["bytes_per_call"])
 
 
@@ -191,7 +193,7 @@ def run_prefill(args):
         # HBM floor (bytes / 8 TB/s) is above its MFMA floor (flops / 2.5 PFLOP/s): it is HBM-bound.
         "roofline": {"bound": "hbm" if ffn_bytes / HBM_PEAK_GBS > flops / 1e3 / MFMA_BF16_PEAK_TFLOPS else "mfma",
                      "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill_traffic.json"),
                      "kernel": "moe_expert_forward bf16: k_bucket + k_gate_up_bf16 + k_down_bf16 + k_combine "
                                "(events around the call)",
                      "bytes_per_launch": ffn_bytes, "flops_per_launch": flops,
