@@ -29,6 +29,7 @@ namespace qmoe {
 
 constexpr int kBucketThreads = 1024;
 constexpr int kBucketWaves = kBucketThreads / 64;
+constexpr int kKeysPerLane = 16;  // routes a lane holds in registers per pass (64 x 16 per wavefront)
 
 // Inclusive prefix sum over the 64 lanes of a wavefront.
 __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
@@ -38,6 +39,32 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
     if (lane >= d) v += o;
   }
   return v;
+}
+
+// One step of the scatter: 64 routes in route order (lane = order).  Lanes
+// holding the same expert find each other with 8 ballots (one per bit of the
+// expert id) and rank themselves by lane; position = expert offset + routes
+// of that expert before this step (run, the wavefront's running count) +
+// lane rank.
+__device__ __forceinline__ void scatter_step(bool valid, int key, int r, uint64_t below, int32_t* run,
+                                             const int32_t* s_off, int32_t* __restrict__ perm,
+                                             int32_t* __restrict__ pos) {
+  uint64_t peers = __ballot(valid);
+#pragma unroll
+  for (int bit = 0; bit < 8; bit++) {
+    const uint64_t b = __ballot(valid && ((key >> bit) & 1));
+    peers &= ((key >> bit) & 1) ? b : ~b;
+  }
+  const int rank = __popcll(peers & below);
+  const int before = run[key];
+  if (valid) {
+    const int at = s_off[key] + before + rank;
+    perm[at] = r;
+    if (pos) pos[r] = at;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (valid && rank == 0) run[key] = before + __popcll(peers);
+  __builtin_amdgcn_wave_barrier();
 }
 
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int T, int K, int E,
@@ -58,8 +85,18 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   const int r0 = min(R, wave * seg), r1 = min(R, r0 + seg);
 
   for (int i = tid; i < kBucketWaves * 256; i += kBucketThreads) (&s_seg[0][0])[i] = 0;
+  // the first 64 x kKeysPerLane routes of the segment stay in registers for the scatter
+  int key0[kKeysPerLane];
+#pragma unroll
+  for (int j = 0; j < kKeysPerLane; j++) {
+    const int r = r0 + 64 * j + lane;
+    key0[j] = r < r1 ? ids[r] : 0;
+  }
   __syncthreads();
-  for (int r = r0 + lane; r < r1; r += 64) atomicAdd(&s_seg[wave][ids[r]], 1);
+#pragma unroll
+  for (int j = 0; j < kKeysPerLane; j++)
+    if (r0 + 64 * j + lane < r1) atomicAdd(&s_seg[wave][key0[j]], 1);
+  for (int r = r0 + 64 * kKeysPerLane + lane; r < r1; r += 64) atomicAdd(&s_seg[wave][ids[r]], 1);
   __syncthreads();
 
   // per expert: exclusive scan over the segments, total count, chunk count
@@ -129,29 +166,23 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   }
   if (tid == 0 && want_chunks) *n_chunks = routed_chunks + shared_chunks;
 
-  // stable scatter, each wavefront over its own segment in route order
+  // stable scatter, each wavefront over its own segment in route order, 64 x
+  // kKeysPerLane routes per pass with all their ids requested at once
   int32_t* run = s_seg[wave];
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = r0; base < r1; base += 64) {
-    const int r = base + lane;
-    const bool valid = r < r1;
-    const int key = valid ? ids[r] : 0;
-    uint64_t peers = __ballot(valid);
+  for (int pass = 0; r0 + 64 * kKeysPerLane * pass < r1; pass++) {
+    int key_p[kKeysPerLane];
 #pragma unroll
-    for (int bit = 0; bit < 8; bit++) {
-      const uint64_t b = __ballot(valid && ((key >> bit) & 1));
-      peers &= ((key >> bit) & 1) ? b : ~b;
+    for (int j = 0; j < kKeysPerLane; j++) {
+      const int r = r0 + 64 * (kKeysPerLane * pass + j) + lane;
+      key_p[j] = pass == 0 ? key0[j] : (r < r1 ? ids[r] : 0);
     }
-    const int rank = __popcll(peers & below);
-    const int before = run[key];
-    if (valid) {
-      const int at = s_off[key] + before + rank;
-      perm[at] = r;
-      if (pos) pos[r] = at;
+#pragma unroll
+    for (int j = 0; j < kKeysPerLane; j++) {
+      const int base = r0 + 64 * (kKeysPerLane * pass + j);
+      if (base >= r1) break;
+      scatter_step(base + lane < r1, key_p[j], base + lane, below, run, s_off, perm, pos);
     }
-    __builtin_amdgcn_wave_barrier();
-    if (valid && rank == 0) run[key] = before + __popcll(peers);
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
