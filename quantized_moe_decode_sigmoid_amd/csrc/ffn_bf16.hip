@@ -47,12 +47,31 @@ constexpr int kStageLoads = kBfRows / 4 / kBfWaves;  // 1 KB LDS DMA loads per w
 // operand fetch fall into distinct banks.  The buffers come first: the LDS
 // address of an LDS DMA load is taken from the low 16 bits of M0, so its
 // destinations must lie in the first 64 KB of the workgroup's LDS.
+//
+// The table starts at 64 KB: 256 entries (one per byte of nibbles: the fp16
+// levels of its low and high nibble) x 64 replicas, entry e of lane l at byte
+// 65536 + 256 e + 4 l.  That address is one v_perm_b32 of the nibble word
+// and a per-lane constant, and the 64 lanes of a lookup hit 64 banks.
+constexpr int kTblReplicas = 64;
+constexpr int kTblWords = 256 * kTblReplicas;
 struct BfLds {
   uint16_t a[2][kBfRows * kBfStep];
-  __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
+  __attribute__((aligned(16))) uint32_t tbl[kTblWords];
   int32_t src[kBfRows];  // source row of each tile row (x row or h row)
 };
-static_assert(sizeof(uint16_t) * 2 * kBfRows * kBfStep <= 65536, "LDS DMA destinations beyond 64 KB");
+static_assert(sizeof(uint16_t) * 2 * kBfRows * kBfStep == 65536, "the table starts at 64 KB");
+static_assert(offsetof(BfLds, tbl) == 65536, "the table starts at 64 KB");
+
+// The fp16 level pairs (exact), kTblReplicas copies of each entry.
+__device__ __forceinline__ void build_pair_table_f16_64(uint32_t* tbl) {
+  for (int i = threadIdx.x; i < kTblWords / 4; i += blockDim.x) {
+    const int v = i / (kTblReplicas / 4);
+    const uint32_t e = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)iq4nl_level(v & 15)) |
+                       ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)iq4nl_level(v >> 4)) << 16);
+    uint32_t __attribute__((ext_vector_type(4))) q = {e, e, e, e};
+    *reinterpret_cast<decltype(q)*>(tbl + 4 * i) = q;
+  }
+}
 static_assert(kBfSub == 8, "the k-loop is instantiated for 1 .. 8 sub-tiles");
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -63,14 +82,18 @@ typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 // scale in fp32 (v_fma_mix_f32 with addend +0: the product is exact; a zero
 // product comes out +0 whatever its sign, which no sum can tell apart), both
 // rounded to nearest even by one v_cvt_pk_bf16_f32.
-__device__ __forceinline__ bf16x8 dequant_bf16(const uint32_t* tbl, uint32_t word, _Float16 d, uint32_t lane32) {
+// lane_sel = 4 * lane | 1 << 16: the address of byte i of word is
+// perm(word, lane_sel) with bytes (lane_sel.b0, word.b_i, lane_sel.b2, 0).
+__device__ __forceinline__ bf16x8 dequant_bf16(const BfLds& sh, uint32_t word, _Float16 d, uint32_t lane_sel) {
+  const char* lds0 = reinterpret_cast<const char*>(sh.tbl) - 65536;
   union {
     uint32_t u[4];
     bf16x8 v;
   } r;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const uint32_t e = tbl[((word >> (8 * i)) & 0xffu) * 32u + lane32];
+    const uint32_t addr = __builtin_amdgcn_perm(word, lane_sel, 0x0c020400u + 0x100u * i);
+    const uint32_t e = *reinterpret_cast<const uint32_t*>(lds0 + addr);
     const _Float16 l0 = __builtin_bit_cast(_Float16, (uint16_t)(e & 0xffffu));
     const _Float16 l1 = __builtin_bit_cast(_Float16, (uint16_t)(e >> 16));
     const f32x2 w = {__builtin_fmaf((float)l0, (float)d, 0.0f), __builtin_fmaf((float)l1, (float)d, 0.0f)};
@@ -136,7 +159,7 @@ __device__ __forceinline__ void step_mfma(const BfLds& sh, const uint16_t* a, co
   for (int b = 0; b < 4; b++) {
     bf16x8 bop[NC];
 #pragma unroll
-    for (int c = 0; c < NC; c++) bop[c] = dequant_bf16(sh.tbl, wt[c].nib[b], lane_scale(wt[c], b), lane & 31);
+    for (int c = 0; c < NC; c++) bop[c] = dequant_bf16(sh, wt[c].nib[b], lane_scale(wt[c], b), (lane << 2) | 0x10000u);
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       const bf16x8 aop = a_operand(a, s, b, lane);
@@ -232,7 +255,7 @@ __global__ __launch_bounds__(kBfThreads) void k_gate_up_bf16(
     const int i = min((int)threadIdx.x, ch.count - 1);
     sh.src[threadIdx.x] = routed ? perm[ch.first + i] / K : ch.first + i;
   }
-  build_pair_table_f16(sh.tbl);
+  build_pair_table_f16_64(sh.tbl);
   __syncthreads();
   const int col0 = slab * (kBfWaves * kGuCols) + wave * kGuCols;
   const int64_t mat_bytes = expert_bytes / 3;
@@ -321,7 +344,7 @@ __global__ __launch_bounds__(kBfThreads) void k_down_bf16(
   const int TK = T * K;
   const int64_t row0 = routed ? (int64_t)ch.first : (int64_t)TK + ch.first;
   if (threadIdx.x < kBfRows) sh.src[threadIdx.x] = (int32_t)(row0 + min((int)threadIdx.x, ch.count - 1));
-  build_pair_table_f16(sh.tbl);
+  build_pair_table_f16_64(sh.tbl);
   __syncthreads();
   const int col0 = slab * (kBfWaves * kDnCols) + wave * kDnCols;
   const int64_t mat_bytes = expert_bytes / 3;
