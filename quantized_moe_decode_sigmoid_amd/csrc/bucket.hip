@@ -19,9 +19,12 @@
 //      offset + earlier segments + running count + lane rank, which is
 //      exactly the stable order (ascending route id in an expert).
 // No step after the scans needs a workgroup barrier.
-// The same pass writes the work list of the FFN kernels: chunks of at most
-// chunk_rows routes of one expert, then chunks of chunk_rows tokens of the
-// shared expert (chunk_rows is a power of two).
+// The same pass writes the work list of the FFN kernels (chunk_rows is a
+// power of two), largest chunks first so that the long ones do not start
+// last: the shared expert's chunks of chunk_rows tokens, then every full
+// chunk of chunk_rows routes of one expert (expert order), then each
+// expert's remainder chunk, by size descending (ties by expert index).  The
+// order only schedules work: every chunk writes its own outputs.
 #include "device.h"
 #include "launch.h"
 
@@ -76,7 +79,8 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   __shared__ int32_t s_cnt[256];
   __shared__ int32_t s_off[256];
   __shared__ int32_t s_chunk_first[257];
-  __shared__ int32_t s_part[2][4];
+  __shared__ int32_t s_part[3][4];
+  __shared__ int32_t s_key[256];  // remainder chunk sort key, or INT32_MAX
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -99,9 +103,10 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   for (int r = r0 + 64 * kKeysPerLane + lane; r < r1; r += 64) atomicAdd(&s_seg[wave][ids[r]], 1);
   __syncthreads();
 
-  // per expert: exclusive scan over the segments, total count, chunk count
+  // per expert: exclusive scan over the segments, total count, full chunks,
+  // remainder
   const int rows = 1 << chunk_shift;
-  int cnt = 0, nch = 0;
+  int cnt = 0, nch = 0, rem = 0;
   if (tid < 256) {
 #pragma unroll
     for (int w = 0; w < kBucketWaves; w++) {
@@ -110,20 +115,25 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
       cnt += c;
     }
     if (tid >= E) cnt = 0;
-    nch = (cnt + rows - 1) >> chunk_shift;
+    nch = cnt >> chunk_shift;
+    rem = cnt & (rows - 1);
     s_cnt[tid] = cnt;
+    s_key[tid] = rem > 0 ? ((rows - rem) << 8) | tid : 0x7fffffff;
   }
   // exclusive scan over the experts (four wavefronts of 64 experts)
-  int inc_c = 0, inc_n = 0;
+  int inc_c = 0, inc_n = 0, inc_r = 0;
   if (tid < 256) {
     inc_c = wave_inclusive_scan(cnt, lane);
     inc_n = wave_inclusive_scan(nch, lane);
+    inc_r = wave_inclusive_scan(rem > 0 ? 1 : 0, lane);
     if (lane == 63) {
       s_part[0][wave] = inc_c;
       s_part[1][wave] = inc_n;
+      s_part[2][wave] = inc_r;
     }
   }
   __syncthreads();
+  int n_rem = 0;
   if (tid < 256) {
     int pc = 0, pn = 0;
     for (int w = 0; w < wave; w++) {
@@ -134,6 +144,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
     s_chunk_first[tid] = pn + inc_n - nch;
     if (tid == 255) s_chunk_first[256] = pn + inc_n;
   }
+  for (int w = 0; w < 4; w++) n_rem += s_part[2][w];
   __syncthreads();
   for (int e = tid; e < E; e += kBucketThreads) {
     counts[e] = s_cnt[e];
@@ -143,28 +154,39 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
 
   // chunk list (independent of the permutation itself); optional
   const bool want_chunks = chunks != nullptr;
-  const int routed_chunks = s_chunk_first[256];
-  if (want_chunks && tid < E) {
-    const int c0 = s_chunk_first[tid];
-    for (int j = 0; j < nch; j++) {
-      Chunk c;
-      c.expert = tid;
-      c.first = s_off[tid] + rows * j;
-      c.count = min(rows, cnt - rows * j);
-      c.pad = 0;
-      chunks[c0 + j] = c;
-    }
-  }
   const int shared_chunks = n_shared ? (T + rows - 1) >> chunk_shift : 0;
+  const int full_chunks = s_chunk_first[256];
   for (int j = tid; want_chunks && j < shared_chunks; j += kBucketThreads) {
     Chunk c;
     c.expert = -1;
     c.first = j << chunk_shift;
     c.count = min(rows, T - (j << chunk_shift));
     c.pad = 0;
-    chunks[routed_chunks + j] = c;
+    chunks[j] = c;
   }
-  if (tid == 0 && want_chunks) *n_chunks = routed_chunks + shared_chunks;
+  if (want_chunks && tid < E) {
+    const int c0 = shared_chunks + s_chunk_first[tid];
+    for (int j = 0; j < nch; j++) {
+      Chunk c;
+      c.expert = tid;
+      c.first = s_off[tid] + rows * j;
+      c.count = rows;
+      c.pad = 0;
+      chunks[c0 + j] = c;
+    }
+    if (rem > 0) {
+      const int key = s_key[tid];
+      int rank = 0;
+      for (int q = 0; q < E; q++) rank += s_key[q] < key;
+      Chunk c;
+      c.expert = tid;
+      c.first = s_off[tid] + rows * nch;
+      c.count = rem;
+      c.pad = 0;
+      chunks[shared_chunks + full_chunks + rank] = c;
+    }
+  }
+  if (tid == 0 && want_chunks) *n_chunks = shared_chunks + full_chunks + n_rem;
 
   // stable scatter, each wavefront over its own segment in route order, 64 x
   // kKeysPerLane routes per pass with all their ids requested at once
