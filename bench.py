@@ -214,7 +214,7 @@ def run_prefill(args):
 def chain(torch, x, out):
     """Next layer's input: bf16(rmsnorm(x + out)), eps 1e-6, no weight (harness glue standing in for the
     rest of a decoder block; not part of the MoE layer)."""
-    h = x.float() + out
+    h = torch.add(out, x)  # fp32 + bf16 -> fp32 in one elementwise kernel (exact widening of x)
     return torch.nn.functional.rms_norm(h, (h.shape[-1],), eps=1e-6).to(torch.bfloat16)
 
 

@@ -8,10 +8,11 @@
 // stay fp32 (PocketLLM design record, section 2).
 //
 // Work: tiles of up to 128 routes of one expert (bucketed order, design
-// record section 4) or 128 tokens of the shared expert.  A workgroup of 8
-// wavefronts owns one tile and one slab of output columns; wavefront w owns
-// 32 gate columns and the same 32 up columns (gate/up) or 64 output columns
-// (down), over all rows of the tile.  Per 128-wide step of the reduction:
+// record section 4) or 128 tokens of the shared expert, largest first.  A
+// workgroup of 16 wavefronts owns one tile and one slab of output columns;
+// wavefront w owns 16 gate columns and the same 16 up columns (gate/up, 256 +
+// 256 per workgroup) or 32 output columns (down, 512 per workgroup), over all
+// rows of the tile.  Per 128-wide step of the reduction:
 //   - the tile's activation rows (the A operand, the same for every
 //     wavefront) go from global memory straight into LDS (LDS DMA loads,
 //     double buffered, one step ahead): gathered rows of x for gate/up,
