@@ -136,6 +136,46 @@ def layer_parity(name, T, first=0, sample=None, bias=None, precision=qm.PREC_AUT
     return out
 
 
+# Shapes off the pages' configurations, for the corners of the supported range: no shared
+# expert with an odd K, the largest expert count with a small hidden size, K = 1, and the largest
+# hidden size of the decode plan.
+EXTRA_SHAPES = {
+    "noshared_k3": synth.Shape("noshared_k3", 1, 512, 16, 3, 256, n_shared=0, routed_scale=1.5, seed=21),
+    "e256_k4": synth.Shape("e256_k4", 1, 512, 256, 4, 128, seed=22),
+    "k1": synth.Shape("k1", 1, 256, 4, 1, 128, routed_scale=1.0, seed=23),
+    "h4096": synth.Shape("h4096", 1, 4096, 8, 2, 256, seed=24),
+}
+
+
+def extra_layer_parity(name, T, first=0):
+    s = EXTRA_SHAPES[name]
+    key = (name, 0)
+    if key not in _CACHE:
+        _CACHE[key] = (s, synth.layer_inputs(s))
+    inp = _CACHE[key][1]
+    dl = qm.DeviceLayer(cfg_of(s), inp["gate_w"], None, inp["arena"], inp["shared"])
+    x = synth.tokens(s, T, first=first)
+    prec = qm.moe_resolved_precision(dl.cfg, T)
+    log(f"layer {name} T={T} precision={prec}")
+    ids = torch.empty((T, s.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.top_k), dtype=torch.float32, device="cuda")
+    out = dl.forward(to_dev_bf16(x), topk_ids=ids, topk_w=w).cpu().numpy()
+    mode = oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32
+    ref, rid, rw = oracle.layer(x, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn, s.routed_scale,
+                                None, mode)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), rw.view(np.uint32))
+    assert_close(out, ref, f"{name} T={T}")
+
+
+@pytest.mark.parametrize("name,T", [("noshared_k3", 1), ("noshared_k3", 40), ("noshared_k3", 300),
+                                    ("e256_k4", 1), ("e256_k4", 77), ("e256_k4", 1200),
+                                    ("k1", 1), ("k1", 33), ("k1", 600), ("h4096", 1), ("h4096", 19)])
+def test_layer_shape_corners(name, T):
+    """Decode plan (T = 1), FP32 and BF16 multi-kernel plans on shapes at the edges of the supported range."""
+    extra_layer_parity(name, T, first=3 * T)
+
+
 def test_layer_tiny():
     layer_parity("tiny", 4)
 
