@@ -32,9 +32,9 @@ PLACEMENTS = 32
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--workload", choices=["decode", "prefill", "stack"], default="decode",
+    p.add_argument("--workload", choices=["decode", "prefill", "stack", "batch"], default="decode",
                    help="decode: the headline T=1 line (default); prefill: one T=2048 layer call per step; "
-                        "stack: 38 chained layers per step, T=1")
+                        "stack: 38 chained layers per step, T=1; batch: one T=128 Xing4 layer call per step")
     p.add_argument("--stack-layers", type=int, default=38, help="layers of the stack workload")
     p.add_argument("--stack-tokens", type=int, default=20,
                    help="distinct tokens captured in the stack graph (steps per replay)")
@@ -83,6 +83,39 @@ def copy_calibration(mib):
     del src, dst
 
 
+def stream_gbs(torch):
+    """The box's own streaming rates: a 1 GiB device copy (read + write) and a 1 GiB sum (read), best of 3."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    copy_s, read_s = [], []
+    for _ in range(3):
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record()
+        dst.copy_(src)
+        b.record()
+        src.sum()
+        c.record()
+        torch.cuda.synchronize()
+        copy_s.append(a.elapsed_time(b) / 1e3)
+        read_s.append(b.elapsed_time(c) / 1e3)
+    del src, dst
+    return {"copy_gbs": round(2 * (1 << 30) / min(copy_s) / 1e9, 1), "read_gbs": round((1 << 30) / min(read_s) / 1e9, 1)}
+
+
+def cpu_info():
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -94,6 +127,8 @@ def main():
         run_prefill(args)
     elif args.workload == "stack":
         run_stack(args)
+    elif args.workload == "batch":
+        run_batch(args)
     else:
         run_decode(args)
 
@@ -155,6 +190,9 @@ def run_prefill(args):
     ffn_us = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)])
     counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
     flops = 2.0 * 3 * H * F * (T * K + T * shape.n_shared)
+    # MFMA rows the 16-row sub-tiles execute per useful row (tiles of 128 routes of one expert)
+    rows_useful = T * K + T * shape.n_shared
+    rows_run = sum(16 * ((c + 15) // 16) for c in counts.tolist()) + 16 * ((T + 15) // 16) * shape.n_shared
     ffn_tflops = flops / (float(np.mean(ffn_us)) * 1e-6) / 1e12
     # algorithmic bytes of one moe_expert_forward call: every expert once (routed + shared), x, the
     # routing (ids + weights), the fp32 output
@@ -171,7 +209,7 @@ def run_prefill(args):
                      oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32)
         cs = time.time() - c0
         cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"the first {n} of the {T} tokens in one oracle.layer call, {cs:.1f} s"}
+               "sample": f"the first {n} of the {T} tokens in one oracle.layer call, {cs:.1f} s", **cpu_info()}
 
     res = {
         "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
@@ -205,7 +243,113 @@ def run_prefill(args):
         "tok_s": round(T / (layer_ms * 1e-3), 1),
         "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
                               "median": float(np.median(counts))},
+        "mfma_rows_per_useful_row": round(rows_run / rows_useful, 4),
         "first_step_ms": round(first_ms, 3),
+        "setup_s": round(gen_s, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
+def run_batch(args):
+    """One Xing4 layer call of T=128 tokens per step (zero selection bias), on the multi-kernel exact-weight
+    path; four placements of the layer cycled so that consecutive steps do not share cached weights."""
+    import torch
+
+    import quantized_moe_decode_sigmoid_amd as qm
+    import synth
+
+    shape = synth.WORKLOADS["batch"]
+    T, H, E, K, F = shape.tokens, shape.hidden, shape.n_experts, shape.top_k, shape.ffn
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = synth.layer_inputs(shape)
+    x_bits = synth.tokens(shape, T)
+    gen_s = time.time() - t0
+    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
+    prec = qm.moe_resolved_precision(cfg, T)
+    n_place = 4
+    dl = qm.DeviceLayer(cfg, inp["gate_w"], None, inp["arena"], inp["shared"])
+    places = [(dl.gate_w.clone(), dl.arena.clone(), dl.shared.clone()) for _ in range(n_place)]
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, K), dtype=torch.float32, device=dev)
+    ws = dl.workspace(T)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        def step(i):
+            g, a, sh = places[i % n_place]
+            qm.moe_layer_forward(cfg, T, x, g, None, a, sh, out, ids, wts, ws)
+
+        for i in range(max(args.warmup, n_place)):
+            step(i)
+        torch.cuda.synchronize()
+        n_steps = max(args.steps, n_place)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for i in range(n_steps):
+            step(i)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        layer_ms = ev0.elapsed_time(ev1) / n_steps
+        # events around each call, queued behind a spin kernel so that host launch time does not enter
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
+        torch.cuda._sleep(50_000_000)
+        for i in range(n_steps):
+            starts[i].record(stream)
+            step(i)
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+    call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)])
+    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
+    touched = int((counts > 0).sum())
+    eb = qm.moe_expert_bytes(cfg)
+    # algorithmic bytes of one call: each expert the batch routes to once, the shared expert, the router
+    # weight, x, the fp32 output
+    call_bytes = (touched + shape.n_shared) * eb + E * H * 4 + T * H * 2 + T * H * 4
+    gbs = call_bytes / (float(np.mean(call_us)) * 1e-6) / 1e9
+
+    cpu = None
+    if args.cpu_sample > 0:
+        import oracle
+        n = min(args.cpu_sample, T)
+        c0 = time.time()
+        oracle.layer(x_bits[:n], inp["gate_w"], inp["arena"], inp["shared"], K, F, shape.routed_scale, None,
+                     oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32)
+        cs = time.time() - c0
+        cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
+               "sample": f"the first {n} of the {T} tokens in one oracle.layer call, {cs:.1f} s", **cpu_info()}
+
+    res = {
+        "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
+        "value": round(T / (layer_ms * 1e-3), 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": max(args.warmup, n_place),
+        "ms_per_step": round(layer_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if prec == qm.PREC_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": "xing4 MoE layer, T=128 per call: hidden 3584, 64 experts top-4 + 1 shared, ffn "
+                               "1024, IQ4_NL experts, sigmoid router, scale 2.0, no selection bias; "
+                               f"{n_place} placements cycled",
+                   "tokens_per_step": T},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "moe_layer_forward T=128: router, top-k, bucketing, gate/up, down, combine "
+                               "(events around the call)",
+                     "bytes_per_launch": call_bytes, "avg_us": round(float(np.mean(call_us)), 3),
+                     "median_us": round(float(np.median(call_us)), 3)},
+        "cpu_baseline": cpu,
+        "experts_touched": touched,
+        "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
+                              "median": float(np.median(counts))},
         "setup_s": round(gen_s, 1),
     }
     print(json.dumps(res), flush=True)
@@ -214,7 +358,7 @@ def run_prefill(args):
 def chain(torch, x, out):
     """Next layer's input: bf16(rmsnorm(x + out)), eps 1e-6, no weight (harness glue standing in for the
     rest of a decoder block; not part of the MoE layer)."""
-    h = torch.add(out, x)  # fp32 + bf16 -> fp32 in one elementwise kernel (exact widening of x)
+    h = x.float() + out  # two same-dtype elementwise kernels: a mixed-dtype add is far slower here
     return torch.nn.functional.rms_norm(h, (h.shape[-1],), eps=1e-6).to(torch.bfloat16)
 
 
@@ -443,7 +587,8 @@ def run_decode(args):
             oracle.layer(x_bits[i:i + 1], l["gate_w"], l["arena"], l["shared"], K, F, shape.routed_scale)
         cs = time.time() - c0
         cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"{n} of the {N_TOKENS} tokens, one oracle.layer call (T=1) each, {cs:.1f} s"}
+               "sample": f"{n} of the {N_TOKENS} tokens, one oracle.layer call (T=1) each, {cs:.1f} s", **cpu_info()}
+    box = stream_gbs(torch)
 
     res = {
         "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
@@ -466,7 +611,8 @@ def run_decode(args):
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode_traffic.json"),
                      "kernel": "moe_layer_forward T=1: k_decode_scores + k_decode_experts (events around the call)",
                      "bytes_per_launch": layer_bytes, "avg_us": round(float(np.mean(ffn_us)), 3),
-                     "median_us": round(float(np.median(ffn_us)), 3)},
+                     "median_us": round(float(np.median(ffn_us)), 3),
+                     "box_stream": box, "frac_of_box_read": round(achieved / box["read_gbs"], 4)},
         "cpu_baseline": cpu,
         "layer_gbs": round(layer_bytes * tok_s / 1e9, 1),
         "first_step_ms": round(first_ms, 3),

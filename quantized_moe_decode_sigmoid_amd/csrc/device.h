@@ -93,6 +93,25 @@ __device__ __forceinline__ bf16x8 decode_word(const uint32_t* tbl, uint32_t word
   return r.v;
 }
 
+// 16 bytes per lane from global memory straight into LDS (LDS DMA): lane i
+// writes bytes [16i, 16i + 16) of the wavefront's 1 KB at lds (uniform over
+// the wavefront; the address comes from the low 16 bits of M0, so every
+// destination lies in the first 64 KB of LDS).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+
+// Every load of this wavefront (LDS DMA included) has landed.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Every load of this wavefront but the last N has landed (vector memory loads
+// complete in order): e.g. the LDS DMA issued before N register loads.
+template <int N>
+__device__ __forceinline__ void wait_dma_before() {
+  static_assert(N >= 0 && N <= 63, "vmcnt immediate (6 bits)");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // fp16 bits -> fp32.
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));

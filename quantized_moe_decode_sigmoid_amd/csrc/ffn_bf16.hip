@@ -142,9 +142,6 @@ __device__ __forceinline__ void stage_rows(uint16_t* a, const uint16_t* base, in
   }
 }
 
-// Every LDS DMA load and weight load of this wavefront has landed.
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // A operand of sub-tile s, block b: row 16s + lane%16, elements 32b + 8*(lane/16) .. +7.
 __device__ __forceinline__ bf16x8 a_operand(const uint16_t* a, int s, int b, int lane) {
   const int r = lane & 15;

@@ -18,16 +18,15 @@
 // activations are exact; only fp32 accumulation rounds.
 //
 // Memory: a packed tile (16 rows x 4 blocks, 1152 bytes) is read by one
-// wavefront with one 16-byte load per lane for the nibbles and two for the
-// scales, fully coalesced.  Each workgroup (4 waves) owns one (chunk, 16-row
-// tile) and splits the reduction dimension over its waves; partial results are
-// added in wave order through LDS, so results are deterministic.
+// wavefront with one 16-byte load per lane for the nibbles (into registers)
+// and one LDS DMA piece per lane covering the scales of 8 tiles, fully
+// coalesced.  A gate/up workgroup owns one (chunk, 16-row tile of F), a down
+// workgroup one (chunk, 64 rows of H); both split the reduction dimension
+// over 8 wavefronts.
 #include "device.h"
 #include "launch.h"
 
 namespace qmoe {
-
-constexpr int kFfnThreads = 256;
 
 // ---------------------------------------------------------------- packing
 
@@ -126,62 +125,139 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat
 
 // ---------------------------------------------------------------- gate / up
 
+// Both FFN kernels run 8 wavefronts per workgroup and split the reduction
+// dimension over them: wavefront w takes packed tiles [w n/8, (w+1) n/8) of
+// the n tiles of a row (n = H/128 for gate/up, F/128 for down), so each
+// activation (or h) element is read once per workgroup.  A wavefront first
+// requests everything its tiles need -- the nibble words and the B operands
+// into registers, the tiles' scales into its own 1 KB of LDS by LDS DMA --
+// and only then computes; partial sums are added in wavefront order through
+// LDS, so results are deterministic.
+constexpr int kExWaves = 8;
+constexpr int kExThreads = 64 * kExWaves;
+// gate/up: a wavefront requests the nibble words and scales of 4 tiles per
+// matrix at once (one pass covers H <= 4096) and holds the activation operands
+// of 3 tiles; the 4th tile's are requested when the first tile is done.
+constexpr int kGuPass = 4;
+constexpr int kGuXSlots = 3;
+constexpr int kDnRowTiles = 4;  // down: 16-row tiles of H per workgroup (8 spill at 128 VGPRs)
+
+struct GateUpExactLds {
+  uint32_t scales[kExWaves][256];  // per wavefront: [matrix][tile of the pass][32 words]; LDS DMA target
+  uint32_t tbl[kPairTableWords];
+  f32x4 red[2][kExWaves][64];
+};
+
+struct DownExactLds {
+  uint32_t scales[kExWaves][256];  // per wavefront: [row tile][32 words] of its current tile column
+  uint32_t tbl[kPairTableWords];
+  f32x4 red[kExWaves][kDnRowTiles / 2][64];  // the row tiles are reduced in two halves
+};
+
+// acc[0..3] (rows 4G..4G+3) += d * c, d from the word pair (rows 4G, 4G+1 | 4G+2, 4G+3).
+__device__ __forceinline__ void scale_acc_words(f32x4& acc, const f32x4& c, uint32_t s01, uint32_t s23) {
+  acc[0] = __builtin_fmaf(half_bits_to_float(s01), c[0], acc[0]);
+  acc[1] = __builtin_fmaf(half_bits_to_float(s01 >> 16), c[1], acc[1]);
+  acc[2] = __builtin_fmaf(half_bits_to_float(s23), c[2], acc[2]);
+  acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), c[3], acc[3]);
+}
+
 // Workgroup = (chunk, 16-row tile of F).  Output: the product h = silu(g)*u of
 // route column c, row f, as two bf16 halves h_hi = bf16(h), h_lo = bf16(h -
 // h_hi), row-major [route][F].
-__global__ __launch_bounds__(kFfnThreads) void k_gate_up_exact(
+__global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gate_up_exact(
     const uint16_t* __restrict__ x, int H, int F, int K, int T, const uint8_t* __restrict__ arena,
     const uint8_t* __restrict__ shared, int64_t expert_bytes, const int32_t* __restrict__ perm,
     const Chunk* __restrict__ chunks, const int32_t* __restrict__ n_chunks, uint16_t* __restrict__ h_hi,
     uint16_t* __restrict__ h_lo) {
-  __shared__ __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
-  __shared__ f32x4 red[2][4][64];
+  __shared__ __attribute__((aligned(16))) GateUpExactLds sh;
   const int n_rt = F >> 4;
   const int chunk_id = blockIdx.x / n_rt;
   const int rt = blockIdx.x % n_rt;
   if (chunk_id >= *n_chunks) return;
-  build_pair_table(tbl);
   const Chunk ch = chunks[chunk_id];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, G = lane >> 4;
   const int64_t mat_bytes = expert_bytes / 3;
   const uint8_t* ex = ch.expert >= 0 ? arena + (int64_t)ch.expert * expert_bytes : shared;
-  const int TK = T * K;
-  int tok = -1;
-  if (c < ch.count) tok = ch.expert >= 0 ? perm[ch.first + c] / K : ch.first + c;
-  const uint16_t* xr = x + (size_t)(tok >= 0 ? tok : 0) * H;
+  const bool live = c < ch.count;
+  const int cc = live ? c : 0;  // a column past the chunk reads column 0's token (never stored)
+  const int tok = ch.expert >= 0 ? perm[ch.first + cc] / K : ch.first + cc;
+  const uint16_t* xr = x + (size_t)tok * H;
   const int nkg = H >> 7;
-  const int kg0 = (wave * nkg) >> 2, kg1 = ((wave + 1) * nkg) >> 2;
-  const uint8_t* gate_t = ex + (int64_t)rt * nkg * kTileBytes;
-  const uint8_t* up_t = ex + mat_bytes + (int64_t)rt * nkg * kTileBytes;
-  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+  const int kg0 = wave * nkg / kExWaves, kg1 = (wave + 1) * nkg / kExWaves;
+  const uint8_t* gate_t = ex + (int64_t)rt * nkg * kTileBytes;  // up: mat_bytes further
+  uint32_t* my_scales = sh.scales[wave];
+
+  u32x4 ng[kGuPass], nu[kGuPass];
+  bf16x8 xb[kGuXSlots][4];
+  // the weight loads of the pass starting at tile p0: scales (piece = lane:
+  // matrix lane / 32, tile (lane / 8) % 4, 16 bytes lane % 8 of its 128) and
+  // nibble words; tiles past the range repeat a valid one (never used)
+  auto issue_weights = [&](int p0) {
+    {
+      const int m = lane >> 5, i = (lane >> 3) & 3, j = lane & 7;
+      const int kg = min(p0 + i, nkg - 1);
+      dma16(gate_t + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * j, my_scales);
+    }
+#pragma unroll
+    for (int i = 0; i < kGuPass; i++) {
+      const int kg = min(p0 + i, nkg - 1);
+      ng[i] = ld16(gate_t + (int64_t)kg * kTileBytes + 16 * lane);
+      nu[i] = ld16(gate_t + mat_bytes + (int64_t)kg * kTileBytes + 16 * lane);
+    }
+  };
+  auto issue_x = [&](int slot, int kg) {
+#pragma unroll
+    for (int b = 0; b < 4; b++) xb[slot][b] = load_x_operand(xr, 4 * min(kg, nkg - 1) + b, G);
+  };
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
-  for (int kg = kg0; kg < kg1; kg++) {
-    const uint8_t* tg = gate_t + (int64_t)kg * kTileBytes;
-    const uint8_t* tu = up_t + (int64_t)kg * kTileBytes;
-    const uint4 ng = *reinterpret_cast<const uint4*>(tg + 16 * lane);
-    const uint4 nu = *reinterpret_cast<const uint4*>(tu + 16 * lane);
-    const TileScales sg = load_scales(tg, G);
-    const TileScales su = load_scales(tu, G);
+  f32x4 accg = zero, accu = zero;
+  // tile i of the pass with the activations in slot
+  auto tile = [&](int i, int slot) {
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-      const bf16x8 xb = tok >= 0 ? load_x_operand(xr, 4 * kg + b, G) : zero_operand();
-      const f32x4 cg = mfma16x16x32(decode_word(tbl, uword(ng, b), lane & 31), xb, zero);
-      const f32x4 cu = mfma16x16x32(decode_word(tbl, uword(nu, b), lane & 31), xb, zero);
-      scale_acc(accg, cg, sg, b);
-      scale_acc(accu, cu, su, b);
+      const f32x4 cg = mfma16x16x32(decode_word(sh.tbl, ng[i][b], lane & 31), xb[slot][b], zero);
+      const f32x4 cu = mfma16x16x32(decode_word(sh.tbl, nu[i][b], lane & 31), xb[slot][b], zero);
+      const uint32_t* sg = my_scales + 32 * i + 8 * G + 2 * b;
+      const uint32_t* su = my_scales + 32 * (kGuPass + i) + 8 * G + 2 * b;
+      scale_acc_words(accg, cg, sg[0], sg[1]);
+      scale_acc_words(accu, cu, su[0], su[1]);
     }
+  };
+  // The scales are read only after a full wait: the compiler may move a
+  // read-only register load past an explicit wait, so counting the loads
+  // issued after the DMA would not be reliable.
+  for (int p0 = kg0; p0 < kg1 || p0 == kg0; p0 += kGuPass) {
+    issue_weights(p0);
+#pragma unroll
+    for (int i = 0; i < kGuXSlots; i++) issue_x(i, p0 + i);
+    if (p0 == kg0) {  // every wavefront, also one with no tiles: the table and the barrier
+      build_pair_table(sh.tbl);
+      wait_loads();
+      __syncthreads();
+    } else {  // only when H > 1024 kGuPass: this wavefront's own scales, no barrier needed
+      wait_loads();
+    }
+    const int np = min(kGuPass, kg1 - p0);
+    if (np <= 0) break;
+    tile(0, 0);
+    issue_x(0, p0 + 3);  // the 4th tile's activations, into the slot just used
+    if (np > 1) tile(1, 1);
+    if (np > 2) tile(2, 2);
+    if (np > 3) tile(3, 0);
   }
-  red[0][wave][lane] = accg;
-  red[1][wave][lane] = accu;
+  sh.red[0][wave][lane] = accg;
+  sh.red[1][wave][lane] = accu;
   __syncthreads();
-  if (wave != 0 || tok < 0) return;
-  f32x4 g = red[0][0][lane], u = red[1][0][lane];
-  for (int w = 1; w < 4; w++) {
-    g += red[0][w][lane];
-    u += red[1][w][lane];
+  if (wave != 0 || !live) return;
+  f32x4 g = sh.red[0][0][lane], u = sh.red[1][0][lane];
+#pragma unroll
+  for (int w = 1; w < kExWaves; w++) {
+    g += sh.red[0][w][lane];
+    u += sh.red[1][w][lane];
   }
+  const int TK = T * K;
   const int64_t hrow = ch.expert >= 0 ? (int64_t)(ch.first + c) : (int64_t)TK + tok;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
@@ -197,19 +273,20 @@ __global__ __launch_bounds__(kFfnThreads) void k_gate_up_exact(
 
 // ---------------------------------------------------------------- down
 
-// Workgroup = (chunk, 16-row tile of H).  y[hrow][n] = sum_f W_down[n][f] h[f]
-// in fp32, one row per route (bucketed position) or per shared-expert token.
-__global__ __launch_bounds__(kFfnThreads) void k_down_exact(
+// Workgroup = (chunk, kDnRowTiles row tiles of H).  y[hrow][n] = sum_f
+// W_down[n][f] h[f] in fp32, one row per route (bucketed position) or per
+// shared-expert token.  Wavefront w takes tile columns [w n/8, (w+1) n/8) of
+// F for all the workgroup's row tiles, one tile column at a time, so its h
+// operands serve each of them.
+__global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_down_exact(
     int H, int F, int K, int T, const uint8_t* __restrict__ arena, const uint8_t* __restrict__ shared,
     int64_t expert_bytes, const Chunk* __restrict__ chunks, const int32_t* __restrict__ n_chunks,
     const uint16_t* __restrict__ h_hi, const uint16_t* __restrict__ h_lo, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
-  __shared__ f32x4 red[4][64];
-  const int n_rt = H >> 4;
-  const int chunk_id = blockIdx.x / n_rt;
-  const int rt = blockIdx.x % n_rt;
+  __shared__ __attribute__((aligned(16))) DownExactLds sh;
+  const int n_slab = H / (16 * kDnRowTiles);
+  const int chunk_id = blockIdx.x / n_slab;
+  const int slab = blockIdx.x % n_slab;
   if (chunk_id >= *n_chunks) return;
-  build_pair_table(tbl);
   const Chunk ch = chunks[chunk_id];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, G = lane >> 4;
@@ -217,39 +294,70 @@ __global__ __launch_bounds__(kFfnThreads) void k_down_exact(
   const uint8_t* ex = ch.expert >= 0 ? arena + (int64_t)ch.expert * expert_bytes : shared;
   const int TK = T * K;
   const bool live = c < ch.count;
-  const int64_t hrow = ch.expert >= 0 ? (int64_t)(ch.first + c) : (int64_t)TK + ch.first + c;
-  const uint16_t* hh = h_hi + (live ? hrow : 0) * F;
-  const uint16_t* hl = h_lo + (live ? hrow : 0) * F;
+  const int cc = live ? c : 0;  // a column past the chunk reads column 0's h (never stored)
+  const int64_t hrow = ch.expert >= 0 ? (int64_t)(ch.first + cc) : (int64_t)TK + ch.first + cc;
+  const uint16_t* hh = h_hi + hrow * F;
+  const uint16_t* hl = h_lo + hrow * F;
   const int nkg = F >> 7;
-  const int kg0 = (wave * nkg) >> 2, kg1 = ((wave + 1) * nkg) >> 2;
-  const uint8_t* down_t = ex + 2 * mat_bytes + (int64_t)rt * nkg * kTileBytes;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
-  for (int kg = kg0; kg < kg1; kg++) {
-    const uint8_t* td = down_t + (int64_t)kg * kTileBytes;
-    const uint4 nd = *reinterpret_cast<const uint4*>(td + 16 * lane);
-    const TileScales sd = load_scales(td, G);
+  const int kg0 = wave * nkg / kExWaves, kg1 = (wave + 1) * nkg / kExWaves;
+  const int64_t rt_bytes = (int64_t)nkg * kTileBytes;
+  const uint8_t* rows = ex + 2 * mat_bytes + (int64_t)slab * kDnRowTiles * rt_bytes;
+  uint32_t* my_scales = sh.scales[wave];
+
+  u32x4 nib[kDnRowTiles];
+  bf16x8 bh[4], bl[4];
+  auto issue = [&](int kg) {
+    dma16(rows + min(lane >> 3, kDnRowTiles - 1) * rt_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes +
+              16 * (lane & 7),
+          my_scales);
+
+#pragma unroll
+    for (int t = 0; t < kDnRowTiles; t++) nib[t] = ld16(rows + t * rt_bytes + (int64_t)kg * kTileBytes + 16 * lane);
 #pragma unroll
     for (int b = 0; b < 4; b++) {
-      const int blk = 4 * kg + b;
-      bf16x8 bh = zero_operand(), bl = zero_operand();
-      if (live) {
-        bh = *reinterpret_cast<const bf16x8*>(hh + 32 * blk + 8 * G);
-        bl = *reinterpret_cast<const bf16x8*>(hl + 32 * blk + 8 * G);
-      }
-      const bf16x8 a = decode_word(tbl, uword(nd, b), lane & 31);
-      f32x4 cc = mfma16x16x32(a, bh, zero);
-      cc = mfma16x16x32(a, bl, cc);
-      scale_acc(acc, cc, sd, b);
+      bh[b] = *reinterpret_cast<const bf16x8*>(hh + 32 * (4 * kg + b) + 8 * G);
+      bl[b] = *reinterpret_cast<const bf16x8*>(hl + 32 * (4 * kg + b) + 8 * G);
     }
-  }
-  red[wave][lane] = acc;
+  };
+  issue(min(kg0, nkg - 1));
+  build_pair_table(sh.tbl);
+  wait_loads();  // as in k_gate_up_exact: a full wait before the scales are read
   __syncthreads();
-  if (wave != 0 || !live) return;
-  f32x4 s = red[0][lane];
-  for (int w = 1; w < 4; w++) s += red[w][lane];
-  *reinterpret_cast<f32x4*>(y + hrow * H + 16 * rt + 4 * G) = s;
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[kDnRowTiles];
+#pragma unroll
+  for (int t = 0; t < kDnRowTiles; t++) acc[t] = zero;
+  for (int kg = kg0; kg < kg1; kg++) {
+    if (kg != kg0) {  // only when F > 1024: this wavefront's own scales, no barrier needed
+      issue(kg);
+      wait_loads();
+    }
+#pragma unroll
+    for (int b = 0; b < 4; b++)
+#pragma unroll
+      for (int t = 0; t < kDnRowTiles; t++) {
+        const bf16x8 a = decode_word(sh.tbl, nib[t][b], lane & 31);
+        f32x4 cr = mfma16x16x32(a, bh[b], zero);
+        cr = mfma16x16x32(a, bl[b], cr);
+        const uint32_t* sd = my_scales + 32 * t + 8 * G + 2 * b;
+        scale_acc_words(acc[t], cr, sd[0], sd[1]);
+      }
+  }
+  // wavefront-order sums, four row tiles at a time; wavefront t stores row tile t
+#pragma unroll
+  for (int half = 0; half < 2; half++) {
+#pragma unroll
+    for (int t = 0; t < kDnRowTiles / 2; t++) sh.red[wave][t][lane] = acc[(kDnRowTiles / 2) * half + t];
+    __syncthreads();
+    if (wave < kDnRowTiles / 2 && live) {
+      f32x4 s = sh.red[0][wave][lane];
+#pragma unroll
+      for (int w = 1; w < kExWaves; w++) s += sh.red[w][wave][lane];
+      const int rt = slab * kDnRowTiles + (kDnRowTiles / 2) * half + wave;
+      *reinterpret_cast<f32x4*>(y + hrow * H + 16 * rt + 4 * G) = s;
+    }
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------- combine
@@ -317,13 +425,13 @@ hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n
                             uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   clear_last_error();
-  hipLaunchKernelGGL(k_gate_up_exact, dim3((unsigned)(max_chunks * (F / 16))), dim3(kFfnThreads), 0, stream, x, H, F,
+  hipLaunchKernelGGL(k_gate_up_exact, dim3((unsigned)(max_chunks * (F / 16))), dim3(kExThreads), 0, stream, x, H, F,
                      K, T, arena, shared, expert_bytes, perm, chunks, n_chunks, h_hi, h_lo);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   clear_last_error();
-  hipLaunchKernelGGL(k_down_exact, dim3((unsigned)(max_chunks * (H / 16))), dim3(kFfnThreads), 0, stream, H, F, K, T,
-                     arena, shared, expert_bytes, chunks, n_chunks, h_hi, h_lo, y);
+  hipLaunchKernelGGL(k_down_exact, dim3((unsigned)(max_chunks * (H / (16 * kDnRowTiles)))), dim3(kExThreads), 0, stream,
+                     H, F, K, T, arena, shared, expert_bytes, chunks, n_chunks, h_hi, h_lo, y);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_combine(y, pos, w, T, K, H, n_shared, out, stream);

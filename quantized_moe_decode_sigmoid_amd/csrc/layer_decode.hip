@@ -69,25 +69,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
-// 16 bytes per lane from global memory straight into LDS (LDS DMA): lane i
-// writes bytes [16i, 16i + 16) of the wavefront's 1 KB at lds (uniform over
-// the wavefront; the address comes from the low 16 bits of M0, so every
-// destination lies in the first 64 KB of LDS).
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
-}
-
-// Every load of this wavefront (LDS DMA included) has landed.
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Every load of this wavefront but the last N (vector loads complete in
-// order) has landed: the LDS DMA issued before N register loads.
-template <int N>
-__device__ __forceinline__ void wait_dma_before() {
-  static_assert(N >= 0 && N <= 15, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 __device__ __forceinline__ bool ready(uint4 v) {
   return v.x != kNotReady && v.y != kNotReady && v.z != kNotReady && v.w != kNotReady;
 }
