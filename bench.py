@@ -341,7 +341,7 @@ def run_batch(args):
                                f"{n_place} placements cycled",
                    "tokens_per_step": T},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("batch_traffic.json"),
                      "kernel": "moe_layer_forward T=128: router, top-k, bucketing, gate/up, down, combine "
                                "(events around the call)",
                      "bytes_per_launch": call_bytes, "avg_us": round(float(np.mean(call_us)), 3),

@@ -250,18 +250,22 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
   sh.red[0][wave][lane] = accg;
   sh.red[1][wave][lane] = accu;
   __syncthreads();
-  if (wave != 0 || !live) return;
-  f32x4 g = sh.red[0][0][lane], u = sh.red[1][0][lane];
+  // the lane's column and row group, recomputed (mbcnt) instead of kept live
+  // through the loop, which needs every register
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int c_e = lane_e & 15, G_e = lane_e >> 4;
+  if (wave != 0 || c_e >= ch.count) return;
+  f32x4 g = sh.red[0][0][lane_e], u = sh.red[1][0][lane_e];
 #pragma unroll
   for (int w = 1; w < kExWaves; w++) {
-    g += sh.red[0][w][lane];
-    u += sh.red[1][w][lane];
+    g += sh.red[0][w][lane_e];
+    u += sh.red[1][w][lane_e];
   }
-  const int TK = T * K;
-  const int64_t hrow = ch.expert >= 0 ? (int64_t)(ch.first + c) : (int64_t)TK + tok;
+  // bucketed position of the route, or T*K + token for the shared expert
+  const int64_t hrow = (ch.expert >= 0 ? 0 : (int64_t)T * K) + ch.first + c_e;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const int f = 16 * rt + 4 * G + i;
+    const int f = 16 * rt + 4 * G_e + i;
     const float gv = g[i];
     const float h = gv / (1.0f + expf(-gv)) * u[i];
     const uint32_t hb = f32_to_bf16_rne(h);

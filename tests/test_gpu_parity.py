@@ -144,6 +144,7 @@ EXTRA_SHAPES = {
     "e256_k4": synth.Shape("e256_k4", 1, 512, 256, 4, 128, seed=22),
     "k1": synth.Shape("k1", 1, 256, 4, 1, 128, routed_scale=1.0, seed=23),
     "h4096": synth.Shape("h4096", 1, 4096, 8, 2, 256, seed=24),
+    "h8192_f2048": synth.Shape("h8192_f2048", 1, 8192, 4, 2, 2048, seed=25),
 }
 
 
@@ -170,9 +171,14 @@ def extra_layer_parity(name, T, first=0):
 
 @pytest.mark.parametrize("name,T", [("noshared_k3", 1), ("noshared_k3", 40), ("noshared_k3", 300),
                                     ("e256_k4", 1), ("e256_k4", 77), ("e256_k4", 1200),
-                                    ("k1", 1), ("k1", 33), ("k1", 600), ("h4096", 1), ("h4096", 19)])
+                                    ("k1", 1), ("k1", 33), ("k1", 600), ("h4096", 1), ("h4096", 19),
+                                    ("h8192_f2048", 1), ("h8192_f2048", 19), ("h8192_f2048", 33)])
 def test_layer_shape_corners(name, T):
-    """Decode plan (T = 1), FP32 and BF16 multi-kernel plans on shapes at the edges of the supported range."""
+    """Decode plan (T = 1), FP32 and BF16 multi-kernel plans on shapes at the edges of the supported range.
+
+    h8192_f2048 (largest hidden size; above the decode plan's limits, so T = 1 takes the multi-kernel
+    FP32 plan): the exact-weight kernels walk their tiles in more than one pass (8 gate/up tiles and
+    2 down tiles per wavefront); T = 33 takes the BF16 plan."""
     extra_layer_parity(name, T, first=3 * T)
 
 
