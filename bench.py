@@ -42,7 +42,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--distinct-layers", type=int, default=4,
                    help="distinct seeded layers generated; placements reuse them at distinct addresses")
-    p.add_argument("--cpu-sample", type=int, default=24, help="tokens the CPU oracle runs (0: skip)")
+    p.add_argument("--cpu-sample", type=int, default=None,
+                   help="tokens the CPU oracle runs (0: skip; default: about 10 s of oracle work, 60 decode tokens, "
+                        "400 prefill tokens, the whole 128-token batch)")
     p.add_argument("--no-graph", action="store_true", help="replay eagerly instead of through a HIP graph")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run one plain device copy of this many MiB (a kernel of known traffic, to scale "
@@ -116,8 +118,13 @@ def cpu_info():
     return {"cpu_model": model, "nproc": os.cpu_count()}
 
 
+CPU_SAMPLE = {"decode": 60, "prefill": 400, "batch": 128, "stack": 0}
+
+
 def main():
     args = parse()
+    if args.cpu_sample is None:
+        args.cpu_sample = CPU_SAMPLE[args.workload]
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
