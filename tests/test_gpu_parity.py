@@ -204,6 +204,18 @@ def test_layer_batch_128_sampled():
     layer_parity("batch", 128, sample=[0, 1, 17, 63, 64, 100, 127])
 
 
+@pytest.mark.parametrize("precision", [qm.PREC_AUTO, qm.PREC_FP32])
+def test_layer_max_tokens_sampled(precision):
+    """T = 65536, the largest call the library accepts, on the Xing4 shape (auto takes the BF16 plan;
+    forced FP32 runs the exact-weight kernels over 20k+ chunks); first, last and interior rows."""
+    layer_parity("batch", 65536, sample=[0, 1, 4095, 4096, 32767, 65534, 65535], precision=precision)
+
+
+def test_layer_top8_small_batch_fp32():
+    """K = 8 (the largest top-k) on the FP32 multi-kernel plan: the prefill shape at T = 3."""
+    layer_parity("prefill", 3, first=11)
+
+
 def test_layer_many_routes_on_one_expert():
     """A selection bias that sends every token to experts 0..K-1: chunks of 16 per expert, ragged tail."""
     s, _ = workload("tiny")
