@@ -40,74 +40,81 @@ __global__ __launch_bounds__(256) void k_router_scores(const uint16_t* __restric
   }
 }
 
-// Batched calls: one workgroup per 16 tokens x 16 experts, four wavefronts of
-// 8 x 8.  Lane j keeps the partial sum p_j of all 64 (token, expert) pairs of
-// its wave in registers, each walking the same elements 256m + 4j + c in the
-// same (m, c) order as the single-row logit, so every partial is the one the
-// per-row form computes.  The 64 lane partials of each pair then go through
-// LDS and one lane per pair adds them in the butterfly's tree: level s pairs
-// index j with j + s for s = 32, 16, ..., 1 (fp32 addition commutes, so this
-// is exactly the value every lane of the shuffle butterfly ends with).
-constexpr int kRtTok = 8, kRtExp = 8, kRtStride = 68;
+// Batched calls: one wavefront per block of TT tokens x TE experts, four per
+// workgroup as 2 x 2 blocks (so that each token row and each router row a
+// workgroup reads serves two wavefronts).  Lane j keeps the partial sum p_j of
+// every (token, expert) pair of its block in registers, each walking the same
+// elements 256m + 4j + c in the same (m, c) order as the single-row logit, so
+// every partial is the one the per-row form computes; the operands of step
+// m + 1 are requested before step m is computed.  The 64 lane partials of each
+// pair then go through LDS and one lane per pair adds them in the butterfly's
+// tree: level s pairs index j with j + s for s = 32, 16, ..., 1 (fp32 addition
+// commutes, so this is exactly the value every lane of the shuffle butterfly
+// ends with).
+constexpr int kRtStride = 68;
 
+template <int TT, int TE>
 __global__ __launch_bounds__(256, 2) void k_router_scores_tiled(const uint16_t* __restrict__ x,
                                                               const float* __restrict__ wg, int T, int H, int E,
                                                               float* __restrict__ scores) {
 #pragma clang fp contract(off)
-  __shared__ __attribute__((aligned(16))) float part[4][kRtTok * kRtExp * kRtStride];
+  static_assert(TT * TE <= 64, "one lane per pair in the final sums");
+  __shared__ __attribute__((aligned(16))) float part[4][TT * TE * kRtStride];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 16 + (wave >> 1) * kRtTok;
-  const int e0 = blockIdx.y * 16 + (wave & 1) * kRtExp;
-  const uint16_t* xr[kRtTok];
-  const float* wr[kRtExp];
+  const int t0 = (2 * blockIdx.x + (wave >> 1)) * TT, e0 = (2 * blockIdx.y + (wave & 1)) * TE;
+  // rows past T or E repeat the last valid one (their sums are never stored);
+  // such a wavefront runs too, so every wavefront reaches the barrier
+  const uint16_t* xr[TT];
+  const float* wr[TE];
 #pragma unroll
-  for (int i = 0; i < kRtTok; i++) xr[i] = x + (size_t)min(t0 + i, T - 1) * H + 4 * lane;
+  for (int i = 0; i < TT; i++) xr[i] = x + (size_t)min(t0 + i, T - 1) * H + 4 * lane;
 #pragma unroll
-  for (int i = 0; i < kRtExp; i++) wr[i] = wg + (size_t)min(e0 + i, E - 1) * H + 4 * lane;
-  float acc[kRtTok][kRtExp];
+  for (int i = 0; i < TE; i++) wr[i] = wg + (size_t)min(e0 + i, E - 1) * H + 4 * lane;
+  float acc[TT][TE];
 #pragma unroll
-  for (int a = 0; a < kRtTok; a++)
+  for (int a = 0; a < TT; a++)
 #pragma unroll
-    for (int b = 0; b < kRtExp; b++) acc[a][b] = 0.0f;
-  uint2 xv[kRtTok];
-  float4 wv[kRtExp];
+    for (int b = 0; b < TE; b++) acc[a][b] = 0.0f;
+  uint2 xv[TT];
+  float4 wv[TE];
 #pragma unroll
-  for (int i = 0; i < kRtTok; i++) xv[i] = *reinterpret_cast<const uint2*>(xr[i]);
+  for (int i = 0; i < TT; i++) xv[i] = *reinterpret_cast<const uint2*>(xr[i]);
 #pragma unroll
-  for (int i = 0; i < kRtExp; i++) wv[i] = *reinterpret_cast<const float4*>(wr[i]);
+  for (int i = 0; i < TE; i++) wv[i] = *reinterpret_cast<const float4*>(wr[i]);
   const int M = H >> 8;
   for (int m = 0; m < M; m++) {
     const int mn = (m + 1 < M ? m + 1 : m) * 256;
-    uint2 xn[kRtTok];
-    float4 wn[kRtExp];
+    uint2 xn[TT];
+    float4 wn[TE];
 #pragma unroll
-    for (int i = 0; i < kRtTok; i++) xn[i] = *reinterpret_cast<const uint2*>(xr[i] + mn);
+    for (int i = 0; i < TT; i++) xn[i] = *reinterpret_cast<const uint2*>(xr[i] + mn);
 #pragma unroll
-    for (int i = 0; i < kRtExp; i++) wn[i] = *reinterpret_cast<const float4*>(wr[i] + mn);
+    for (int i = 0; i < TE; i++) wn[i] = *reinterpret_cast<const float4*>(wr[i] + mn);
 #pragma unroll
     for (int c = 0; c < 4; c++) {
 #pragma unroll
-      for (int a = 0; a < kRtTok; a++) {
+      for (int a = 0; a < TT; a++) {
         const uint32_t word = c < 2 ? xv[a].x : xv[a].y;
         const float xf = bf16_bits_to_f32((c & 1) ? word >> 16 : word & 0xffffu);
 #pragma unroll
-        for (int b = 0; b < kRtExp; b++) {
+        for (int b = 0; b < TE; b++) {
           const float wf = c == 0 ? wv[b].x : c == 1 ? wv[b].y : c == 2 ? wv[b].z : wv[b].w;
           acc[a][b] = __builtin_fmaf(xf, wf, acc[a][b]);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kRtTok; i++) xv[i] = xn[i];
+    for (int i = 0; i < TT; i++) xv[i] = xn[i];
 #pragma unroll
-    for (int i = 0; i < kRtExp; i++) wv[i] = wn[i];
+    for (int i = 0; i < TE; i++) wv[i] = wn[i];
   }
   float* pw = part[wave];
 #pragma unroll
-  for (int a = 0; a < kRtTok; a++)
+  for (int a = 0; a < TT; a++)
 #pragma unroll
-    for (int b = 0; b < kRtExp; b++) pw[(a * kRtExp + b) * kRtStride + lane] = acc[a][b];
+    for (int b = 0; b < TE; b++) pw[(a * TE + b) * kRtStride + lane] = acc[a][b];
   __syncthreads();
+  if (lane >= TT * TE) return;
   float p[64];
 #pragma unroll
   for (int i = 0; i < 16; i++) {
@@ -121,8 +128,15 @@ __global__ __launch_bounds__(256, 2) void k_router_scores_tiled(const uint16_t* 
   for (int s = 32; s >= 1; s >>= 1)
 #pragma unroll
     for (int j = 0; j < s; j++) p[j] = p[j] + p[j + s];
-  const int t = t0 + lane / kRtExp, e = e0 + lane % kRtExp;
+  const int t = t0 + lane / TE, e = e0 + lane % TE;
   if (t < T && e < E) scores[(size_t)t * E + e] = sigmoid_fixed(p[0]);
+}
+
+template <int TT, int TE>
+void launch_router_tiled(const uint16_t* x, const float* wg, int T, int H, int E, float* scores_ws,
+                         hipStream_t stream) {
+  const dim3 grid((unsigned)((T + 2 * TT - 1) / (2 * TT)), (unsigned)((E + 2 * TE - 1) / (2 * TE)));
+  hipLaunchKernelGGL((k_router_scores_tiled<TT, TE>), grid, dim3(256), 0, stream, x, wg, T, H, E, scores_ws);
 }
 
 // One wavefront per token.
@@ -136,8 +150,11 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, 
 }
 
 // Below this many tokens a wavefront per (expert, run of tokens) has more
-// workgroups to spread over the chip than 16 x 16 tiles.
+// workgroups to spread over the chip than token x expert blocks.
 constexpr int kRouterTiledMinTokens = 64;
+// Blocks of 8 x 8 pairs once they give more than this many wavefronts (two
+// per CU); below, blocks of 4 x 4 keep four times as many wavefronts busy.
+constexpr int64_t kRouterBigBlockWaves = 512;
 
 hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
                          float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream) {
@@ -147,10 +164,12 @@ hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, 
   const int64_t waves = (int64_t)E * ((T + tpw - 1) / tpw);
   const int blocks = (int)((waves + 3) / 4);
   clear_last_error();
-  if (T >= kRouterTiledMinTokens)
-    hipLaunchKernelGGL(k_router_scores_tiled, dim3((T + 15) / 16, (E + 15) / 16), dim3(256), 0, stream, x, wg, T, H,
-                       E, scores_ws);
-  else if (H <= 16 * 256)
+  if (T >= kRouterTiledMinTokens) {
+    if ((int64_t)((T + 7) / 8) * ((E + 7) / 8) > kRouterBigBlockWaves)
+      launch_router_tiled<8, 8>(x, wg, T, H, E, scores_ws, stream);
+    else
+      launch_router_tiled<4, 4>(x, wg, T, H, E, scores_ws, stream);
+  } else if (H <= 16 * 256)
     hipLaunchKernelGGL(k_router_scores<16>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores_ws);
   else
     hipLaunchKernelGGL(k_router_scores<32>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores_ws);
