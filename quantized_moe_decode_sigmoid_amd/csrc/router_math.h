@@ -91,59 +91,85 @@ __device__ __forceinline__ bool sel_before(float sa, int ea, float sb, int eb) {
   return sa > sb || (sa == sb && ea < eb);
 }
 
-// One wavefront selects the K experts of one token from its E sigmoid scores:
-// K rounds of a wave-wide arg-max under (selection score descending, expert
-// index ascending), selection score = s + bias.  Lane 0 writes the slots to
-// ids[0..K) and the weights scale * s_k / (((s_0 + s_1) + s_2) + ...) to w
-// (either may point to global or LDS memory).
+// The (selection score, expert) order as one unsigned 64-bit key: larger key
+// = earlier.  High word: the score's bits mapped so that unsigned order is
+// float order (a selection score is never -0: a sigmoid is +0 or positive, and
+// +0 plus a bias never rounds to -0); low word: ~expert, so that on equal
+// scores the smaller index wins.  0 is below every key (no candidate).
+__device__ __forceinline__ uint64_t sel_key(float s, int e) {
+  const uint32_t u = __float_as_uint(s);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+}
+
+// key of the partner lane selected by a DPP control (both words moved)
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_key(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Largest key of the wavefront, in every lane: within each quad (xor 1, xor
+// 2), then half-rows of 8 and rows of 16 (mirrors), then across rows (xor 16,
+// xor 32).  max is associative and commutative, so any pairing gives the
+// same result.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+  uint64_t o = dpp_key<kQuadXor1>(k);
+  k = o > k ? o : k;
+  o = dpp_key<kQuadXor2>(k);
+  k = o > k ? o : k;
+  o = dpp_key<kRowHalfMirror>(k);
+  k = o > k ? o : k;
+  o = dpp_key<kRowMirror>(k);
+  k = o > k ? o : k;
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, off, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), off, 64);
+    o = ((uint64_t)hi << 32) | lo;
+    k = o > k ? o : k;
+  }
+  return k;
+}
+
+// One wavefront selects the K experts of one token from its E sigmoid scores
+// (E <= 256): K rounds of a wave-wide maximum of the (selection score
+// descending, expert index ascending) key, selection score = s + bias.  Lane
+// 0 writes the slots to ids[0..K) and the weights
+// scale * s_k / (((s_0 + s_1) + s_2) + ...) to w (either may point to global
+// or LDS memory).
 __device__ __forceinline__ void topk_wave(const float* scores, const float* bias, int E, int K, float scale,
                                           int lane, int32_t* ids, float* wout) {
 #pragma clang fp contract(off)
-  float s[4], sel[4];
-  bool avail[4];
+  float s[4];
+  uint64_t key[4];
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const int e = lane + 64 * q;
-    avail[q] = e < E;
-    s[q] = avail[q] ? scores[e] : 0.0f;
-    sel[q] = avail[q] ? (bias ? s[q] + bias[e] : s[q]) : 0.0f;
+    const bool avail = e < E;
+    s[q] = avail ? scores[e] : 0.0f;
+    const float sel = bias && avail ? s[q] + bias[e] : s[q];
+    key[q] = avail ? sel_key(sel, e) : 0ull;
   }
   int chosen[8];
   float chosen_s[8];
   for (int k = 0; k < K; k++) {
-    bool have = false;
-    float bs = 0.0f;
-    int be = 0x7fffffff;
+    uint64_t m = key[0];
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      if (avail[q] && (!have || sel[q] > bs)) {
-        have = true;
-        bs = sel[q];
-        be = lane + 64 * q;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float os = __shfl_xor(bs, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      const bool ohave = oe != 0x7fffffff;
-      if (ohave && (!have || os > bs || (os == bs && oe < be))) {
-        have = true;
-        bs = os;
-        be = oe;
-      }
-    }
+    for (int q = 1; q < 4; q++) m = key[q] > m ? key[q] : m;
+    const uint64_t win = wave_max_key(m);
+    const int e = __builtin_amdgcn_readfirstlane((int)~(uint32_t)win);
+    // the owner lane retires the winner; its unbiased score to every lane
     float sw = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      if (lane + 64 * q == be) {
-        avail[q] = false;
-        sw = s[q];
-      }
+      if (key[q] == win) key[q] = 0ull;
+      if (q == (e >> 6)) sw = s[q];
     }
-    sw = __shfl(sw, be & 63, 64);
-    chosen[k] = be;
-    chosen_s[k] = sw;
+    chosen[k] = e;
+    chosen_s[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw), e & 63));
   }
   if (lane == 0) {
     float S = 0.0f;
