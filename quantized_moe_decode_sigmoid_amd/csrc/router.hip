@@ -53,12 +53,91 @@ __global__ __launch_bounds__(256) void k_router_scores(const uint16_t* __restric
 // ends with).
 constexpr int kRtStride = 68;
 
+// The 64 lane partials of each of the wavefront's TT x TE pairs through the
+// wavefront's LDS area pw, then one lane per pair: the butterfly's tree, the
+// sigmoid, the store.  Every wavefront of the workgroup calls it (barrier).
+template <int TT, int TE>
+__device__ __forceinline__ void pair_sums(const float (&acc)[TT][TE], float* pw, int lane, int t0, int e0, int T,
+                                          int E, float* __restrict__ scores) {
+#pragma clang fp contract(off)
+  static_assert(TT * TE <= 64, "one lane per pair in the final sums");
+#pragma unroll
+  for (int a = 0; a < TT; a++)
+#pragma unroll
+    for (int b = 0; b < TE; b++) pw[(a * TE + b) * kRtStride + lane] = acc[a][b];
+  __syncthreads();
+  if (lane >= TT * TE) return;
+  float p[64];
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const float4 q = *reinterpret_cast<const float4*>(pw + lane * kRtStride + 4 * i);
+    p[4 * i] = q.x;
+    p[4 * i + 1] = q.y;
+    p[4 * i + 2] = q.z;
+    p[4 * i + 3] = q.w;
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1)
+#pragma unroll
+    for (int j = 0; j < s; j++) p[j] = p[j] + p[j + s];
+  const int t = t0 + lane / TE, e = e0 + lane % TE;
+  if (t < T && e < E) scores[(size_t)t * E + e] = sigmoid_fixed(p[0]);
+}
+
+// The same blocks of 2 x 2 pairs with every operand of the row requested at
+// once (H <= 256 MMAX), for calls whose blocks of 4 x 4 would leave the
+// wavefronts waiting for one 256-element step after another.
+template <int MMAX>
+__global__ __launch_bounds__(256) void k_router_scores_resident(const uint16_t* __restrict__ x,
+                                                               const float* __restrict__ wg, int T, int H, int E,
+                                                               float* __restrict__ scores) {
+#pragma clang fp contract(off)
+  constexpr int TT = 2, TE = 2;
+  __shared__ __attribute__((aligned(16))) float part[4][TT * TE * kRtStride];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = (2 * blockIdx.x + (wave >> 1)) * TT, e0 = (2 * blockIdx.y + (wave & 1)) * TE;
+  const int M = H >> 8;
+  uint2 xv[MMAX][TT];
+  float4 wv[MMAX][TE];
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    const int mm = 256 * min(m, M - 1) + 4 * lane;  // steps past H repeat the last one (never used)
+#pragma unroll
+    for (int i = 0; i < TT; i++) xv[m][i] = *reinterpret_cast<const uint2*>(x + (size_t)min(t0 + i, T - 1) * H + mm);
+#pragma unroll
+    for (int i = 0; i < TE; i++) wv[m][i] = *reinterpret_cast<const float4*>(wg + (size_t)min(e0 + i, E - 1) * H + mm);
+  }
+  float acc[TT][TE];
+#pragma unroll
+  for (int a = 0; a < TT; a++)
+#pragma unroll
+    for (int b = 0; b < TE; b++) acc[a][b] = 0.0f;
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    if (m < M) {
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+#pragma unroll
+        for (int a = 0; a < TT; a++) {
+          const uint32_t word = c < 2 ? xv[m][a].x : xv[m][a].y;
+          const float xf = bf16_bits_to_f32((c & 1) ? word >> 16 : word & 0xffffu);
+#pragma unroll
+          for (int b = 0; b < TE; b++) {
+            const float wf = c == 0 ? wv[m][b].x : c == 1 ? wv[m][b].y : c == 2 ? wv[m][b].z : wv[m][b].w;
+            acc[a][b] = __builtin_fmaf(xf, wf, acc[a][b]);
+          }
+        }
+      }
+    }
+  }
+  pair_sums<TT, TE>(acc, part[wave], lane, t0, e0, T, E, scores);
+}
+
 template <int TT, int TE>
 __global__ __launch_bounds__(256, 2) void k_router_scores_tiled(const uint16_t* __restrict__ x,
                                                               const float* __restrict__ wg, int T, int H, int E,
                                                               float* __restrict__ scores) {
 #pragma clang fp contract(off)
-  static_assert(TT * TE <= 64, "one lane per pair in the final sums");
   __shared__ __attribute__((aligned(16))) float part[4][TT * TE * kRtStride];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = (2 * blockIdx.x + (wave >> 1)) * TT, e0 = (2 * blockIdx.y + (wave & 1)) * TE;
@@ -108,28 +187,7 @@ __global__ __launch_bounds__(256, 2) void k_router_scores_tiled(const uint16_t* 
 #pragma unroll
     for (int i = 0; i < TE; i++) wv[i] = wn[i];
   }
-  float* pw = part[wave];
-#pragma unroll
-  for (int a = 0; a < TT; a++)
-#pragma unroll
-    for (int b = 0; b < TE; b++) pw[(a * TE + b) * kRtStride + lane] = acc[a][b];
-  __syncthreads();
-  if (lane >= TT * TE) return;
-  float p[64];
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const float4 q = *reinterpret_cast<const float4*>(pw + lane * kRtStride + 4 * i);
-    p[4 * i] = q.x;
-    p[4 * i + 1] = q.y;
-    p[4 * i + 2] = q.z;
-    p[4 * i + 3] = q.w;
-  }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1)
-#pragma unroll
-    for (int j = 0; j < s; j++) p[j] = p[j] + p[j + s];
-  const int t = t0 + lane / TE, e = e0 + lane % TE;
-  if (t < T && e < E) scores[(size_t)t * E + e] = sigmoid_fixed(p[0]);
+  pair_sums<TT, TE>(acc, part[wave], lane, t0, e0, T, E, scores);
 }
 
 template <int TT, int TE>
@@ -153,8 +211,11 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, 
 // workgroups to spread over the chip than token x expert blocks.
 constexpr int kRouterTiledMinTokens = 64;
 // Blocks of 8 x 8 pairs once they give more than this many wavefronts (two
-// per CU); below, blocks of 4 x 4 keep four times as many wavefronts busy.
+// per CU); below, blocks of 4 x 4 keep four times as many wavefronts busy,
+// and blocks of 2 x 2 with every operand requested at once up to this many
+// wavefronts (H <= 4096).
 constexpr int64_t kRouterBigBlockWaves = 512;
+constexpr int64_t kRouterResidentWaves = 2048;
 
 hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
                          float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream) {
@@ -165,10 +226,17 @@ hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, 
   const int blocks = (int)((waves + 3) / 4);
   clear_last_error();
   if (T >= kRouterTiledMinTokens) {
-    if ((int64_t)((T + 7) / 8) * ((E + 7) / 8) > kRouterBigBlockWaves)
+    if ((int64_t)((T + 7) / 8) * ((E + 7) / 8) > kRouterBigBlockWaves) {
       launch_router_tiled<8, 8>(x, wg, T, H, E, scores_ws, stream);
-    else
+    } else if (H <= 16 * 256 && (int64_t)((T + 1) / 2) * ((E + 1) / 2) <= kRouterResidentWaves) {
+      const dim3 grid((unsigned)((T + 3) / 4), (unsigned)((E + 3) / 4));
+      if (H <= 8 * 256)
+        hipLaunchKernelGGL(k_router_scores_resident<8>, grid, dim3(256), 0, stream, x, wg, T, H, E, scores_ws);
+      else
+        hipLaunchKernelGGL(k_router_scores_resident<16>, grid, dim3(256), 0, stream, x, wg, T, H, E, scores_ws);
+    } else {
       launch_router_tiled<4, 4>(x, wg, T, H, E, scores_ws, stream);
+    }
   } else if (H <= 16 * 256)
     hipLaunchKernelGGL(k_router_scores<16>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores_ws);
   else
