@@ -72,8 +72,10 @@ def run_route(dl, x_bits, bias_dev=None):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 1), ("tiny", 100), ("xing4", 64), ("batch", 128),
-                                     ("prefill", 300), ("prefill", 2048)])
+                                     ("xing4", 300), ("prefill", 300), ("prefill", 2048)])
 def test_route_bit_exact(name, T):
+    """Every router kernel: one row per wavefront (T < 64), 2 x 2 blocks with resident operands (tiny T=100,
+    Xing4 T=64, batch T=128), 4 x 4 blocks (Xing4 T=300), 8 x 8 blocks (prefill T=300, 2048)."""
     s, inp, dl = device_layer(name)
     x = synth.tokens(s, T, first=1000)
     log(f"route {name} T={T}")
@@ -92,6 +94,22 @@ def test_route_with_selection_bias_bit_exact():
     rid, rw, _, _ = oracle.route(x, inp["gate_w"], s.top_k, s.routed_scale, bias)
     assert np.array_equal(ids, rid)
     assert np.array_equal(w.view(np.uint32), rw.view(np.uint32))
+
+
+def test_route_large_hidden_bit_exact():
+    """H = 8192 (above the resident-operand router's limit) at T = 70: 4 x 4 blocks streaming 32 steps."""
+    s = EXTRA_SHAPES["h8192_f2048"]
+    g = synth.gate_weights(s)
+    x = synth.tokens(s, 70, first=5)
+    log("route h8192 T=70")
+    cfg = cfg_of(s)
+    ids = torch.empty((70, s.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((70, s.top_k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, 70), dtype=torch.uint8, device="cuda")
+    qm.moe_route(cfg, 70, to_dev_bf16(x), torch.from_numpy(g).cuda(), None, ids, w, ws)
+    rid, rw, _, _ = oracle.route(x, g, s.top_k, s.routed_scale)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), rw.view(np.uint32))
 
 
 # ---------------------------------------------------------------- bucketing (bit-exact)
