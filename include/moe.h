@@ -196,6 +196,16 @@ moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev
                              float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
                              size_t ws_bytes, hipStream_t stream);
 
+/* ---- measurement ----------------------------------------------------------
+ * Not part of the layer: a kernel of known traffic for reporting achieved
+ * bandwidth against this GPU's own streaming rate as well as the vendor peak.
+ *
+ * Read bytes of src_dev exactly once (16-byte vector loads, a grid-stride walk
+ * over the whole GPU) and write nothing except, with negligible probability,
+ * one word to sink_dev (so the reads cannot be optimised away).  bytes must be
+ * a multiple of 16; src_dev and sink_dev 16-byte aligned. */
+moe_status moe_stream_read(const void* src_dev, size_t bytes, uint32_t* sink_dev, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -63,6 +63,7 @@ _SIGS = {
     "moe_bucket": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_expert_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_layer_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_stream_read": ([_vp, _sz, _vp, _vp], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -123,6 +124,11 @@ def moe_workspace_init(cfg, T, ws, ws_bytes=None, stream=None):
 
 def moe_pack_experts(cfg, n_experts, src, dst, stream=None):
     _check(_lib.moe_pack_experts(ctypes.byref(cfg), n_experts, _p(src), _p(dst), _stream(stream)), "moe_pack_experts")
+
+
+def moe_stream_read(src, nbytes, sink, stream=None):
+    """Measurement kernel: read nbytes of src once (no writes); sink is a 16-byte aligned device word."""
+    _check(_lib.moe_stream_read(_p(src), nbytes, _p(sink), _stream(stream)), "moe_stream_read")
 
 
 def moe_dequant(cfg, packed_expert, matrix, precision, out, stream=None):

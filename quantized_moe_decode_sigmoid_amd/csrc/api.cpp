@@ -223,6 +223,13 @@ MOE_API moe_status moe_dequant(const moe_config* cfg, const void* packed_expert_
                                        cols, precision == MOE_PREC_BF16 ? 1 : 0, out_dev, stream));
 }
 
+MOE_API moe_status moe_stream_read(const void* src_dev, size_t bytes, uint32_t* sink_dev, hipStream_t stream) {
+  if (bytes % 16 != 0) return MOE_EINVAL;
+  TRY(need(src_dev));
+  TRY(need(sink_dev));
+  return launched(qmoe::launch_stream_read(src_dev, (int64_t)bytes, sink_dev, stream));
+}
+
 MOE_API moe_status moe_route(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
                              const float* sel_bias_dev, int32_t* topk_ids_dev, float* topk_w_dev, void* ws_dev,
                              size_t ws_bytes, hipStream_t stream) {

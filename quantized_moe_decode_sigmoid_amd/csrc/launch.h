@@ -65,4 +65,8 @@ hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream);
 
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 
+// ---- measurement (stream.hip)
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace qmoe

@@ -142,3 +142,17 @@ def test_bucket_pack_dequant_argument_errors():
 def test_zero_sized_calls_enqueue_nothing():
     cfg = qm.make_config(**XING4)
     qm.moe_pack_experts(cfg, 0, A, A + (1 << 24), stream=0)  # no work, no launch
+
+
+def test_stream_read_argument_errors():
+    def call(src=A, n=1 << 20, sink=A):
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_stream_read(src, n, sink, stream=0)
+        return ei.value.status
+
+    assert call(n=(1 << 20) + 8) == qm.MOE_EINVAL
+    assert call(src=None) == qm.MOE_EINVAL
+    assert call(sink=None) == qm.MOE_EINVAL
+    assert call(src=A + 4) == qm.MOE_EALIGN
+    assert call(sink=A + 4) == qm.MOE_EALIGN
+    qm.moe_stream_read(A, 0, A, stream=0)  # zero bytes: validated, nothing enqueued

@@ -507,3 +507,17 @@ def test_stack_layers_chained_with_zipf_bias():
         assert_close(out.cpu().numpy(), ref, f"stack layer {layer}")
         h = x.float() + out
         x = torch.nn.functional.rms_norm(h, (s.hidden,), eps=1e-6).to(torch.bfloat16)
+
+
+def test_stream_read_reads_and_writes_nothing():
+    """The measurement kernel: a zero buffer XORs to zero, so the sink keeps its value; a ragged size
+    (not a multiple of the grid's stride) ends without touching memory past the buffer (the buffer sits
+    inside a larger allocation whose tail is never read: its words would flip the XOR only if read)."""
+    n = (1 << 24) + 16 * 12345
+    buf = torch.zeros(n // 4 + 4096, dtype=torch.int32, device="cuda")
+    buf[n // 4:] = 0x9E3779B9 - (1 << 32)  # the pattern the kernel stores on; never read when in bounds
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    log("stream_read ragged")
+    qm.moe_stream_read(buf, n, sink)
+    torch.cuda.synchronize()
+    assert sink.cpu().tolist() == [7, 7, 7, 7]
