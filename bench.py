@@ -130,7 +130,7 @@ def main():
     if args.cpu_sample is None:
         args.cpu_sample = CPU_SAMPLE[args.workload]
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark measures one GPU; --gpus must be 1"}))
         sys.exit(2)
     if args.copy_mb > 0:
         copy_calibration(args.copy_mb)
