@@ -13,8 +13,8 @@
 //      over the experts gives the expert offsets and the first chunk of each
 //      expert;
 //   3. each wavefront walks its own segment 64 routes at a time, in order:
-//      lanes holding the same expert find each other with 8 ballots (one per
-//      bit of the expert id) and rank themselves by lane; the wavefront's
+//      lanes holding the same expert find each other with one ballot per bit
+//      of the expert id and rank themselves by lane; the wavefront's
 //      running count per expert carries across steps.  Position = expert
 //      offset + earlier segments + running count + lane rank, which is
 //      exactly the stable order (ascending route id in an expert).
@@ -45,18 +45,22 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 }
 
 // One step of the scatter: 64 routes in route order (lane = order).  Lanes
-// holding the same expert find each other with 8 ballots (one per bit of the
-// expert id) and rank themselves by lane; position = expert offset + routes
-// of that expert before this step (run, the wavefront's running count) +
-// lane rank.
-__device__ __forceinline__ void scatter_step(bool valid, int key, int r, uint64_t below, int32_t* run,
+// holding the same expert find each other with one ballot per bit of the
+// expert id (key_bits of them) and rank themselves by lane; position = expert
+// offset + routes of that expert before this step (run, the wavefront's
+// running count) + lane rank.  The mask of valid lanes starts the match, so
+// the per-bit ballots need no validity term.
+__device__ __forceinline__ void scatter_step(bool valid, int key, int r, uint64_t below, int key_bits, int32_t* run,
                                              const int32_t* s_off, int32_t* __restrict__ perm,
                                              int32_t* __restrict__ pos) {
-  uint64_t peers = __ballot(valid);
+  uint64_t peers = __builtin_amdgcn_ballot_w64(valid);
 #pragma unroll
   for (int bit = 0; bit < 8; bit++) {
-    const uint64_t b = __ballot(valid && ((key >> bit) & 1));
-    peers &= ((key >> bit) & 1) ? b : ~b;
+    if (bit < key_bits) {  // uniform
+      const bool set = (key >> bit) & 1;
+      const uint64_t b = __builtin_amdgcn_ballot_w64(set);
+      peers &= set ? b : ~b;
+    }
   }
   const int rank = __popcll(peers & below);
   const int before = run[key];
@@ -192,6 +196,8 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   // kKeysPerLane routes per pass with all their ids requested at once
   int32_t* run = s_seg[wave];
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int key_bits = 0;  // bits of the largest expert id
+  while ((1 << key_bits) < E) key_bits++;
   for (int pass = 0; r0 + 64 * kKeysPerLane * pass < r1; pass++) {
     int key_p[kKeysPerLane];
 #pragma unroll
@@ -203,7 +209,7 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
     for (int j = 0; j < kKeysPerLane; j++) {
       const int base = r0 + 64 * (kKeysPerLane * pass + j);
       if (base >= r1) break;
-      scatter_step(base + lane < r1, key_p[j], base + lane, below, run, s_off, perm, pos);
+      scatter_step(base + lane < r1, key_p[j], base + lane, below, key_bits, run, s_off, perm, pos);
     }
   }
 }
