@@ -104,24 +104,29 @@ __device__ __forceinline__ bf16x8 dequant_bf16(const BfLds& sh, uint32_t word, _
 }
 
 // The packed tile of 16 columns that a lane reads: its nibble word and the
-// fp16 scales of its column (lane % 16) for the tile's 4 blocks.
+// fp16 scales of its column (lane % 16) for the tile's 4 blocks, two per
+// register (each loaded into its half).
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 struct LaneTile {
   u32x4 nib;
-  uint32_t sc[4];
+  f16x2 sc[2];  // blocks 0, 1 | 2, 3
 };
 
 __device__ __forceinline__ LaneTile load_lane_tile(const uint8_t* tile, int lane) {
   LaneTile t;
   t.nib = ld16(tile + 16 * lane);
   const int n = lane & 15;
-  const uint16_t* sp = reinterpret_cast<const uint16_t*>(tile + kTileNibbleBytes + 32 * (n >> 2) + 2 * (n & 3));
+  const _Float16* sp = reinterpret_cast<const _Float16*>(tile + kTileNibbleBytes + 32 * (n >> 2) + 2 * (n & 3));
 #pragma unroll
-  for (int b = 0; b < 4; b++) t.sc[b] = sp[4 * b];
+  for (int h = 0; h < 2; h++) {
+    t.sc[h].x = sp[8 * h];
+    t.sc[h].y = sp[8 * h + 4];
+  }
   return t;
 }
 
 __device__ __forceinline__ _Float16 lane_scale(const LaneTile& t, int b) {
-  return __builtin_bit_cast(_Float16, (uint16_t)(t.sc[b] & 0xffffu));
+  return (b & 1) ? t.sc[b >> 1].y : t.sc[b >> 1].x;
 }
 
 // Activation rows of one step, global memory straight into LDS
