@@ -140,7 +140,7 @@ constexpr int kExThreads = 64 * kExWaves;
 // of 3 tiles; the 4th tile's are requested when the first tile is done.
 constexpr int kGuPass = 4;
 constexpr int kGuXSlots = 3;
-constexpr int kDnRowTiles = 4;  // down: 16-row tiles of H per workgroup (8 spill at 128 VGPRs)
+constexpr int kDnRowTiles = 8;  // down: 16-row tiles of H per workgroup
 
 struct GateUpExactLds {
   uint32_t scales[kExWaves][256];  // per wavefront: [matrix][tile of the pass][32 words]; LDS DMA target
@@ -310,13 +310,18 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
 
   u32x4 nib[kDnRowTiles];
   bf16x8 bh[4], bl[4];
+  // the row tiles' nibble words through one buffer resource: row tile t at
+  // scalar offset t * rt_bytes, so one lane offset serves all of them
+  const __amdgpu_buffer_rsrc_t rows_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rows), (short)0, 0x7fffffff, 0x00020000);
   auto issue = [&](int kg) {
     dma16(rows + min(lane >> 3, kDnRowTiles - 1) * rt_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes +
               16 * (lane & 7),
           my_scales);
-
+    const int voff = kg * kTileBytes + 16 * lane;
 #pragma unroll
-    for (int t = 0; t < kDnRowTiles; t++) nib[t] = ld16(rows + t * rt_bytes + (int64_t)kg * kTileBytes + 16 * lane);
+    for (int t = 0; t < kDnRowTiles; t++)
+      nib[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc, voff, (int)(t * rt_bytes), 0));
 #pragma unroll
     for (int b = 0; b < 4; b++) {
       bh[b] = *reinterpret_cast<const bf16x8*>(hh + 32 * (4 * kg + b) + 8 * G);
@@ -347,18 +352,23 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
         scale_acc_words(acc[t], cr, sd[0], sd[1]);
       }
   }
-  // wavefront-order sums, four row tiles at a time; wavefront t stores row tile t
+  // wavefront-order sums, half of the row tiles at a time; wavefront t stores
+  // row tile t.  The lane's column, row group and output row are recomputed
+  // (mbcnt) instead of kept live through the loop, which needs every register.
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int c_e = lane_e & 15, G_e = lane_e >> 4;
+  const int64_t hrow_e = (ch.expert >= 0 ? 0 : (int64_t)TK) + ch.first + c_e;
 #pragma unroll
   for (int half = 0; half < 2; half++) {
 #pragma unroll
-    for (int t = 0; t < kDnRowTiles / 2; t++) sh.red[wave][t][lane] = acc[(kDnRowTiles / 2) * half + t];
+    for (int t = 0; t < kDnRowTiles / 2; t++) sh.red[wave][t][lane_e] = acc[(kDnRowTiles / 2) * half + t];
     __syncthreads();
-    if (wave < kDnRowTiles / 2 && live) {
-      f32x4 s = sh.red[0][wave][lane];
+    if (wave < kDnRowTiles / 2 && c_e < ch.count) {
+      f32x4 s = sh.red[0][wave][lane_e];
 #pragma unroll
-      for (int w = 1; w < kExWaves; w++) s += sh.red[w][wave][lane];
+      for (int w = 1; w < kExWaves; w++) s += sh.red[w][wave][lane_e];
       const int rt = slab * kDnRowTiles + (kDnRowTiles / 2) * half + wave;
-      *reinterpret_cast<f32x4*>(y + hrow * H + 16 * rt + 4 * G) = s;
+      *reinterpret_cast<f32x4*>(y + hrow_e * H + 16 * rt + 4 * G_e) = s;
     }
     __syncthreads();
   }
