@@ -206,6 +206,15 @@ moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev
  * a multiple of 16; src_dev and sink_dev 16-byte aligned. */
 moe_status moe_stream_read(const void* src_dev, size_t bytes, uint32_t* sink_dev, hipStream_t stream);
 
+/* Not part of the layer either: the chaining between consecutive layers of a
+ * stack, y = bf16(rmsnorm(x + out)) with no weight, one fused kernel.
+ *   out_dev fp32 [T][H] (a layer's output), x_dev bf16 [T][H] (its input),
+ *   y_dev   bf16 [T][H] (the next layer's input; may alias x_dev)
+ * Per row: h = fp32(x) + out, r = 1 / sqrt(mean(h^2) + eps) in fp32, y =
+ * bf16(h * r) rounded to nearest even.  H % 256 == 0 as for the layer. */
+moe_status moe_residual_rmsnorm(const float* out_dev, const void* x_dev, int32_t T, int32_t H, float eps,
+                                void* y_dev, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

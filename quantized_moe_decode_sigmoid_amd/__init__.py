@@ -64,6 +64,7 @@ _SIGS = {
     "moe_expert_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_layer_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_stream_read": ([_vp, _sz, _vp, _vp], _i32),
+    "moe_residual_rmsnorm": ([_vp, _vp, _i32, _i32, ctypes.c_float, _vp, _vp], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -129,6 +130,12 @@ def moe_pack_experts(cfg, n_experts, src, dst, stream=None):
 def moe_stream_read(src, nbytes, sink, stream=None):
     """Measurement kernel: read nbytes of src once (no writes); sink is a 16-byte aligned device word."""
     _check(_lib.moe_stream_read(_p(src), nbytes, _p(sink), _stream(stream)), "moe_stream_read")
+
+
+def moe_residual_rmsnorm(out, x, y, eps=1e-6, stream=None):
+    """Chaining between stacked layers: y = bf16(rmsnorm(x + out)), one fused kernel (not part of the layer)."""
+    T, H = out.shape
+    _check(_lib.moe_residual_rmsnorm(_p(out), _p(x), T, H, eps, _p(y), _stream(stream)), "moe_residual_rmsnorm")
 
 
 def moe_dequant(cfg, packed_expert, matrix, precision, out, stream=None):

@@ -230,6 +230,18 @@ MOE_API moe_status moe_stream_read(const void* src_dev, size_t bytes, uint32_t* 
   return launched(qmoe::launch_stream_read(src_dev, (int64_t)bytes, sink_dev, stream));
 }
 
+MOE_API moe_status moe_residual_rmsnorm(const float* out_dev, const void* x_dev, int32_t T, int32_t H, float eps,
+                                        void* y_dev, hipStream_t stream) {
+  if (T < 0 || T > kMaxTokens || H <= 0 || H % 256 != 0 || H > kMaxHidden) return MOE_EUNSUPPORTED;
+  if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  TRY(need(out_dev));
+  TRY(need(x_dev));
+  TRY(need(y_dev));
+  return launched(qmoe::launch_residual_rmsnorm(out_dev, static_cast<const uint16_t*>(x_dev), T, H, eps,
+                                                static_cast<uint16_t*>(y_dev), stream));
+}
+
 MOE_API moe_status moe_route(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
                              const float* sel_bias_dev, int32_t* topk_ids_dev, float* topk_w_dev, void* ws_dev,
                              size_t ws_bytes, hipStream_t stream) {

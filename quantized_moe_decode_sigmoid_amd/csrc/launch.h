@@ -65,8 +65,11 @@ hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream);
 
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 
-// ---- measurement (stream.hip)
+// ---- measurement (stream.hip) and the stack workload's chaining (chain.hip)
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
+hipError_t launch_residual_rmsnorm(const float* out, const uint16_t* x, int T, int H, float eps, uint16_t* y,
+                                   hipStream_t stream);
 
 }  // namespace qmoe

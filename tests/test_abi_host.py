@@ -156,3 +156,14 @@ def test_stream_read_argument_errors():
     assert call(src=A + 4) == qm.MOE_EALIGN
     assert call(sink=A + 4) == qm.MOE_EALIGN
     qm.moe_stream_read(A, 0, A, stream=0)  # zero bytes: validated, nothing enqueued
+
+
+def test_residual_rmsnorm_argument_errors():
+    assert qm._lib.moe_residual_rmsnorm(A, A, 1, 3584 + 64, 1e-6, A, 0) == qm.MOE_EUNSUPPORTED
+    assert qm._lib.moe_residual_rmsnorm(A, A, -1, 3584, 1e-6, A, 0) == qm.MOE_EUNSUPPORTED
+    assert qm._lib.moe_residual_rmsnorm(A, A, 1, 3584, float("nan"), A, 0) == qm.MOE_EINVAL
+    assert qm._lib.moe_residual_rmsnorm(A, A, 1, 3584, -1.0, A, 0) == qm.MOE_EINVAL
+    assert qm._lib.moe_residual_rmsnorm(None, A, 1, 3584, 1e-6, A, 0) == qm.MOE_EINVAL
+    assert qm._lib.moe_residual_rmsnorm(A, A + 2, 1, 3584, 1e-6, A, 0) == qm.MOE_EALIGN
+    assert qm._lib.moe_residual_rmsnorm(A, A, 1, 3584, 1e-6, A + 8, 0) == qm.MOE_EALIGN
+    assert qm._lib.moe_residual_rmsnorm(A, A, 0, 3584, 1e-6, None, 0) == qm.MOE_OK  # T = 0: nothing to do

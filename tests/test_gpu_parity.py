@@ -521,3 +521,20 @@ def test_stream_read_reads_and_writes_nothing():
     qm.moe_stream_read(buf, n, sink)
     torch.cuda.synchronize()
     assert sink.cpu().tolist() == [7, 7, 7, 7]
+
+
+@pytest.mark.parametrize("T,alias", [(1, False), (5, True)])
+def test_residual_rmsnorm_matches_torch(T, alias):
+    """The stack's chaining kernel against torch's widening + add + rms_norm + bf16 rounding: equal up to one
+    bf16 ulp (the fp32 sum of squares is formed in another order), in place (y = x) or not."""
+    H = 3584
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16).cuda()
+    out = torch.randn(T, H, generator=g).cuda()
+    want = torch.nn.functional.rms_norm(x.float() + out, (H,), eps=1e-6).to(torch.bfloat16)
+    y = x if alias else torch.empty_like(x)
+    log(f"residual_rmsnorm T={T} alias={alias}")
+    qm.moe_residual_rmsnorm(out, x, y)
+    a = y.view(torch.int16).cpu().numpy().astype(np.int32)
+    b = want.view(torch.int16).cpu().numpy().astype(np.int32)
+    assert np.max(np.abs(a - b)) <= 1
