@@ -135,18 +135,20 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat
 // LDS, so results are deterministic.
 constexpr int kExWaves = 8;
 constexpr int kExThreads = 64 * kExWaves;
-// gate/up: a wavefront requests the nibble words and scales of 4 tiles per
-// matrix at once (one pass covers H <= 4096) and holds the activation operands
-// of 3 tiles; the 4th tile's are requested when the first tile is done.
-constexpr int kGuPass = 4;
-constexpr int kGuXSlots = 3;
+// gate/up: a workgroup covers 2 row tiles of F (32 rows), so that each
+// activation operand a wavefront loads serves 4 tiles (2 row tiles x gate/up);
+// a wavefront requests its tiles 2 columns at a time (kGuPass), nibble words,
+// scales and activations together.
+constexpr int kGuRowTiles = 2;
+constexpr int kGuPass = 2;
 constexpr int kDnRowTiles = 8;  // down: 16-row tiles of H per workgroup
 
 struct GateUpExactLds {
-  uint32_t scales[kExWaves][256];  // per wavefront: [matrix][tile of the pass][32 words]; LDS DMA target
+  uint32_t scales[kExWaves][256];  // per wavefront: [row tile][matrix][tile of the pass][32 words]; LDS DMA target
   uint32_t tbl[kPairTableWords];
-  f32x4 red[2][kExWaves][64];
+  f32x4 red[kGuRowTiles][2][kExWaves][64];
 };
+static_assert(kGuRowTiles * 2 * kGuPass * 8 == 64, "one LDS DMA load (64 pieces) covers the scales of a pass");
 
 struct DownExactLds {
   uint32_t scales[kExWaves][256];  // per wavefront: [row tile][32 words] of its current tile column
@@ -162,8 +164,8 @@ __device__ __forceinline__ void scale_acc_words(f32x4& acc, const f32x4& c, uint
   acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), c[3], acc[3]);
 }
 
-// Workgroup = (chunk, 16-row tile of F).  Output: the product h = silu(g)*u of
-// route column c, row f, as two bf16 halves h_hi = bf16(h), h_lo = bf16(h -
+// Workgroup = (chunk, 2 row tiles of F).  Output: the product h = silu(g)*u
+// of route column c, row f, as two bf16 halves h_hi = bf16(h), h_lo = bf16(h -
 // h_hi), row-major [route][F].
 __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gate_up_exact(
     const uint16_t* __restrict__ x, int H, int F, int K, int T, const uint8_t* __restrict__ arena,
@@ -171,9 +173,9 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const Chunk* __restrict__ chunks, const int32_t* __restrict__ n_chunks, uint16_t* __restrict__ h_hi,
     uint16_t* __restrict__ h_lo) {
   __shared__ __attribute__((aligned(16))) GateUpExactLds sh;
-  const int n_rt = F >> 4;
-  const int chunk_id = blockIdx.x / n_rt;
-  const int rt = blockIdx.x % n_rt;
+  const int n_rp = F / (16 * kGuRowTiles);
+  const int chunk_id = blockIdx.x / n_rp;
+  const int rt0 = kGuRowTiles * (blockIdx.x % n_rp);
   if (chunk_id >= *n_chunks) return;
   const Chunk ch = chunks[chunk_id];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -186,86 +188,92 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const uint16_t* xr = x + (size_t)tok * H;
   const int nkg = H >> 7;
   const int kg0 = wave * nkg / kExWaves, kg1 = (wave + 1) * nkg / kExWaves;
-  const uint8_t* gate_t = ex + (int64_t)rt * nkg * kTileBytes;  // up: mat_bytes further
+  const int64_t rt_bytes = (int64_t)nkg * kTileBytes;
+  const uint8_t* gate_t = ex + rt0 * rt_bytes;  // row tile r: + r * rt_bytes; up: mat_bytes further
   uint32_t* my_scales = sh.scales[wave];
 
-  u32x4 ng[kGuPass], nu[kGuPass];
-  bf16x8 xb[kGuXSlots][4];
-  // the weight loads of the pass starting at tile p0: scales (piece = lane:
-  // matrix lane / 32, tile (lane / 8) % 4, 16 bytes lane % 8 of its 128) and
-  // nibble words; tiles past the range repeat a valid one (never used)
-  auto issue_weights = [&](int p0) {
+  u32x4 nib[kGuRowTiles][2][kGuPass];
+  bf16x8 xb[kGuPass][4];
+  // the loads of the pass starting at tile p0: scales (piece = lane: row tile
+  // lane / 32, matrix (lane / 16) % 2, tile (lane / 8) % 2, 16 bytes lane % 8
+  // of its 128), nibble words and activations; tiles past the range repeat a
+  // valid one (never used)
+  auto issue = [&](int p0) {
     {
-      const int m = lane >> 5, i = (lane >> 3) & 3, j = lane & 7;
+      const int r = lane >> 5, m = (lane >> 4) & 1, i = (lane >> 3) & 1, j = lane & 7;
       const int kg = min(p0 + i, nkg - 1);
-      dma16(gate_t + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * j, my_scales);
+      dma16(gate_t + r * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * j, my_scales);
     }
 #pragma unroll
     for (int i = 0; i < kGuPass; i++) {
       const int kg = min(p0 + i, nkg - 1);
-      ng[i] = ld16(gate_t + (int64_t)kg * kTileBytes + 16 * lane);
-      nu[i] = ld16(gate_t + mat_bytes + (int64_t)kg * kTileBytes + 16 * lane);
-    }
-  };
-  auto issue_x = [&](int slot, int kg) {
 #pragma unroll
-    for (int b = 0; b < 4; b++) xb[slot][b] = load_x_operand(xr, 4 * min(kg, nkg - 1) + b, G);
+      for (int r = 0; r < kGuRowTiles; r++)
+#pragma unroll
+        for (int m = 0; m < 2; m++)
+          nib[r][m][i] = ld16(gate_t + r * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + 16 * lane);
+    }
+#pragma unroll
+    for (int i = 0; i < kGuPass; i++) {
+      const int kg = min(p0 + i, nkg - 1);
+#pragma unroll
+      for (int b = 0; b < 4; b++) xb[i][b] = load_x_operand(xr, 4 * kg + b, G);
+    }
   };
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4 accg = zero, accu = zero;
-  // tile i of the pass with the activations in slot
-  auto tile = [&](int i, int slot) {
+  f32x4 acc[kGuRowTiles][2];
 #pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const f32x4 cg = mfma16x16x32(decode_word(sh.tbl, ng[i][b], lane & 31), xb[slot][b], zero);
-      const f32x4 cu = mfma16x16x32(decode_word(sh.tbl, nu[i][b], lane & 31), xb[slot][b], zero);
-      const uint32_t* sg = my_scales + 32 * i + 8 * G + 2 * b;
-      const uint32_t* su = my_scales + 32 * (kGuPass + i) + 8 * G + 2 * b;
-      scale_acc_words(accg, cg, sg[0], sg[1]);
-      scale_acc_words(accu, cu, su[0], su[1]);
-    }
-  };
+  for (int r = 0; r < kGuRowTiles; r++) acc[r][0] = acc[r][1] = zero;
   // The scales are read only after a full wait: the compiler may move a
   // read-only register load past an explicit wait, so counting the loads
   // issued after the DMA would not be reliable.
   for (int p0 = kg0; p0 < kg1 || p0 == kg0; p0 += kGuPass) {
-    issue_weights(p0);
-#pragma unroll
-    for (int i = 0; i < kGuXSlots; i++) issue_x(i, p0 + i);
+    issue(p0);
     if (p0 == kg0) {  // every wavefront, also one with no tiles: the table and the barrier
       build_pair_table(sh.tbl);
       wait_loads();
       __syncthreads();
-    } else {  // only when H > 1024 kGuPass: this wavefront's own scales, no barrier needed
+    } else {  // this wavefront's own scales, no barrier needed
       wait_loads();
     }
     const int np = min(kGuPass, kg1 - p0);
-    if (np <= 0) break;
-    tile(0, 0);
-    issue_x(0, p0 + 3);  // the 4th tile's activations, into the slot just used
-    if (np > 1) tile(1, 1);
-    if (np > 2) tile(2, 2);
-    if (np > 3) tile(3, 0);
+#pragma unroll
+    for (int i = 0; i < kGuPass; i++) {
+      if (i >= np) break;
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+#pragma unroll
+        for (int r = 0; r < kGuRowTiles; r++)
+#pragma unroll
+          for (int m = 0; m < 2; m++) {
+            const f32x4 cr = mfma16x16x32(decode_word(sh.tbl, nib[r][m][i][b], lane & 31), xb[i][b], zero);
+            const uint32_t* sp = my_scales + 32 * ((r * 2 + m) * kGuPass + i) + 8 * G + 2 * b;
+            scale_acc_words(acc[r][m], cr, sp[0], sp[1]);
+          }
+    }
   }
-  sh.red[0][wave][lane] = accg;
-  sh.red[1][wave][lane] = accu;
+#pragma unroll
+  for (int r = 0; r < kGuRowTiles; r++) {
+    sh.red[r][0][wave][lane] = acc[r][0];
+    sh.red[r][1][wave][lane] = acc[r][1];
+  }
   __syncthreads();
-  // the lane's column and row group, recomputed (mbcnt) instead of kept live
-  // through the loop, which needs every register
+  // wavefront r finishes row tile r; the lane's column and row group are
+  // recomputed (mbcnt) instead of kept live through the loop
   const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int c_e = lane_e & 15, G_e = lane_e >> 4;
-  if (wave != 0 || c_e >= ch.count) return;
-  f32x4 g = sh.red[0][0][lane_e], u = sh.red[1][0][lane_e];
+  if (wave >= kGuRowTiles || c_e >= ch.count) return;
+  f32x4 g = sh.red[wave][0][0][lane_e], u = sh.red[wave][1][0][lane_e];
 #pragma unroll
   for (int w = 1; w < kExWaves; w++) {
-    g += sh.red[0][w][lane_e];
-    u += sh.red[1][w][lane_e];
+    g += sh.red[wave][0][w][lane_e];
+    u += sh.red[wave][1][w][lane_e];
   }
   // bucketed position of the route, or T*K + token for the shared expert
   const int64_t hrow = (ch.expert >= 0 ? 0 : (int64_t)T * K) + ch.first + c_e;
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const int f = 16 * rt + 4 * G_e + i;
+    const int f = 16 * (rt0 + wave) + 4 * G_e + i;
     const float gv = g[i];
     const float h = gv / (1.0f + expf(-gv)) * u[i];
     const uint32_t hb = f32_to_bf16_rne(h);
@@ -439,8 +447,8 @@ hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n
                             uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   clear_last_error();
-  hipLaunchKernelGGL(k_gate_up_exact, dim3((unsigned)(max_chunks * (F / 16))), dim3(kExThreads), 0, stream, x, H, F,
-                     K, T, arena, shared, expert_bytes, perm, chunks, n_chunks, h_hi, h_lo);
+  hipLaunchKernelGGL(k_gate_up_exact, dim3((unsigned)(max_chunks * (F / (16 * kGuRowTiles)))), dim3(kExThreads), 0,
+                     stream, x, H, F, K, T, arena, shared, expert_bytes, perm, chunks, n_chunks, h_hi, h_lo);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   clear_last_error();
