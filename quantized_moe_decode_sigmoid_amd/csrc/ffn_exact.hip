@@ -20,7 +20,7 @@
 // Memory: a packed tile (16 rows x 4 blocks, 1152 bytes) is read by one
 // wavefront with one 16-byte load per lane for the nibbles (into registers)
 // and one LDS DMA piece per lane covering the scales of 8 tiles, fully
-// coalesced.  A gate/up workgroup owns one (chunk, 16-row tile of F), a down
+// coalesced.  A gate/up workgroup owns one (chunk, 32 rows of F), a down
 // workgroup one (chunk, 128 rows of H); both split the reduction dimension
 // over 8 wavefronts.
 #include "device.h"
