@@ -119,8 +119,8 @@ __device__ __forceinline__ LaneTile load_lane_tile(const uint8_t* tile, int lane
   const _Float16* sp = reinterpret_cast<const _Float16*>(tile + kTileNibbleBytes + 32 * (n >> 2) + 2 * (n & 3));
 #pragma unroll
   for (int h = 0; h < 2; h++) {
-    t.sc[h].x = sp[8 * h];
-    t.sc[h].y = sp[8 * h + 4];
+    t.sc[h].x = __builtin_nontemporal_load(sp + 8 * h);
+    t.sc[h].y = __builtin_nontemporal_load(sp + 8 * h + 4);
   }
   return t;
 }

@@ -202,7 +202,8 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
     {
       const int r = lane >> 5, m = (lane >> 4) & 1, i = (lane >> 3) & 1, j = lane & 7;
       const int kg = min(p0 + i, nkg - 1);
-      dma16(gate_t + r * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * j, my_scales);
+      dma16_stream(gate_t + r * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * j,
+                   my_scales);
     }
 #pragma unroll
     for (int i = 0; i < kGuPass; i++) {
@@ -323,13 +324,13 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const __amdgpu_buffer_rsrc_t rows_rsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(rows), (short)0, 0x7fffffff, 0x00020000);
   auto issue = [&](int kg) {
-    dma16(rows + min(lane >> 3, kDnRowTiles - 1) * rt_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes +
-              16 * (lane & 7),
-          my_scales);
+    dma16_stream(rows + min(lane >> 3, kDnRowTiles - 1) * rt_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes +
+                     16 * (lane & 7),
+                 my_scales);
     const int voff = kg * kTileBytes + 16 * lane;
 #pragma unroll
     for (int t = 0; t < kDnRowTiles; t++)
-      nib[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc, voff, (int)(t * rt_bytes), 0));
+      nib[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc, voff, (int)(t * rt_bytes), kNonTemporal));
 #pragma unroll
     for (int b = 0; b < 4; b++) {
       bh[b] = *reinterpret_cast<const bf16x8*>(hh + 32 * (4 * kg + b) + 8 * G);

@@ -202,8 +202,8 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
   for (int j = wave; j < 8 * NRT + 8; j += kDecWaves) {
     if (j < 8 * NRT) {
       const int t = j >> 3, p = 64 * (j & 7) + lane, m = p >> 8, kg = min((p >> 3) & 31, nkg - 1);
-      dma16(rowtiles + t * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
-            &g.scales[t][0][0][0] + 256 * (j & 7));
+      dma16_stream(rowtiles + t * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
+                   &g.scales[t][0][0][0] + 256 * (j & 7));
     } else {
       const int p = 64 * (j - 8 * NRT) + lane;
       dma16(a.x + 8 * min(p, (a.H >> 3) - 1), &g.x[512 * (j - 8 * NRT)]);
@@ -298,8 +298,8 @@ __device__ __forceinline__ void load_routed_slots(const DecodeArgs& a, const Rou
 __device__ __forceinline__ void dma_slot_scales(DownLds& d, const uint8_t* down_rows, int nkg, int slot, int half) {
   const int p = 64 * half + (threadIdx.x & 63);
   const int rtl = p >> 6, kg = min((p >> 3) & 7, nkg - 1);
-  dma16(down_rows + ((int64_t)rtl * nkg + kg) * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
-        &d.scales[slot][0][0][0] + 256 * half);
+  dma16_stream(down_rows + ((int64_t)rtl * nkg + kg) * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
+               &d.scales[slot][0][0][0] + 256 * half);
 }
 
 // MFMAs of slot S over this wave's tile.  Column 0 of the B operand carries
