@@ -23,6 +23,8 @@
 // coalesced.  A gate/up workgroup owns one (chunk, 32 rows of F), a down
 // workgroup one (chunk, 128 rows of H); both split the reduction dimension
 // over 8 wavefronts.
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -128,27 +130,31 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat
 // Both FFN kernels run 8 wavefronts per workgroup and split the reduction
 // dimension over them: wavefront w takes packed tiles [w n/8, (w+1) n/8) of
 // the n tiles of a row (n = H/128 for gate/up, F/128 for down), so each
-// activation (or h) element is read once per workgroup.  A wavefront first
-// requests everything its tiles need -- the nibble words and the B operands
-// into registers, the tiles' scales into its own 1 KB of LDS by LDS DMA --
-// and only then computes; partial sums are added in wavefront order through
-// LDS, so results are deterministic.
+// activation (or h) element is read once per workgroup.  A wavefront requests
+// everything a tile column needs -- the nibble words and the B operands into
+// registers, the tiles' scales into its own LDS by LDS DMA -- before it
+// computes on it; partial sums are added in wavefront order through LDS, so
+// results are deterministic.
 constexpr int kExWaves = 8;
 constexpr int kExThreads = 64 * kExWaves;
 // gate/up: a workgroup covers 2 row tiles of F (32 rows), so that each
-// activation operand a wavefront loads serves 4 tiles (2 row tiles x gate/up);
-// a wavefront requests its tiles 2 columns at a time (kGuPass), nibble words,
-// scales and activations together.
+// activation operand a wavefront loads serves 4 tiles (2 row tiles x gate/up).
+// A wavefront walks its tile columns with two sets of registers: the loads of
+// column j + 1 are in flight while column j is computed.  The scales travel
+// through registers too and are written to the wavefront's LDS when their
+// column starts (an LDS DMA would make the compiler wait for every load in
+// flight before any LDS read).
 constexpr int kGuRowTiles = 2;
-constexpr int kGuPass = 2;
 constexpr int kDnRowTiles = 8;  // down: 16-row tiles of H per workgroup
 
 struct GateUpExactLds {
-  uint32_t scales[kExWaves][256];  // per wavefront: [row tile][matrix][tile of the pass][32 words]; LDS DMA target
+  union {
+    uint32_t scales[kExWaves][256];           // per wavefront: 32 words of (row tile r, matrix m) at 32 (2r + m)
+    f32x4 red[kGuRowTiles][2][kExWaves][64];  // wavefront partials, after the last column
+  } u;
   uint32_t tbl[kPairTableWords];
-  f32x4 red[kGuRowTiles][2][kExWaves][64];
 };
-static_assert(kGuRowTiles * 2 * kGuPass * 8 == 64, "one LDS DMA load (64 pieces) covers the scales of a pass");
+static_assert(kGuRowTiles * 2 * 8 == 32, "32 lanes of 16 bytes cover the scales of a column");
 
 struct DownExactLds {
   uint32_t scales[kExWaves][256];  // per wavefront: [row tile][32 words] of its current tile column
@@ -164,6 +170,9 @@ __device__ __forceinline__ void scale_acc_words(f32x4& acc, const f32x4& c, uint
   acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), c[3], acc[3]);
 }
 
+template <int B>
+using BufferIndex = std::integral_constant<int, B>;
+
 // Workgroup = (chunk, 2 row tiles of F).  Output: the product h = silu(g)*u
 // of route column c, row f, as two bf16 halves h_hi = bf16(h), h_lo = bf16(h -
 // h_hi), row-major [route][F].
@@ -178,85 +187,94 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const int rt0 = kGuRowTiles * (blockIdx.x % n_rp);
   if (chunk_id >= *n_chunks) return;
   const Chunk ch = chunks[chunk_id];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, G = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar buffer offsets
+  const int G = lane >> 4;
   const int64_t mat_bytes = expert_bytes / 3;
   const uint8_t* ex = ch.expert >= 0 ? arena + (int64_t)ch.expert * expert_bytes : shared;
-  const bool live = c < ch.count;
-  const int cc = live ? c : 0;  // a column past the chunk reads column 0's token (never stored)
+  const int cc = (lane & 15) < ch.count ? (lane & 15) : 0;  // a column past the chunk reads column 0's token
   const int tok = ch.expert >= 0 ? perm[ch.first + cc] / K : ch.first + cc;
-  const uint16_t* xr = x + (size_t)tok * H;
   const int nkg = H >> 7;
-  const int kg0 = wave * nkg / kExWaves, kg1 = (wave + 1) * nkg / kExWaves;
-  const int64_t rt_bytes = (int64_t)nkg * kTileBytes;
+  const int kg0 = wave * nkg / kExWaves, n_cols = (wave + 1) * nkg / kExWaves - kg0;
+  const int rt_bytes = nkg * kTileBytes;
   const uint8_t* gate_t = ex + rt0 * rt_bytes;  // row tile r: + r * rt_bytes; up: mat_bytes further
-  uint32_t* my_scales = sh.scales[wave];
 
-  u32x4 nib[kGuRowTiles][2][kGuPass];
-  bf16x8 xb[kGuPass][4];
-  // the loads of the pass starting at tile p0: scales (piece = lane: row tile
-  // lane / 32, matrix (lane / 16) % 2, tile (lane / 8) % 2, 16 bytes lane % 8
-  // of its 128), nibble words and activations; tiles past the range repeat a
-  // valid one (never used)
-  auto issue = [&](int p0) {
-    {
-      const int r = lane >> 5, m = (lane >> 4) & 1, i = (lane >> 3) & 1, j = lane & 7;
-      const int kg = min(p0 + i, nkg - 1);
-      dma16_stream(gate_t + r * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * j,
-                   my_scales);
-    }
+  // The weight rows and the activations through buffer resources (byte
+  // offsets fit in 32 bits: an expert matrix is < 2 GB, T * H * 2 <= 1 GB).
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(gate_t), (short)0, 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), (short)0, 0x7fffffff, 0x00020000);
+  const int x_off = 2 * (tok * H + 8 * G);  // + 256 kg + 64 b: elements 32 (4 kg + b) + 8 G .. + 7
+
+  u32x4 nib[2][kGuRowTiles][2];
+  bf16x8 xb[2][4];
+  u32x4 scw[2];
+  // this lane's 16-byte scale piece: piece lane % 8 of row tile (lane / 16) %
+  // 2, matrix (lane / 8) % 2 (lanes 32-63 repeat lanes 0-31; their copy lands
+  // in the second half of the LDS buffer and is never read)
+  const int sc_off = ((lane >> 4) & 1) * rt_bytes + ((lane >> 3) & 1) * (int)mat_bytes + kTileNibbleBytes + 16 * (lane & 7);
+  // The loads of tile column kg into register set B.  A column past this
+  // wavefront's range (valid false) gets a byte offset past the buffer's
+  // range: such a load returns zeros and makes no memory request, so the
+  // loop below can issue unconditionally and keep no old values alive.
+  auto issue = [&](auto bc, int kg, bool valid) {
+    constexpr int B = decltype(bc)::value;
+    const int oob = valid ? 0 : INT32_MIN;  // 0x80000000 >= the range 0x7fffffff
+    const int voff = (kg * kTileBytes + 16 * lane) | oob;
+    scw[B] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, sc_off | oob, kg * kTileBytes, kNonTemporal));
 #pragma unroll
-    for (int i = 0; i < kGuPass; i++) {
-      const int kg = min(p0 + i, nkg - 1);
+    for (int r = 0; r < kGuRowTiles; r++)
 #pragma unroll
-      for (int r = 0; r < kGuRowTiles; r++)
+      for (int m = 0; m < 2; m++)
+        nib[B][r][m] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, voff, (int)(r * rt_bytes + m * mat_bytes), kNonTemporal));
+    const int xo = (x_off + 256 * kg) | oob;
 #pragma unroll
-        for (int m = 0; m < 2; m++)
-          nib[r][m][i] = ld16(gate_t + r * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + 16 * lane);
-    }
-#pragma unroll
-    for (int i = 0; i < kGuPass; i++) {
-      const int kg = min(p0 + i, nkg - 1);
-#pragma unroll
-      for (int b = 0; b < 4; b++) xb[i][b] = load_x_operand(xr, 4 * kg + b, G);
-    }
+    for (int b = 0; b < 4; b++)
+      xb[B][b] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xo + 64 * b, 0, 0));
   };
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[kGuRowTiles][2];
 #pragma unroll
   for (int r = 0; r < kGuRowTiles; r++) acc[r][0] = acc[r][1] = zero;
-  // The scales are read only after a full wait: the compiler may move a
-  // read-only register load past an explicit wait, so counting the loads
-  // issued after the DMA would not be reliable.
-  for (int p0 = kg0; p0 < kg1 || p0 == kg0; p0 += kGuPass) {
-    issue(p0);
-    if (p0 == kg0) {  // every wavefront, also one with no tiles: the table and the barrier
-      build_pair_table(sh.tbl);
-      wait_loads();
-      __syncthreads();
-    } else {  // this wavefront's own scales, no barrier needed
-      wait_loads();
-    }
-    const int np = min(kGuPass, kg1 - p0);
+  uint32_t* sc = sh.u.scales[wave];
+  // one column from register set B; a wavefront's LDS operations run in
+  // order, so the scale words are written after the previous column's reads
+  // and read after this write
+  auto compute = [&](auto bc) {
+    constexpr int B = decltype(bc)::value;
+    *reinterpret_cast<u32x4*>(sc + 4 * lane) = scw[B];
 #pragma unroll
-    for (int i = 0; i < kGuPass; i++) {
-      if (i >= np) break;
+    for (int b = 0; b < 4; b++)
 #pragma unroll
-      for (int b = 0; b < 4; b++)
+      for (int r = 0; r < kGuRowTiles; r++)
 #pragma unroll
-        for (int r = 0; r < kGuRowTiles; r++)
-#pragma unroll
-          for (int m = 0; m < 2; m++) {
-            const f32x4 cr = mfma16x16x32(decode_word(sh.tbl, nib[r][m][i][b], lane & 31), xb[i][b], zero);
-            const uint32_t* sp = my_scales + 32 * ((r * 2 + m) * kGuPass + i) + 8 * G + 2 * b;
-            scale_acc_words(acc[r][m], cr, sp[0], sp[1]);
-          }
-    }
+        for (int m = 0; m < 2; m++) {
+          const f32x4 cr = mfma16x16x32(decode_word(sh.tbl, nib[B][r][m][b], lane & 31), xb[B][b], zero);
+          const uint32_t* sp = sc + 32 * (r * 2 + m) + 8 * G + 2 * b;
+          scale_acc_words(acc[r][m], cr, sp[0], sp[1]);
+        }
+  };
+  const BufferIndex<0> b0;
+  const BufferIndex<1> b1;
+  issue(b0, kg0, n_cols > 0);
+  issue(b1, kg0 + 1, n_cols > 1);
+  build_pair_table(sh.tbl);
+  __syncthreads();
+  // columns j (set 0) and j + 1 (set 1) are in flight at the top of a pass;
+  // each set is refilled with the column two ahead once computed
+  for (int j = 0; j < n_cols; j += 2) {
+    compute(b0);
+    issue(b0, kg0 + j + 2, j + 2 < n_cols);
+    if (j + 1 < n_cols) compute(b1);
+    issue(b1, kg0 + j + 3, j + 3 < n_cols);
   }
+  __syncthreads();  // the scale buffers become the reduction buffer
 #pragma unroll
   for (int r = 0; r < kGuRowTiles; r++) {
-    sh.red[r][0][wave][lane] = acc[r][0];
-    sh.red[r][1][wave][lane] = acc[r][1];
+    sh.u.red[r][0][wave][lane] = acc[r][0];
+    sh.u.red[r][1][wave][lane] = acc[r][1];
   }
   __syncthreads();
   // wavefront r finishes row tile r; the lane's column and row group are
@@ -264,11 +282,11 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int c_e = lane_e & 15, G_e = lane_e >> 4;
   if (wave >= kGuRowTiles || c_e >= ch.count) return;
-  f32x4 g = sh.red[wave][0][0][lane_e], u = sh.red[wave][1][0][lane_e];
+  f32x4 g = sh.u.red[wave][0][0][lane_e], u = sh.u.red[wave][1][0][lane_e];
 #pragma unroll
   for (int w = 1; w < kExWaves; w++) {
-    g += sh.red[wave][0][w][lane_e];
-    u += sh.red[wave][1][w][lane_e];
+    g += sh.u.red[wave][0][w][lane_e];
+    u += sh.u.red[wave][1][w][lane_e];
   }
   // bucketed position of the route, or T*K + token for the shared expert
   const int64_t hrow = (ch.expert >= 0 ? 0 : (int64_t)T * K) + ch.first + c_e;
