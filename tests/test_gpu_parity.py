@@ -163,16 +163,20 @@ EXTRA_SHAPES = {
     "k1": synth.Shape("k1", 1, 256, 4, 1, 128, routed_scale=1.0, seed=23),
     "h4096": synth.Shape("h4096", 1, 4096, 8, 2, 256, seed=24),
     "h8192_f2048": synth.Shape("h8192_f2048", 1, 8192, 4, 2, 2048, seed=25),
+    # 2, 5 and 7 tile columns per gate/up wavefront of the exact-weight kernel (H / 128 / 8)
+    "h2048": synth.Shape("h2048", 1, 2048, 8, 2, 256, seed=26),
+    "h5120": synth.Shape("h5120", 1, 5120, 8, 2, 256, seed=27),
+    "h7168": synth.Shape("h7168", 1, 7168, 8, 2, 256, seed=28),
 }
 
 
-def extra_layer_parity(name, T, first=0):
+def extra_layer_parity(name, T, first=0, precision=qm.PREC_AUTO):
     s = EXTRA_SHAPES[name]
     key = (name, 0)
     if key not in _CACHE:
         _CACHE[key] = (s, synth.layer_inputs(s))
     inp = _CACHE[key][1]
-    dl = qm.DeviceLayer(cfg_of(s), inp["gate_w"], None, inp["arena"], inp["shared"])
+    dl = qm.DeviceLayer(cfg_of(s, precision), inp["gate_w"], None, inp["arena"], inp["shared"])
     x = synth.tokens(s, T, first=first)
     prec = qm.moe_resolved_precision(dl.cfg, T)
     log(f"layer {name} T={T} precision={prec}")
@@ -198,6 +202,14 @@ def test_layer_shape_corners(name, T):
     FP32 plan): the exact-weight kernels walk their tiles in more than one pass (8 gate/up tiles and
     2 down tiles per wavefront); T = 33 takes the BF16 plan."""
     extra_layer_parity(name, T, first=3 * T)
+
+
+@pytest.mark.parametrize("name", ["h2048", "h5120", "h7168"])
+def test_layer_fp32_column_counts(name):
+    """FP32 contract at hidden sizes whose gate/up wavefronts walk 2, 5 and 7 tile columns: the
+    double-buffered column loop with an odd last column and loads past the range (zeros)."""
+    extra_layer_parity(name, 19, first=5, precision=qm.PREC_FP32)
+    extra_layer_parity(name, 1, first=2, precision=qm.PREC_FP32)
 
 
 def test_layer_tiny():
