@@ -91,85 +91,74 @@ __device__ __forceinline__ bool sel_before(float sa, int ea, float sb, int eb) {
   return sa > sb || (sa == sb && ea < eb);
 }
 
-// The (selection score, expert) order as one unsigned 64-bit key: larger key
-// = earlier.  High word: the score's bits mapped so that unsigned order is
-// float order (a selection score is never -0: a sigmoid is +0 or positive, and
-// +0 plus a bias never rounds to -0); low word: ~expert, so that on equal
-// scores the smaller index wins.  0 is below every key (no candidate).
-__device__ __forceinline__ uint64_t sel_key(float s, int e) {
+// A selection score's bits mapped so that unsigned order is float order (a
+// selection score is never -0: a sigmoid is +0 or positive, and +0 plus a
+// bias never rounds to -0, and never NaN).  Every such key is >= 1, so 0 is
+// below every key (no candidate).
+__device__ __forceinline__ uint32_t sel_order_bits(float s) {
   const uint32_t u = __float_as_uint(s);
-  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)e;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// key of the partner lane selected by a DPP control (both words moved)
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_key(uint64_t k) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Largest key of the wavefront, in every lane: within each quad (xor 1, xor
-// 2), then half-rows of 8 and rows of 16 (mirrors), then across rows (xor 16,
-// xor 32).  max is associative and commutative, so any pairing gives the
-// same result.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+// Largest key of the wavefront, as a scalar: within each quad (xor 1, xor 2),
+// then half-rows of 8 and rows of 16 (mirrors), so that every lane holds its
+// row's maximum; then the four row maxima read from lanes 0, 16, 32, 48.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
   constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
-  uint64_t o = dpp_key<kQuadXor1>(k);
-  k = o > k ? o : k;
-  o = dpp_key<kQuadXor2>(k);
-  k = o > k ? o : k;
-  o = dpp_key<kRowHalfMirror>(k);
-  k = o > k ? o : k;
-  o = dpp_key<kRowMirror>(k);
-  k = o > k ? o : k;
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)k, off, 64);
-    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(k >> 32), off, 64);
-    o = ((uint64_t)hi << 32) | lo;
-    k = o > k ? o : k;
-  }
-  return k;
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kQuadXor1, 0xf, 0xf, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kQuadXor2, 0xf, 0xf, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kRowHalfMirror, 0xf, 0xf, false));
+  k = max(k, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)k, kRowMirror, 0xf, 0xf, false));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)k, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)k, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)k, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)k, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
 // One wavefront selects the K experts of one token from its E sigmoid scores
-// (E <= 256): K rounds of a wave-wide maximum of the (selection score
-// descending, expert index ascending) key, selection score = s + bias.  Lane
-// 0 writes the slots to ids[0..K) and the weights
+// (E <= 256; lane l holds experts l, l + 64, l + 128, l + 192): K rounds, each
+// taking the largest selection score (s + bias) left, as a wave-wide maximum
+// of its order-preserving bits, and among equal scores the smallest expert
+// index (first set bit of the first non-empty ballot, in expert order), then
+// retiring it.  Lane 0 writes the slots to ids[0..K) and the weights
 // scale * s_k / (((s_0 + s_1) + s_2) + ...) to w (either may point to global
 // or LDS memory).
 __device__ __forceinline__ void topk_wave(const float* scores, const float* bias, int E, int K, float scale,
                                           int lane, int32_t* ids, float* wout) {
 #pragma clang fp contract(off)
   float s[4];
-  uint64_t key[4];
+  uint32_t key[4];
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const int e = lane + 64 * q;
     const bool avail = e < E;
     s[q] = avail ? scores[e] : 0.0f;
     const float sel = bias && avail ? s[q] + bias[e] : s[q];
-    key[q] = avail ? sel_key(sel, e) : 0ull;
+    key[q] = avail ? sel_order_bits(sel) : 0u;
   }
   int chosen[8];
   float chosen_s[8];
   for (int k = 0; k < K; k++) {
-    uint64_t m = key[0];
+    const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+    int e = 256;
 #pragma unroll
-    for (int q = 1; q < 4; q++) m = key[q] > m ? key[q] : m;
-    const uint64_t win = wave_max_key(m);
-    const int e = __builtin_amdgcn_readfirstlane((int)~(uint32_t)win);
+    for (int q = 3; q >= 0; q--) {
+      const uint64_t b = __builtin_amdgcn_ballot_w64(key[q] == m);
+      if (b) e = 64 * q + (int)__builtin_ctzll(b);
+    }
     // the owner lane retires the winner; its unbiased score to every lane
+    const int qe = e >> 6, le = e & 63;
     float sw = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      if (key[q] == win) key[q] = 0ull;
-      if (q == (e >> 6)) sw = s[q];
+      if (q == qe) {
+        if (lane == le) key[q] = 0u;
+        sw = s[q];
+      }
     }
     chosen[k] = e;
-    chosen_s[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw), e & 63));
+    chosen_s[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw), le));
   }
   if (lane == 0) {
     float S = 0.0f;
