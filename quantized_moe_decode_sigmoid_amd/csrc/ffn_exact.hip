@@ -20,9 +20,9 @@
 // Memory: a packed tile (16 rows x 4 blocks, 1152 bytes) is read by one
 // wavefront with one 16-byte load per lane for the nibbles (into registers)
 // and one LDS DMA piece per lane covering the scales of 8 tiles, fully
-// coalesced.  A gate/up workgroup owns one (chunk, 32 rows of F), a down
-// workgroup one (chunk, 128 rows of H); both split the reduction dimension
-// over 8 wavefronts.
+// coalesced.  A gate/up workgroup owns one (chunk, 32 rows of F) and splits
+// the reduction dimension over 4 wavefronts, a down workgroup one (chunk, 128
+// rows of H) over 8.
 #include <type_traits>
 
 #include "device.h"
@@ -127,16 +127,21 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat
 
 // ---------------------------------------------------------------- gate / up
 
-// Both FFN kernels run 8 wavefronts per workgroup and split the reduction
-// dimension over them: wavefront w takes packed tiles [w n/8, (w+1) n/8) of
-// the n tiles of a row (n = H/128 for gate/up, F/128 for down), so each
-// activation (or h) element is read once per workgroup.  A wavefront requests
+// Both FFN kernels split the reduction dimension over the W wavefronts of a
+// workgroup (W = 4 for gate/up, 8 for down): wavefront w takes packed tiles
+// [w n/W, (w+1) n/W) of the n tiles of a row (n = H/128 for gate/up, F/128
+// for down), so each activation (or h) element is read once per workgroup.  A wavefront requests
 // everything a tile column needs -- the nibble words and the B operands into
 // registers, the tiles' scales into its own LDS by LDS DMA -- before it
 // computes on it; partial sums are added in wavefront order through LDS, so
 // results are deterministic.
-constexpr int kExWaves = 8;
+constexpr int kExWaves = 8;  // down
 constexpr int kExThreads = 64 * kExWaves;
+// gate/up: 4 wavefronts (Xing4: 7 tile columns each); with the
+// reduction buffer holding one matrix at a time a workgroup needs 40 KB of
+// LDS, so 4 workgroups (16 wavefronts, 118 VGPRs each) fit on a CU.
+constexpr int kGuWaves = 4;
+constexpr int kGuThreads = 64 * kGuWaves;
 // gate/up: a workgroup covers 2 row tiles of F (32 rows), so that each
 // activation operand a wavefront loads serves 4 tiles (2 row tiles x gate/up).
 // A wavefront walks its tile columns with two sets of registers: the loads of
@@ -149,8 +154,8 @@ constexpr int kDnRowTiles = 8;  // down: 16-row tiles of H per workgroup
 
 struct GateUpExactLds {
   union {
-    uint32_t scales[kExWaves][256];           // per wavefront: 32 words of (row tile r, matrix m) at 32 (2r + m)
-    f32x4 red[kGuRowTiles][2][kExWaves][64];  // wavefront partials, after the last column
+    uint32_t scales[kGuWaves][256];        // per wavefront: 32 words of (row tile r, matrix m) at 32 (2r + m)
+    f32x4 red[kGuRowTiles][kGuWaves][64];  // wavefront partials of one matrix, after the last column
   } u;
   uint32_t tbl[kPairTableWords];
 };
@@ -176,7 +181,7 @@ using BufferIndex = std::integral_constant<int, B>;
 // Workgroup = (chunk, 2 row tiles of F).  Output: the product h = silu(g)*u
 // of route column c, row f, as two bf16 halves h_hi = bf16(h), h_lo = bf16(h -
 // h_hi), row-major [route][F].
-__global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gate_up_exact(
+__global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gate_up_exact(
     const uint16_t* __restrict__ x, int H, int F, int K, int T, const uint8_t* __restrict__ arena,
     const uint8_t* __restrict__ shared, int64_t expert_bytes, const int32_t* __restrict__ perm,
     const Chunk* __restrict__ chunks, const int32_t* __restrict__ n_chunks, uint16_t* __restrict__ h_hi,
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const int cc = (lane & 15) < ch.count ? (lane & 15) : 0;  // a column past the chunk reads column 0's token
   const int tok = ch.expert >= 0 ? perm[ch.first + cc] / K : ch.first + cc;
   const int nkg = H >> 7;
-  const int kg0 = wave * nkg / kExWaves, n_cols = (wave + 1) * nkg / kExWaves - kg0;
+  const int kg0 = wave * nkg / kGuWaves, n_cols = (wave + 1) * nkg / kGuWaves - kg0;
   const int rt_bytes = nkg * kTileBytes;
   const uint8_t* gate_t = ex + rt0 * rt_bytes;  // row tile r: + r * rt_bytes; up: mat_bytes further
 
@@ -272,22 +277,27 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
   }
   __syncthreads();  // the scale buffers become the reduction buffer
 #pragma unroll
-  for (int r = 0; r < kGuRowTiles; r++) {
-    sh.u.red[r][0][wave][lane] = acc[r][0];
-    sh.u.red[r][1][wave][lane] = acc[r][1];
-  }
+  for (int r = 0; r < kGuRowTiles; r++) sh.u.red[r][wave][lane] = acc[r][0];
   __syncthreads();
-  // wavefront r finishes row tile r; the lane's column and row group are
-  // recomputed (mbcnt) instead of kept live through the loop
+  // wavefront r finishes row tile r (gate sums, then up sums through the same
+  // buffer); the lane's column and row group are recomputed (mbcnt) instead of
+  // kept live through the loop
   const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   const int c_e = lane_e & 15, G_e = lane_e >> 4;
-  if (wave >= kGuRowTiles || c_e >= ch.count) return;
-  f32x4 g = sh.u.red[wave][0][0][lane_e], u = sh.u.red[wave][1][0][lane_e];
+  f32x4 g = zero;
+  if (wave < kGuRowTiles) {
+    g = sh.u.red[wave][0][lane_e];
 #pragma unroll
-  for (int w = 1; w < kExWaves; w++) {
-    g += sh.u.red[wave][0][w][lane_e];
-    u += sh.u.red[wave][1][w][lane_e];
+    for (int w = 1; w < kGuWaves; w++) g += sh.u.red[wave][w][lane_e];
   }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kGuRowTiles; r++) sh.u.red[r][wave][lane] = acc[r][1];
+  __syncthreads();
+  if (wave >= kGuRowTiles || c_e >= ch.count) return;
+  f32x4 u = sh.u.red[wave][0][lane_e];
+#pragma unroll
+  for (int w = 1; w < kGuWaves; w++) u += sh.u.red[wave][w][lane_e];
   // bucketed position of the route, or T*K + token for the shared expert
   const int64_t hrow = (ch.expert >= 0 ? 0 : (int64_t)T * K) + ch.first + c_e;
 #pragma unroll
@@ -466,7 +476,7 @@ hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n
                             uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   clear_last_error();
-  hipLaunchKernelGGL(k_gate_up_exact, dim3((unsigned)(max_chunks * (F / (16 * kGuRowTiles)))), dim3(kExThreads), 0,
+  hipLaunchKernelGGL(k_gate_up_exact, dim3((unsigned)(max_chunks * (F / (16 * kGuRowTiles)))), dim3(kGuThreads), 0,
                      stream, x, H, F, K, T, arena, shared, expert_bytes, perm, chunks, n_chunks, h_hi, h_lo);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
