@@ -105,7 +105,9 @@ __device__ __forceinline__ bf16x8 dequant_bf16(const BfLds& sh, uint32_t word, _
 
 // The packed tile of 16 columns that a lane reads: its nibble word and the
 // fp16 scales of its column (lane % 16) for the tile's 4 blocks, two per
-// register (each loaded into its half).
+// register (each loaded into its half).  Ordinary (temporal) loads: every
+// tile of 128 routes of an expert reads the expert's weights, and a popular
+// expert (or the shared one) has many tiles, which then hit in L2.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 struct LaneTile {
   u32x4 nib;
@@ -114,13 +116,13 @@ struct LaneTile {
 
 __device__ __forceinline__ LaneTile load_lane_tile(const uint8_t* tile, int lane) {
   LaneTile t;
-  t.nib = ld16(tile + 16 * lane);
+  t.nib = *reinterpret_cast<const u32x4*>(tile + 16 * lane);
   const int n = lane & 15;
   const _Float16* sp = reinterpret_cast<const _Float16*>(tile + kTileNibbleBytes + 32 * (n >> 2) + 2 * (n & 3));
 #pragma unroll
   for (int h = 0; h < 2; h++) {
-    t.sc[h].x = __builtin_nontemporal_load(sp + 8 * h);
-    t.sc[h].y = __builtin_nontemporal_load(sp + 8 * h + 4);
+    t.sc[h].x = *(sp + 8 * h);
+    t.sc[h].y = *(sp + 8 * h + 4);
   }
   return t;
 }
