@@ -3,15 +3,18 @@
 // section 4: the routes are sorted by expert so that every output element has
 // exactly one writer and the top-k can be summed in slot order afterwards).
 //
-// One workgroup of 1024 threads (16 wavefronts).  Integer work only, so the
-// result is bit-exact whatever the scheduling.  The routes are cut into 16
-// contiguous segments, one per wavefront, in route order:
-//   1. each wavefront counts its segment per expert (LDS atomics; a count does
-//      not depend on order);
-//   2. per expert, a scan over the 16 segment counts gives each wavefront the
-//      number of earlier routes of that expert in earlier segments; a scan
-//      over the experts gives the expert offsets and the first chunk of each
-//      expert;
+// Workgroups of 1024 threads (16 wavefronts), each scattering one block of
+// consecutive routes (launch_bucket sizes the blocks: one block for small
+// calls).  Integer work only, so the result is bit-exact whatever
+// the scheduling.  A block is cut into 16 contiguous segments, one per
+// wavefront, in route order:
+//   1. each wavefront counts its segment per expert, and the workgroup counts
+//      the routes before and after its block per expert (LDS atomics; a count
+//      does not depend on order) -- every workgroup reads all the ids;
+//   2. per expert, a scan over the 16 segment counts, starting at the routes
+//      before the block, gives each wavefront the number of earlier routes of
+//      that expert; a scan over the experts gives the expert offsets and the
+//      first chunk of each expert;
 //   3. each wavefront walks its own segment 64 routes at a time, in order:
 //      lanes holding the same expert find each other with one ballot per bit
 //      of the expert id and rank themselves by lane; the wavefront's
@@ -75,7 +78,8 @@ __device__ __forceinline__ void scatter_step(bool valid, int key, int r, uint64_
 }
 
 __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __restrict__ ids, int T, int K, int E,
-                                                           int n_shared, int chunk_shift, int32_t* __restrict__ counts,
+                                                           int n_shared, int chunk_shift, int block_routes,
+                                                           int32_t* __restrict__ counts,
                                                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
                                                            int32_t* __restrict__ pos, Chunk* __restrict__ chunks,
                                                            int32_t* __restrict__ n_chunks) {
@@ -85,14 +89,18 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   __shared__ int32_t s_chunk_first[257];
   __shared__ int32_t s_part[3][4];
   __shared__ int32_t s_key[256];  // remainder chunk sort key, or INT32_MAX
+  __shared__ int32_t s_before[256], s_after[256];  // routes of each expert before / after this block
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int R = T * K;
-  const int seg = (R + kBucketWaves - 1) / kBucketWaves;
-  const int r0 = min(R, wave * seg), r1 = min(R, r0 + seg);
+  const int b0 = min(R, (int)blockIdx.x * block_routes), b1 = min(R, b0 + block_routes);  // this block
+  const int seg = (b1 - b0 + kBucketWaves - 1) / kBucketWaves;
+  const int r0 = min(b1, b0 + wave * seg), r1 = min(b1, r0 + seg);
+  const bool lead = blockIdx.x == 0;  // writes the counts, offsets and chunk list (every block computes them)
 
   for (int i = tid; i < kBucketWaves * 256; i += kBucketThreads) (&s_seg[0][0])[i] = 0;
+  for (int i = tid; i < 256; i += kBucketThreads) s_before[i] = s_after[i] = 0;
   // the first 64 x kKeysPerLane routes of the segment stay in registers for the scatter
   int key0[kKeysPerLane];
 #pragma unroll
@@ -105,19 +113,23 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   for (int j = 0; j < kKeysPerLane; j++)
     if (r0 + 64 * j + lane < r1) atomicAdd(&s_seg[wave][key0[j]], 1);
   for (int r = r0 + 64 * kKeysPerLane + lane; r < r1; r += 64) atomicAdd(&s_seg[wave][ids[r]], 1);
+  for (int r = tid; r < b0; r += kBucketThreads) atomicAdd(&s_before[ids[r]], 1);
+  for (int r = b1 + tid; r < R; r += kBucketThreads) atomicAdd(&s_after[ids[r]], 1);
   __syncthreads();
 
-  // per expert: exclusive scan over the segments, total count, full chunks,
-  // remainder
+  // per expert: exclusive scan over the segments from the routes before the
+  // block, total count, full chunks, remainder
   const int rows = 1 << chunk_shift;
   int cnt = 0, nch = 0, rem = 0;
   if (tid < 256) {
+    cnt = s_before[tid];
 #pragma unroll
     for (int w = 0; w < kBucketWaves; w++) {
       const int c = s_seg[w][tid];
       s_seg[w][tid] = cnt;
       cnt += c;
     }
+    cnt += s_after[tid];
     if (tid >= E) cnt = 0;
     nch = cnt >> chunk_shift;
     rem = cnt & (rows - 1);
@@ -150,14 +162,14 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   }
   for (int w = 0; w < 4; w++) n_rem += s_part[2][w];
   __syncthreads();
-  for (int e = tid; e < E; e += kBucketThreads) {
+  for (int e = tid; lead && e < E; e += kBucketThreads) {
     counts[e] = s_cnt[e];
     offsets[e] = s_off[e];
   }
-  if (tid == 0) offsets[E] = R;
+  if (lead && tid == 0) offsets[E] = R;
 
   // chunk list (independent of the permutation itself); optional
-  const bool want_chunks = chunks != nullptr;
+  const bool want_chunks = lead && chunks != nullptr;
   const int shared_chunks = n_shared ? (T + rows - 1) >> chunk_shift : 0;
   const int full_chunks = s_chunk_first[256];
   for (int j = tid; want_chunks && j < shared_chunks; j += kBucketThreads) {
@@ -214,14 +226,24 @@ __global__ __launch_bounds__(kBucketThreads) void k_bucket(const int32_t* __rest
   }
 }
 
+// Blocks of at least kBucketMinBlock routes (one scatter step per wavefront),
+// at most kBucketMaxBlocks of them: every workgroup counts all the routes, so
+// more blocks only pay while the scatter outweighs that count.
+constexpr int kBucketMinBlock = 64 * kBucketWaves;
+constexpr int kBucketMaxBlocks = 64;
+
 hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int n_shared, int chunk_rows, int32_t* counts,
                          int32_t* offsets, int32_t* perm, int32_t* pos, Chunk* chunks, int32_t* n_chunks,
                          hipStream_t stream) {
   int shift = 0;
   while ((1 << shift) < chunk_rows) shift++;
+  const int R = T * K;
+  int block = (R + kBucketMaxBlocks - 1) / kBucketMaxBlocks;
+  block = block < kBucketMinBlock ? kBucketMinBlock : block;
+  const int n_blocks = R > 0 ? (R + block - 1) / block : 1;
   clear_last_error();
-  hipLaunchKernelGGL(k_bucket, dim3(1), dim3(kBucketThreads), 0, stream, ids, T, K, E, n_shared, shift, counts,
-                     offsets, perm, pos, chunks, n_chunks);
+  hipLaunchKernelGGL(k_bucket, dim3(n_blocks), dim3(kBucketThreads), 0, stream, ids, T, K, E, n_shared, shift, block,
+                     counts, offsets, perm, pos, chunks, n_chunks);
   return hipGetLastError();
 }
 
