@@ -18,11 +18,12 @@
 // activations are exact; only fp32 accumulation rounds.
 //
 // Memory: a packed tile (16 rows x 4 blocks, 1152 bytes) is read by one
-// wavefront with one 16-byte load per lane for the nibbles (into registers)
-// and one LDS DMA piece per lane covering the scales of 8 tiles, fully
-// coalesced.  A gate/up workgroup owns one (chunk, 32 rows of F) and splits
-// the reduction dimension over 4 wavefronts, a down workgroup one (chunk, 128
-// rows of H) over 8.
+// wavefront with one 16-byte load per lane for the nibbles (into registers);
+// the scales of a wavefront's tiles of one column come as one 16-byte piece
+// per lane (gate/up: into a register, then the wavefront's LDS; down: by LDS
+// DMA), fully coalesced.  A gate/up workgroup owns one (chunk, 32 rows of F)
+// and splits the reduction dimension over 4 wavefronts, a down workgroup one
+// (chunk, 128 rows of H) over 8.
 #include <type_traits>
 
 #include "device.h"
@@ -130,16 +131,16 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ mat
 // Both FFN kernels split the reduction dimension over the W wavefronts of a
 // workgroup (W = 4 for gate/up, 8 for down): wavefront w takes packed tiles
 // [w n/W, (w+1) n/W) of the n tiles of a row (n = H/128 for gate/up, F/128
-// for down), so each activation (or h) element is read once per workgroup.  A wavefront requests
-// everything a tile column needs -- the nibble words and the B operands into
-// registers, the tiles' scales into its own LDS by LDS DMA -- before it
-// computes on it; partial sums are added in wavefront order through LDS, so
-// results are deterministic.
+// for down), so each activation (or h) element is read once per workgroup.
+// A wavefront requests everything a tile column needs -- the nibble words and
+// the B operands into registers, the tiles' scales for its own LDS -- before
+// it computes on it; partial sums are added in wavefront order through LDS,
+// so results are deterministic.
 constexpr int kExWaves = 8;  // down
 constexpr int kExThreads = 64 * kExWaves;
-// gate/up: 4 wavefronts (Xing4: 7 tile columns each); with the
-// reduction buffer holding one matrix at a time a workgroup needs 40 KB of
-// LDS, so 4 workgroups (16 wavefronts, 118 VGPRs each) fit on a CU.
+// gate/up: 4 wavefronts (Xing4: 7 tile columns each); with the reduction
+// buffer holding one matrix at a time a workgroup needs 40 KB of LDS, so 4
+// workgroups (16 wavefronts, 118 VGPRs each) fit on a CU.
 constexpr int kGuWaves = 4;
 constexpr int kGuThreads = 64 * kGuWaves;
 // gate/up: a workgroup covers 2 row tiles of F (32 rows), so that each
