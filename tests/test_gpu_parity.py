@@ -114,7 +114,8 @@ def test_route_large_hidden_bit_exact():
 
 # ---------------------------------------------------------------- bucketing (bit-exact)
 
-@pytest.mark.parametrize("T,K,E", [(4, 2, 8), (1, 4, 64), (128, 4, 64), (2048, 8, 256), (1000, 3, 5), (0, 4, 64)])
+@pytest.mark.parametrize("T,K,E", [(4, 2, 8), (1, 4, 64), (128, 4, 64), (2048, 8, 256), (1000, 3, 5), (0, 4, 64),
+                                   (5000, 8, 256), (65536, 8, 256)])
 def test_bucket_bit_exact(T, K, E):
     rng = np.random.default_rng(T * 7 + K)
     ids = np.array([rng.choice(E, K, replace=False) for _ in range(T)], np.int32).reshape(T, K)
