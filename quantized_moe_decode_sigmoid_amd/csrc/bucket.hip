@@ -5,9 +5,10 @@
 //
 // Workgroups of 1024 threads (16 wavefronts), each scattering one block of
 // consecutive routes (launch_bucket sizes the blocks: one block for small
-// calls).  Integer work only, so the result is bit-exact whatever
-// the scheduling.  A block is cut into 16 contiguous segments, one per
-// wavefront, in route order:
+// calls); the first workgroup also writes the counts, offsets and chunk
+// list.  Integer work only, so the result is bit-exact whatever the
+// scheduling.  A block is cut into 16 contiguous segments, one per wavefront,
+// in route order:
 //   1. each wavefront counts its segment per expert, and the workgroup counts
 //      the routes before and after its block per expert (LDS atomics; a count
 //      does not depend on order) -- every workgroup reads all the ids;
@@ -19,8 +20,8 @@
 //      lanes holding the same expert find each other with one ballot per bit
 //      of the expert id and rank themselves by lane; the wavefront's
 //      running count per expert carries across steps.  Position = expert
-//      offset + earlier segments + running count + lane rank, which is
-//      exactly the stable order (ascending route id in an expert).
+//      offset + earlier blocks and segments + running count + lane rank,
+//      which is exactly the stable order (ascending route id in an expert).
 // No step after the scans needs a workgroup barrier.
 // The same pass writes the work list of the FFN kernels (chunk_rows is a
 // power of two), largest chunks first so that the long ones do not start
