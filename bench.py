@@ -1,18 +1,25 @@
 """Benchmark of the quantized MoE layer on one MI355X.
 
-Workload (the headline decode configuration): one Xing4.0-29B-A4B MoE layer --
-hidden 3584, 64 routed experts top-4 + 1 shared, expert_ffn 1024, sigmoid router,
-routed_scaling 2.0, IQ4_NL experts -- decoding 1000 independent tokens, T=1 per call.
-The layer is placed 32 times in HBM (12.9 GB) and token i uses placement i mod 32, so
-the 256 MB last-level cache cannot serve one token's expert reads from an earlier
-token's.  A step is the 1000-token sweep, captured once as a HIP graph and replayed.
+Default run (no flags): the four measured workloads in one process, one JSON line.
+  * decode (the headline, top-level `value`): one Xing4.0-29B-A4B MoE layer -- hidden 3584,
+    64 routed experts top-4 + 1 shared, expert_ffn 1024, sigmoid router, routed_scaling 2.0,
+    IQ4_NL experts -- decoding 1000 independent tokens, T=1 per call.  The layer is placed 32
+    times in HBM (12.9 GB) and token i uses placement i mod 32, so the 256 MB last-level cache
+    cannot serve one token's expert reads from an earlier token's.  A step is the 1000-token
+    sweep, captured once as a HIP graph and replayed.
+  * prefill (nested object): one T=2048 call of the prefill shape (hidden 2048, 256 experts
+    top-8 + 1 shared, ffn 512, Zipf(1.0) popularity), bf16 grouped MFMA; reports TFLOP/s and
+    the fraction of bf16 MFMA peak, and the HBM fraction.
+  * batch (nested): one T=128 call of the Xing4 layer per step.
+  * stack (nested): 38 Xing4 layers resident in HBM, T=1 per step through all of them, each
+    layer's input chained from the previous one; Zipf(1.1) popularity.
+Every leg times its steps with HIP events on the stream it launches on (median and spread
+over the steps), runs the CPU oracle on a bounded sample of its own inputs (the cpu_baseline),
+compares the GPU rows of those tokens with the oracle's (routing bit-exact, outputs within
+max-abs 2e-2 / rel-L2 1e-3) and, on the decode path, reads the status word.  Any miss makes
+the exit status non-zero after the line is printed.
 
-Printed JSON line: tok/s for the whole sweep; the roofline of one layer call (two
-launches per token: k_decode_scores, the router logits and sigmoids, then
-k_decode_experts, the selection, the five expert FFNs and the combine) from the HIP
-events around the timed region divided by the layer calls in it (HIP events around
-each eager call, with the stream kept busy so that host launch time does not enter,
-are reported beside it); the CPU oracle timed on a bounded sample of the same tokens.
+`--workload X` runs one leg alone and prints its line at top level (profiling runs).
 """
 import argparse
 import json
@@ -26,49 +33,50 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+METRIC = "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)"
+TOL_MAX_ABS, TOL_REL_L2 = 2e-2, 1e-3
 N_TOKENS = 1000
 PLACEMENTS = 32
+CPU_LABEL = "CPU oracle (reference semantics, double-precision sums), not an optimized CPU kernel"
 
 
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--workload", choices=["decode", "prefill", "stack", "batch"], default="decode",
-                   help="decode: the headline T=1 line (default); prefill: one T=2048 layer call per step; "
-                        "stack: 38 chained layers per step, T=1; batch: one T=128 Xing4 layer call per step")
+    p.add_argument("--workload", choices=["all", "decode", "prefill", "stack", "batch"], default="all",
+                   help="all (default): decode line with prefill, batch and stack nested; or one leg alone")
     p.add_argument("--stack-layers", type=int, default=38, help="layers of the stack workload")
     p.add_argument("--stack-tokens", type=int, default=20,
                    help="distinct tokens captured in the stack graph (steps per replay)")
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--distinct-layers", type=int, default=4,
-                   help="distinct seeded layers generated; placements reuse them at distinct addresses")
-    p.add_argument("--cpu-sample", type=int, default=None,
-                   help="tokens the CPU oracle runs (0: skip; default: about 10 s of oracle work, 60 decode tokens, "
-                        "400 prefill tokens, the whole 128-token batch)")
-    p.add_argument("--no-graph", action="store_true", help="replay eagerly instead of through a HIP graph")
+                   help="decode: distinct seeded layers generated; placements reuse them at distinct addresses")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs (and the output checks)")
+    p.add_argument("--no-graph", action="store_true", help="decode: replay eagerly instead of through a HIP graph")
     p.add_argument("--copy-mb", type=int, default=0,
                    help="first run one plain device copy of this many MiB (a kernel of known traffic, to scale "
                         "the HBM byte counters of a profiler run)")
     return p.parse_args()
 
 
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
-
+# ---------------------------------------------------------------- helpers
 
 def measured_traffic(record):
-    """HBM bytes per launch from the committed counter summary, or None when the counted kernel source
-    has changed since the counters were taken."""
+    """HBM bytes per launch from the committed counter summary, or None when a source of the counted
+    kernels (their .hip files and the headers they include) has changed since the counters were taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", record)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    sources = rec["kernel_sources"] if "kernel_sources" in rec else [rec["kernel_source"]]
-    hashes = rec["sha256"] if isinstance(rec["sha256"], list) else [rec["sha256"]]
-    for src, sha in zip(sources, hashes):
-        with open(os.path.join(ROOT, src), "rb") as f:
+    for src, sha in zip(rec["kernel_sources"], rec["sha256"]):
+        p = os.path.join(ROOT, src)
+        if not os.path.exists(p):
+            return None
+        with open(p, "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != sha:
                 return None
     return int(rec["bytes_per_call"])
@@ -95,13 +103,14 @@ def stream_gbs(torch):
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     dst = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     read_s, copy_s = [], []
+    stream = torch.cuda.current_stream()
     for _ in range(3):
         a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        a.record()
+        a.record(stream)
         qm.moe_stream_read(src, nbytes, sink)
-        b.record()
+        b.record(stream)
         dst.copy_(src[: 1 << 28])
-        c.record()
+        c.record(stream)
         torch.cuda.synchronize()
         read_s.append(a.elapsed_time(b) / 1e3)
         copy_s.append(b.elapsed_time(c) / 1e3)
@@ -123,377 +132,70 @@ def cpu_info():
     return {"cpu_model": model, "nproc": os.cpu_count()}
 
 
-CPU_SAMPLE = {"decode": 60, "prefill": 400, "batch": 128, "stack": 0}
+def spread(ms):
+    """Median and spread of per-step times (ms)."""
+    a = np.asarray(ms, np.float64)
+    return {"median_ms": round(float(np.median(a)), 4), "min_ms": round(float(a.min()), 4),
+            "max_ms": round(float(a.max()), 4), "n": int(a.size)}
 
 
-def main():
-    args = parse()
-    if args.cpu_sample is None:
-        args.cpu_sample = CPU_SAMPLE[args.workload]
-    if args.gpus != 1:
-        print(json.dumps({"error": "the benchmark measures one GPU; --gpus must be 1"}))
-        sys.exit(2)
-    if args.copy_mb > 0:
-        copy_calibration(args.copy_mb)
-    if args.workload == "prefill":
-        run_prefill(args)
-    elif args.workload == "stack":
-        run_stack(args)
-    elif args.workload == "batch":
-        run_batch(args)
-    else:
-        run_decode(args)
-
-
-def run_prefill(args):
-    """One prefill-sized layer call per step: T=2048, H=2048, 256 experts top-8 + 1 shared, ffn 512,
-    Zipf(1.0) expert popularity through the selection bias; bf16 grouped MFMA FFN."""
-    import torch
-
-    import quantized_moe_decode_sigmoid_amd as qm
-    import synth
-
-    shape = synth.WORKLOADS["prefill"]
-    T, H, E, K, F = shape.tokens, shape.hidden, shape.n_experts, shape.top_k, shape.ffn
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    t0 = time.time()
-    lam = synth.zipf_lambda(shape)
-    inp = synth.layer_inputs(shape, lam=lam)
-    x_bits = synth.tokens(shape, T)
-    gen_s = time.time() - t0
-    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
-    prec = qm.moe_resolved_precision(cfg, T)
-    dl = qm.DeviceLayer(cfg, inp["gate_w"], inp["bias"], inp["arena"], inp["shared"])
-    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
-    out = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
-    wts = torch.empty((T, K), dtype=torch.float32, device=dev)
-    ws = dl.workspace(T)
-
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        def step():
-            qm.moe_layer_forward(cfg, T, x, dl.gate_w, dl.bias, dl.arena, dl.shared, out, ids, wts, ws)
-
-        t_first = time.time()
-        step()
-        torch.cuda.synchronize()
-        first_ms = (time.time() - t_first) * 1e3
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(args.steps):
-            step()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        layer_ms = ev0.elapsed_time(ev1) / args.steps
-        # the expert FFN alone (bucketing, gate/up, down, combine) on the routing just computed
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        torch.cuda._sleep(50_000_000)
-        for i in range(args.steps):
-            starts[i].record(stream)
-            qm.moe_expert_forward(cfg, T, x, ids, wts, dl.arena, dl.shared, out, ws)
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-    ffn_us = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)])
-    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
-    flops = 2.0 * 3 * H * F * (T * K + T * shape.n_shared)
-    # MFMA rows the 16-row sub-tiles execute per useful row (tiles of 128 routes of one expert)
-    rows_useful = T * K + T * shape.n_shared
-    rows_run = sum(16 * ((c + 15) // 16) for c in counts.tolist()) + 16 * ((T + 15) // 16) * shape.n_shared
-    ffn_tflops = flops / (float(np.mean(ffn_us)) * 1e-6) / 1e12
-    # algorithmic bytes of one moe_expert_forward call: every expert once (routed + shared), x, the
-    # routing (ids + weights), the fp32 output
-    ebytes = 3 * F * (H // 32) * 18
-    ffn_bytes = (E + shape.n_shared) * ebytes + T * H * 2 + T * K * 8 + T * H * 4
-    ffn_gbs = ffn_bytes / (float(np.mean(ffn_us)) * 1e-6) / 1e9
-
-    cpu = None
-    if args.cpu_sample > 0:
-        import oracle
-        n = args.cpu_sample
-        c0 = time.time()
-        oracle.layer(x_bits[:n], inp["gate_w"], inp["arena"], inp["shared"], K, F, shape.routed_scale, inp["bias"],
-                     oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32)
-        cs = time.time() - c0
-        cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"the first {n} of the {T} tokens in one oracle.layer call, {cs:.1f} s", **cpu_info()}
-
-    res = {
-        "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
-        "value": round(flops / (layer_ms * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(layer_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if prec == qm.PREC_BF16 else "f32",
-        "data": "synthetic",
-        "config": {"workload": "prefill MoE layer, T=2048: hidden 2048, 256 experts top-8 + 1 shared, ffn 512, "
-                               "IQ4_NL experts, sigmoid router, scale 2.0, Zipf(1.0) expert popularity",
-                   "tokens_per_step": T, "zipf_lambda": lam},
-        # The FFN needs every expert's weights once (more bytes than the 256 MB last-level cache), so its
-        # HBM floor (bytes / 8 TB/s) is above its MFMA floor (flops / 2.5 PFLOP/s): it is HBM-bound.
-        "roofline": {"bound": "hbm" if ffn_bytes / HBM_PEAK_GBS > flops / 1e3 / MFMA_BF16_PEAK_TFLOPS else "mfma",
-                     "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill_traffic.json"),
-                     "kernel": "moe_expert_forward bf16: k_bucket + k_gate_up_bf16 + k_down_bf16 + k_combine "
-                               "(events around the call)",
-                     "bytes_per_launch": ffn_bytes, "flops_per_launch": flops,
-                     "mfma_tflops": round(ffn_tflops, 2), "mfma_frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "hbm_floor_us": round(ffn_bytes / HBM_PEAK_GBS / 1e3, 2),
-                     "mfma_floor_us": round(flops / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
-                     "avg_us": round(float(np.mean(ffn_us)), 3)},
-        "cpu_baseline": cpu,
-        "tok_s": round(T / (layer_ms * 1e-3), 1),
-        "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
-                              "median": float(np.median(counts))},
-        "mfma_rows_per_useful_row": round(rows_run / rows_useful, 4),
-        "first_step_ms": round(first_ms, 3),
-        "setup_s": round(gen_s, 1),
-    }
-    print(json.dumps(res), flush=True)
-
-
-def run_batch(args):
-    """One Xing4 layer call of T=128 tokens per step (zero selection bias), on the multi-kernel exact-weight
-    path; four placements of the layer cycled so that consecutive steps do not share cached weights."""
-    import torch
-
-    import quantized_moe_decode_sigmoid_amd as qm
-    import synth
-
-    shape = synth.WORKLOADS["batch"]
-    T, H, E, K, F = shape.tokens, shape.hidden, shape.n_experts, shape.top_k, shape.ffn
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    t0 = time.time()
-    inp = synth.layer_inputs(shape)
-    x_bits = synth.tokens(shape, T)
-    gen_s = time.time() - t0
-    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
-    prec = qm.moe_resolved_precision(cfg, T)
-    n_place = 4
-    dl = qm.DeviceLayer(cfg, inp["gate_w"], None, inp["arena"], inp["shared"])
-    places = [(dl.gate_w.clone(), dl.arena.clone(), dl.shared.clone()) for _ in range(n_place)]
-    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
-    out = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
-    wts = torch.empty((T, K), dtype=torch.float32, device=dev)
-    ws = dl.workspace(T)
-
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        def step(i):
-            g, a, sh = places[i % n_place]
-            qm.moe_layer_forward(cfg, T, x, g, None, a, sh, out, ids, wts, ws)
-
-        for i in range(max(args.warmup, n_place)):
-            step(i)
-        torch.cuda.synchronize()
-        n_steps = max(args.steps, n_place)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for i in range(n_steps):
-            step(i)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        layer_ms = ev0.elapsed_time(ev1) / n_steps
-        # events around each call, queued behind a spin kernel so that host launch time does not enter
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_steps)]
-        torch.cuda._sleep(50_000_000)
-        for i in range(n_steps):
-            starts[i].record(stream)
-            step(i)
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-    call_us = np.array([a.elapsed_time(b) * 1e3 for a, b in zip(starts, ends)])
-    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
-    touched = int((counts > 0).sum())
-    eb = qm.moe_expert_bytes(cfg)
-    # algorithmic bytes of one call: each expert the batch routes to once, the shared expert, the router
-    # weight, x, the fp32 output
-    call_bytes = (touched + shape.n_shared) * eb + E * H * 4 + T * H * 2 + T * H * 4
-    # one call's duration over the timed region (events bracketing the calls, divided by them)
-    gbs = call_bytes / (layer_ms * 1e-3) / 1e9
-
-    cpu = None
-    if args.cpu_sample > 0:
-        import oracle
-        n = min(args.cpu_sample, T)
-        c0 = time.time()
-        oracle.layer(x_bits[:n], inp["gate_w"], inp["arena"], inp["shared"], K, F, shape.routed_scale, None,
-                     oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32)
-        cs = time.time() - c0
-        cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"the first {n} of the {T} tokens in one oracle.layer call, {cs:.1f} s", **cpu_info()}
-
-    res = {
-        "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
-        "value": round(T / (layer_ms * 1e-3), 1),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": n_steps,
-        "warmup": max(args.warmup, n_place),
-        "ms_per_step": round(layer_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if prec == qm.PREC_BF16 else "f32",
-        "data": "synthetic",
-        "config": {"workload": "xing4 MoE layer, T=128 per call: hidden 3584, 64 experts top-4 + 1 shared, ffn "
-                               "1024, IQ4_NL experts, sigmoid router, scale 2.0, no selection bias; "
-                               f"{n_place} placements cycled",
-                   "tokens_per_step": T},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("batch_traffic.json"),
-                     "kernel": "moe_layer_forward T=128: router, top-k, bucketing, gate/up, down, combine "
-                               "(HIP events around the timed region, divided by the calls in it)",
-                     "bytes_per_launch": call_bytes, "avg_us": round(layer_ms * 1e3, 3),
-                     "per_call_events": {"avg_us": round(float(np.mean(call_us)), 3),
-                                         "median_us": round(float(np.median(call_us)), 3),
-                                         "note": "calls with HIP events around each"}},
-        "cpu_baseline": cpu,
-        "experts_touched": touched,
-        "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
-                              "median": float(np.median(counts))},
-        "setup_s": round(gen_s, 1),
-    }
-    print(json.dumps(res), flush=True)
-
-
-def chain(qm, x, out, y):
-    """Next layer's input into y: bf16(rmsnorm(x + out)), eps 1e-6, no weight (the chaining that stands in for
-    the rest of a decoder block; not part of the MoE layer), one fused kernel of the library."""
-    qm.moe_residual_rmsnorm(out, x, y, eps=1e-6)
-    return y
-
-
-def run_stack(args):
-    """38 MoE layers of the Xing4 shape resident in HBM, one token per step (T=1) through all of them,
-    each layer's input chained from the previous layer's output; Zipf(1.1) expert popularity."""
-    import torch
-
-    import quantized_moe_decode_sigmoid_amd as qm
-    import synth
-
-    shape = synth.WORKLOADS["stack"]
-    H, E, K, F = shape.hidden, shape.n_experts, shape.top_k, shape.ffn
-    nl = args.stack_layers
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    lam = synth.zipf_lambda(shape)
-    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
-    t0 = time.time()
-    layers = []
-    for l in range(nl):
-        inp = synth.layer_inputs(shape, layer=l, lam=lam)
-        layers.append(qm.DeviceLayer(cfg, inp["gate_w"], inp["bias"], inp["arena"], inp["shared"]))
-        del inp
+def timed_steps(torch, stream, fn, steps):
+    """Run fn() `steps` times on `stream` with a HIP event between consecutive steps; returns the total
+    and the per-step times in ms (events recorded on the launching stream)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record(stream)
+    for i in range(steps):
+        fn()
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    gen_s = time.time() - t0
-    S = args.stack_tokens
-    x_bits = synth.tokens(shape, S, first=7000)
-    x0 = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
-    ws = layers[0].workspace(1)
-    outs = [torch.empty((1, H), dtype=torch.float32, device=dev) for _ in range(nl)]
-    xs = [torch.empty((1, H), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
-    ids = torch.empty((S, nl, K), dtype=torch.int32, device=dev)
-    wts = torch.empty((S, nl, K), dtype=torch.float32, device=dev)
-
-    def steps():
-        for i in range(S):
-            x = x0[i:i + 1]
-            for l, dl in enumerate(layers):
-                qm.moe_layer_forward(cfg, 1, x, dl.gate_w, dl.bias, dl.arena, dl.shared, outs[l], ids[i, l],
-                                     wts[i, l], ws)
-                x = chain(qm, x, outs[l], xs[l])
-
-    stream = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        steps()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            steps()
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        # the MoE layer calls alone: events around each call of one eager pass over the S tokens, the
-        # queue kept busy by a spin kernel so that host launch gaps do not enter
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
-        torch.cuda._sleep(200_000_000)
-        for i in range(S):
-            x = x0[i:i + 1]
-            for l, dl in enumerate(layers):
-                starts[i * nl + l].record(stream)
-                qm.moe_layer_forward(cfg, 1, x, dl.gate_w, dl.bias, dl.arena, dl.shared, outs[l], ids[i, l],
-                                     wts[i, l], ws)
-                ends[i * nl + l].record(stream)
-                x = chain(qm, x, outs[l], xs[l])
-        torch.cuda.synchronize()
-    ms_per_token = ev0.elapsed_time(ev1) / (args.steps * S)
-    moe_ms_per_token = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / S
-    eb = qm.moe_expert_bytes(cfg)
-    expert_bytes = nl * (K + shape.n_shared) * eb
-    router_bytes = nl * E * H * 4
-    # rank-frequency: each layer's expert counts sorted (layers rank their experts differently), summed by rank
-    ids_h = ids.cpu().numpy()
-    by_rank = np.zeros(E, np.int64)
-    for l in range(nl):
-        by_rank += np.sort(np.bincount(ids_h[:, l, :].reshape(-1), minlength=E))[::-1]
-    counts = by_rank
-    c = by_rank.astype(np.float64)
-    c = c[c > 0]
-    slope = float(np.polyfit(np.log(np.arange(1, c.size + 1)), np.log(c), 1)[0]) if c.size > 1 else None
-    gbs = (expert_bytes + router_bytes) / (ms_per_token * 1e-3) / 1e9
-    res = {
-        "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
-        "value": round(1e3 / ms_per_token, 2),
-        "unit": "tok/s",
-        "n_gpus": 1,
-        "steps": args.steps * S,
-        "warmup": args.warmup * S,
-        "ms_per_step": round(ms_per_token, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": f"{nl}-layer MoE stack decode, T=1: each layer hidden 3584, 64 experts top-4 + 1 "
-                               "shared, ffn 1024, IQ4_NL, sigmoid router, scale 2.0; layer input = bf16(rmsnorm("
-                               "previous input + previous output)) by one fused kernel; Zipf(1.1) expert popularity",
-                   "layers": nl, "distinct_tokens": S, "zipf_lambda": lam, "graph": True},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "whole step: per layer k_decode_scores + k_decode_experts + k_residual_rmsnorm",
-                     "bytes_per_token": expert_bytes + router_bytes},
-        "expert_bytes_per_token": expert_bytes,
-        "moe_calls_ms_per_token": round(moe_ms_per_token, 4),
-        "moe_calls_gbs": round((expert_bytes + router_bytes) / (moe_ms_per_token * 1e-3) / 1e9, 1),
-        "popularity": {"rank_frequency_slope": slope, "routes_by_rank": [int(v) for v in by_rank[:16]],
-                       "routes": int(by_rank.sum())},
-        "setup_s": round(gen_s, 1),
-    }
-    print(json.dumps(res), flush=True)
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]), per
 
 
-def run_decode(args):
+class Check:
+    """Collects the output checks of every leg; a miss makes the exit status non-zero."""
+
+    def __init__(self):
+        self.failures = []
+
+    def compare(self, leg, got, want, ids=None, rid=None, w=None, rw=None):
+        got = np.asarray(got, np.float64)
+        want = np.asarray(want, np.float64)
+        mae = float(np.max(np.abs(got - want))) if got.size else 0.0
+        rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)) if got.size else 0.0
+        ok = bool(np.all(np.isfinite(got))) and mae <= TOL_MAX_ABS and rel <= TOL_REL_L2
+        res = {"rows": int(got.shape[0]) if got.ndim else 1, "max_abs": float(f"{mae:.3e}"),
+               "rel_l2": float(f"{rel:.3e}")}
+        if ids is not None:
+            same = bool(np.array_equal(ids, rid)) and bool(np.array_equal(
+                np.asarray(w, np.float32).view(np.uint32), np.asarray(rw, np.float32).view(np.uint32)))
+            res["routing_bit_exact"] = same
+            ok = ok and same
+        res["ok"] = ok
+        if not ok:
+            self.failures.append(f"{leg}: {res}")
+        return res
+
+    def status(self, leg, word):
+        if word != 0:
+            self.failures.append(f"{leg}: status word {word} (a decode wait gave up)")
+        return int(word)
+
+
+def status_word(torch, qm, cfg, T, ws):
+    st = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    qm.moe_workspace_status(cfg, T, ws, st)
+    return int(st[0].item())
+
+
+def oracle_rate(oracle, n, seconds, threads, sample):
+    return {"value": round(n / seconds, 3), "unit": "tok/s", "cores": threads, "kind": "oracle", "label": CPU_LABEL,
+            "sample": sample, "seconds": round(seconds, 2), **cpu_info()}
+
+
+# ---------------------------------------------------------------- decode (headline)
+
+def run_decode(args, check):
     import torch
 
     import quantized_moe_decode_sigmoid_amd as qm
@@ -547,7 +249,7 @@ def run_decode(args):
     stream = torch.cuda.Stream()
     graph = None
     with torch.cuda.stream(stream):
-        sweep()  # eager warm-up outside the graph (also the first-call figure)
+        sweep()  # eager warm-up outside the graph
         torch.cuda.synchronize()
         if not args.no_graph:
             graph = torch.cuda.CUDAGraph()
@@ -561,15 +263,9 @@ def run_decode(args):
         for _ in range(args.warmup):
             run()
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_wall = time.time()
-        ev0.record(stream)
-        for _ in range(args.steps):
-            run()
-        ev1.record(stream)
-        torch.cuda.synchronize()
+        total_ms, per_step = timed_steps(torch, stream, run, args.steps)
         wall_s = time.time() - t_wall
-        total_ms = ev0.elapsed_time(ev1)
 
         # kernel timing: HIP events around each token's launch on this stream, queued
         # behind a spin kernel so that the GPU never waits for the host
@@ -583,34 +279,60 @@ def run_decode(args):
                                  ids[i:i + 1], wts[i:i + 1], ws)
             ends[i].record(stream)
         torch.cuda.synchronize()
-    ffn_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
+        word = status_word(torch, qm, cfg, 1, ws)
+    call_ev_us = np.array([s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)])
 
     ms_per_step = total_ms / args.steps
     tok_s = N_TOKENS / (ms_per_step / 1e3)
-    expert_bytes_per_token = (K + shape.n_shared) * eb
     # algorithmic bytes of one layer launch (T=1): 5 experts, router weight, x, out
-    layer_bytes = expert_bytes_per_token + E * H * 4 + H * 2 + H * 4
+    layer_bytes = (K + shape.n_shared) * eb + E * H * 4 + H * 2 + H * 4
     # one layer call's duration over the timed region: the events bracketing the
-    # graph replays, divided by the calls they hold (the per-call events of the
-    # eager leg also hold the gap an event record adds between calls)
+    # graph replays, divided by the calls they hold
     call_us = ms_per_step * 1e3 / N_TOKENS
     achieved = layer_bytes / (call_us / 1e6) / 1e9
 
-    cpu = None
-    if args.cpu_sample > 0:
+    cpu, parity = None, None
+    if not args.no_cpu:
         import oracle
-        n = args.cpu_sample
+        thr = oracle.threads()
+        # tokens i < n use distinct layer i % distinct (placement i mod 32): one oracle call per distinct layer
+        n = 128 * distinct
+        want = np.empty((n, H), np.float32)
+        rid = np.empty((n, K), np.int32)
+        rw = np.empty((n, K), np.float32)
         c0 = time.time()
-        for i in range(n):
-            l = layers[(i % PLACEMENTS) % distinct]
-            oracle.layer(x_bits[i:i + 1], l["gate_w"], l["arena"], l["shared"], K, F, shape.routed_scale)
+        for d in range(distinct):
+            rows = np.arange(d, n, distinct)
+            l = layers[d]
+            want[rows], rid[rows], rw[rows] = oracle.layer(x_bits[rows], l["gate_w"], l["arena"], l["shared"], K, F,
+                                                           shape.routed_scale)
         cs = time.time() - c0
-        cpu = {"value": round(n / cs, 3), "unit": "tok/s", "cores": oracle.threads(), "kind": "oracle",
-               "sample": f"{n} of the {N_TOKENS} tokens, one oracle.layer call (T=1) each, {cs:.1f} s", **cpu_info()}
+        used = min(thr, n // distinct)
+        cpu = oracle_rate(oracle, n, cs, used, f"the first {n} of the {N_TOKENS} tokens, one oracle.layer call of "
+                                               f"{n // distinct} tokens per distinct layer ({used} threads)")
+        # the single-threaded oracle on a few of the same tokens: same bits (tokens are independent and each
+        # token's sums run in one fixed order), and its rate
+        oracle.set_threads(1)
+        n1 = 8
+        c0 = time.time()
+        one, _, _ = oracle.layer(x_bits[0:n1:distinct], layers[0]["gate_w"], layers[0]["arena"], layers[0]["shared"],
+                                 K, F, shape.routed_scale)
+        c1 = time.time() - c0
+        oracle.set_threads(0)
+        cpu["single_thread"] = {"value": round((n1 // distinct) / c1, 3), "unit": "tok/s", "cores": 1,
+                                "sample": f"{n1 // distinct} tokens of distinct layer 0, one call"}
+        cpu["single_equals_all_cores"] = bool(np.array_equal(one.view(np.uint32),
+                                                             want[0:n1:distinct].view(np.uint32)))
+        if not cpu["single_equals_all_cores"]:
+            check.failures.append("decode: single-threaded oracle differs from the all-core run")
+        got = out[:n].cpu().numpy()
+        parity = check.compare("decode", got, want, ids[:n].cpu().numpy(), rid, wts[:n].cpu().numpy(), rw)
     box = stream_gbs(torch)
+    parity = parity or {}
+    parity["status_word"] = check.status("decode", word)
 
-    res = {
-        "metric": "MoE-layer decode tok/s + achieved HBM GB/s (% peak); prefill TFLOP/s (% MFMA)",
+    return {
+        "metric": METRIC,
         "value": round(tok_s, 1),
         "unit": "tok/s",
         "n_gpus": 1,
@@ -626,22 +348,438 @@ def run_decode(args):
                                "ffn 1024, IQ4_NL experts, sigmoid router, scale 2.0; 1000 tokens per step over "
                                f"{PLACEMENTS} placements of {distinct} distinct seeded layers",
                    "tokens_per_step": N_TOKENS, "graph": graph is not None},
+        "step_spread": spread(per_step),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic("decode_traffic.json"),
                      "kernel": "moe_layer_forward T=1: k_decode_scores + k_decode_experts (HIP events around the "
                                "timed region of graph replays, divided by the layer calls in it)",
                      "bytes_per_launch": layer_bytes, "avg_us": round(call_us, 3),
-                     "per_call_events": {"avg_us": round(float(np.mean(ffn_us)), 3),
-                                         "median_us": round(float(np.median(ffn_us)), 3),
+                     "per_call_events": {"avg_us": round(float(np.mean(call_ev_us)), 3),
+                                         "median_us": round(float(np.median(call_ev_us)), 3),
                                          "note": "eager calls with HIP events around each"},
                      "box_stream": box, "frac_of_box_read": round(achieved / box["read_gbs"], 4)},
         "cpu_baseline": cpu,
+        "parity": parity,
         "layer_gbs": round(layer_bytes * tok_s / 1e9, 1),
         "first_step_ms": round(first_ms, 3),
         "wall_s": round(wall_s, 3),
         "setup_s": round(gen_s, 1),
     }
-    print(json.dumps(res), flush=True)
+
+
+# ---------------------------------------------------------------- prefill
+
+def run_prefill(args, check):
+    """One prefill-sized layer call per step: T=2048, H=2048, 256 experts top-8 + 1 shared, ffn 512,
+    Zipf(1.0) expert popularity through the selection bias; bf16 grouped MFMA FFN."""
+    import torch
+
+    import quantized_moe_decode_sigmoid_amd as qm
+    import synth
+
+    shape = synth.WORKLOADS["prefill"]
+    T, H, E, K, F = shape.tokens, shape.hidden, shape.n_experts, shape.top_k, shape.ffn
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    lam = synth.zipf_lambda(shape)
+    inp = synth.layer_inputs(shape, lam=lam)
+    x_bits = synth.tokens(shape, T)
+    gen_s = time.time() - t0
+    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
+    prec = qm.moe_resolved_precision(cfg, T)
+    dl = qm.DeviceLayer(cfg, inp["gate_w"], inp["bias"], inp["arena"], inp["shared"])
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, K), dtype=torch.float32, device=dev)
+    ws = dl.workspace(T)
+    steps = max(args.steps, 5)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        def step():
+            qm.moe_layer_forward(cfg, T, x, dl.gate_w, dl.bias, dl.arena, dl.shared, out, ids, wts, ws)
+
+        t_first = time.time()
+        step()
+        torch.cuda.synchronize()
+        first_ms = (time.time() - t_first) * 1e3
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        total_ms, per_step = timed_steps(torch, stream, step, steps)
+        layer_ms = total_ms / steps
+        # the expert FFN alone (bucketing, gate/up, down, combine) on the routing just computed
+        def ffn():
+            qm.moe_expert_forward(cfg, T, x, ids, wts, dl.arena, dl.shared, out, ws)
+        torch.cuda._sleep(50_000_000)
+        ffn_total, ffn_per = timed_steps(torch, stream, ffn, steps)
+    ffn_us = np.array(ffn_per) * 1e3
+    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
+    flops = 2.0 * 3 * H * F * (T * K + T * shape.n_shared)
+    # MFMA rows the 16-row sub-tiles execute per useful row (tiles of 128 routes of one expert)
+    rows_useful = T * K + T * shape.n_shared
+    rows_run = sum(16 * ((c + 15) // 16) for c in counts.tolist()) + 16 * ((T + 15) // 16) * shape.n_shared
+    ffn_avg_us = ffn_total * 1e3 / steps
+    ffn_tflops = flops / (ffn_avg_us * 1e-6) / 1e12
+    # algorithmic bytes of one moe_expert_forward call: every expert once (routed + shared), x, the
+    # routing (ids + weights), the fp32 output
+    ebytes = 3 * F * (H // 32) * 18
+    ffn_bytes = (E + shape.n_shared) * ebytes + T * H * 2 + T * K * 8 + T * H * 4
+    ffn_gbs = ffn_bytes / (ffn_avg_us * 1e-6) / 1e9
+
+    cpu, parity = None, None
+    if not args.no_cpu:
+        import oracle
+        n = 400
+        c0 = time.time()
+        want, rid, rw = oracle.layer(x_bits[:n], inp["gate_w"], inp["arena"], inp["shared"], K, F,
+                                     shape.routed_scale, inp["bias"], oracle.BF16 if prec == qm.PREC_BF16 else
+                                     oracle.FP32)
+        cs = time.time() - c0
+        used = min(oracle.threads(), n)
+        cpu = oracle_rate(oracle, n, cs, used, f"the first {n} of the {T} tokens in one oracle.layer call")
+        parity = check.compare("prefill", out[:n].cpu().numpy(), want, ids[:n].cpu().numpy(), rid,
+                               wts[:n].cpu().numpy(), rw)
+
+    mfma_bound = ffn_bytes / HBM_PEAK_GBS <= flops / 1e3 / MFMA_BF16_PEAK_TFLOPS
+    return {
+        "metric": METRIC,
+        "value": round(flops / (layer_ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(layer_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if prec == qm.PREC_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": "prefill MoE layer, T=2048: hidden 2048, 256 experts top-8 + 1 shared, ffn 512, "
+                               "IQ4_NL experts, sigmoid router, scale 2.0, Zipf(1.0) expert popularity",
+                   "tokens_per_step": T, "zipf_lambda": lam},
+        "step_spread": spread(per_step),
+        "mfma_tflops": round(ffn_tflops, 2),
+        "mfma_frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "hbm_frac": round(ffn_gbs / HBM_PEAK_GBS, 4),
+        # Every expert's weights are read once per call (more bytes than the 256 MB last-level cache), so
+        # the FFN's HBM floor (bytes / 8 TB/s) is above its MFMA floor (flops / 2.5 PFLOP/s): HBM-bound.
+        "roofline": {"bound": "mfma" if mfma_bound else "hbm",
+                     "achieved": round(ffn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ffn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("prefill_traffic.json"),
+                     "kernel": "moe_expert_forward bf16: k_bucket + k_gate_up_bf16 + k_down_bf16 (+ combine) "
+                               "(HIP events around each call on its stream)",
+                     "bytes_per_launch": ffn_bytes, "flops_per_launch": flops,
+                     "mfma_tflops": round(ffn_tflops, 2), "mfma_peak": MFMA_BF16_PEAK_TFLOPS,
+                     "mfma_frac": round(ffn_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "hbm_floor_us": round(ffn_bytes / HBM_PEAK_GBS / 1e3, 2),
+                     "mfma_floor_us": round(flops / 1e6 / MFMA_BF16_PEAK_TFLOPS, 2),
+                     "avg_us": round(ffn_avg_us, 3), "ffn_spread_us": spread(ffn_us)},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "tok_s": round(T / (layer_ms * 1e-3), 1),
+        "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
+                              "median": float(np.median(counts))},
+        "mfma_rows_per_useful_row": round(rows_run / rows_useful, 4),
+        "first_step_ms": round(first_ms, 3),
+        "setup_s": round(gen_s, 1),
+    }
+
+
+# ---------------------------------------------------------------- batch
+
+def run_batch(args, check):
+    """One Xing4 layer call of T=128 tokens per step (zero selection bias), on the multi-kernel exact-weight
+    path; four placements of the layer cycled so that consecutive steps do not share cached weights."""
+    import torch
+
+    import quantized_moe_decode_sigmoid_amd as qm
+    import synth
+
+    shape = synth.WORKLOADS["batch"]
+    T, H, E, K, F = shape.tokens, shape.hidden, shape.n_experts, shape.top_k, shape.ffn
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = synth.layer_inputs(shape)
+    x_bits = synth.tokens(shape, T)
+    gen_s = time.time() - t0
+    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
+    prec = qm.moe_resolved_precision(cfg, T)
+    n_place = 4
+    dl = qm.DeviceLayer(cfg, inp["gate_w"], None, inp["arena"], inp["shared"])
+    places = [(dl.gate_w.clone(), dl.arena.clone(), dl.shared.clone()) for _ in range(n_place)]
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, K), dtype=torch.float32, device=dev)
+    ws = dl.workspace(T)
+    n_steps = max(args.steps, 2 * n_place)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        it = [0]
+
+        def step():
+            g, a, sh = places[it[0] % n_place]
+            it[0] += 1
+            qm.moe_layer_forward(cfg, T, x, g, None, a, sh, out, ids, wts, ws)
+
+        for _ in range(max(args.warmup, n_place)):
+            step()
+        torch.cuda.synchronize()
+        total_ms, per_step = timed_steps(torch, stream, step, n_steps)
+        layer_ms = total_ms / n_steps
+    counts = np.bincount(ids.cpu().numpy().reshape(-1), minlength=E)
+    touched = int((counts > 0).sum())
+    eb = qm.moe_expert_bytes(cfg)
+    # algorithmic bytes of one call: each expert the batch routes to once, the shared expert, the router
+    # weight, x, the fp32 output
+    call_bytes = (touched + shape.n_shared) * eb + E * H * 4 + T * H * 2 + T * H * 4
+    gbs = call_bytes / (layer_ms * 1e-3) / 1e9
+
+    cpu, parity = None, None
+    if not args.no_cpu:
+        import oracle
+        c0 = time.time()
+        want, rid, rw = oracle.layer(x_bits, inp["gate_w"], inp["arena"], inp["shared"], K, F, shape.routed_scale,
+                                     None, oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32)
+        cs = time.time() - c0
+        used = min(oracle.threads(), T)
+        cpu = oracle_rate(oracle, T, cs, used, f"all {T} tokens of the call in one oracle.layer call")
+        parity = check.compare("batch", out.cpu().numpy(), want, ids.cpu().numpy(), rid, wts.cpu().numpy(), rw)
+
+    return {
+        "metric": METRIC,
+        "value": round(T / (layer_ms * 1e-3), 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": n_steps,
+        "warmup": max(args.warmup, n_place),
+        "ms_per_step": round(layer_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if prec == qm.PREC_BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": "xing4 MoE layer, T=128 per call: hidden 3584, 64 experts top-4 + 1 shared, ffn "
+                               "1024, IQ4_NL experts, sigmoid router, scale 2.0, no selection bias; "
+                               f"{n_place} placements cycled",
+                   "tokens_per_step": T},
+        "step_spread": spread(per_step),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("batch_traffic.json"),
+                     "kernel": "moe_layer_forward T=128: router, top-k, bucketing, gate/up, down, combine "
+                               "(HIP events around the timed region, divided by the calls in it)",
+                     "bytes_per_launch": call_bytes, "avg_us": round(layer_ms * 1e3, 3)},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "experts_touched": touched,
+        "routes_per_expert": {"max": int(counts.max()), "min": int(counts.min()),
+                              "median": float(np.median(counts))},
+        "setup_s": round(gen_s, 1),
+    }
+
+
+# ---------------------------------------------------------------- stack
+
+def run_stack(args, check):
+    """38 MoE layers of the Xing4 shape resident in HBM, one token per step (T=1) through all of them,
+    each layer's input chained from the previous layer's output by bf16(rmsnorm(x + out)) (one fused
+    kernel of the library); Zipf(1.1) expert popularity."""
+    import torch
+
+    import quantized_moe_decode_sigmoid_amd as qm
+    import synth
+
+    shape = synth.WORKLOADS["stack"]
+    H, E, K, F = shape.hidden, shape.n_experts, shape.top_k, shape.ffn
+    nl = args.stack_layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lam = synth.zipf_lambda(shape)
+    cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
+    t0 = time.time()
+    layers, host = [], []
+    for l in range(nl):
+        inp = synth.layer_inputs(shape, layer=l, lam=lam)
+        layers.append(qm.DeviceLayer(cfg, inp["gate_w"], inp["bias"], inp["arena"], inp["shared"]))
+        host.append(inp)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    S = args.stack_tokens
+    x_bits = synth.tokens(shape, S, first=7000)
+    x0 = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device=dev)
+    qm.moe_workspace_init(cfg, 1, ws)
+    outs = [torch.empty((1, H), dtype=torch.float32, device=dev) for _ in range(nl)]
+    xs = [torch.empty((1, H), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
+    ids = torch.empty((S, nl, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((S, nl, K), dtype=torch.float32, device=dev)
+
+    def token(i, x_in=None, o_out=None):
+        x = x0[i:i + 1]
+        for l, dl in enumerate(layers):
+            if x_in is not None:
+                x_in[l].copy_(x[0])
+            qm.moe_layer_forward(cfg, 1, x, dl.gate_w, dl.bias, dl.arena, dl.shared, outs[l], ids[i, l],
+                                 wts[i, l], ws)
+            if o_out is not None:
+                o_out[l].copy_(outs[l][0])
+            qm.moe_residual_rmsnorm(outs[l], x, xs[l], eps=1e-6)
+            x = xs[l]
+
+    def steps():
+        for i in range(S):
+            token(i)
+
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        steps()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            steps()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        total_ms, per_replay = timed_steps(torch, stream, graph.replay, args.steps)
+        # the MoE layer calls alone: events around each call of one eager pass over the S tokens, the
+        # queue kept busy by a spin kernel so that host launch gaps do not enter
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
+        torch.cuda._sleep(200_000_000)
+        for i in range(S):
+            x = x0[i:i + 1]
+            for l, dl in enumerate(layers):
+                starts[i * nl + l].record(stream)
+                qm.moe_layer_forward(cfg, 1, x, dl.gate_w, dl.bias, dl.arena, dl.shared, outs[l], ids[i, l],
+                                     wts[i, l], ws)
+                ends[i * nl + l].record(stream)
+                qm.moe_residual_rmsnorm(outs[l], x, xs[l], eps=1e-6)
+                x = xs[l]
+        torch.cuda.synchronize()
+        # every layer's input and output of the first tokens, for the oracle (eager, same kernels)
+        n_chk = min(S, 16)
+        x_in = torch.empty((n_chk, nl, H), dtype=torch.bfloat16, device=dev)
+        o_out = torch.empty((n_chk, nl, H), dtype=torch.float32, device=dev)
+        for i in range(n_chk):
+            token(i, x_in[i], o_out[i])
+        torch.cuda.synchronize()
+        word = status_word(torch, qm, cfg, 1, ws)
+    ms_per_token = total_ms / (args.steps * S)
+    moe_ms_per_token = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / S
+    eb = qm.moe_expert_bytes(cfg)
+    expert_bytes = nl * (K + shape.n_shared) * eb
+    router_bytes = nl * E * H * 4
+    # rank-frequency: each layer's expert counts sorted (layers rank their experts differently), summed by rank
+    ids_h = ids.cpu().numpy()
+    by_rank = np.zeros(E, np.int64)
+    for l in range(nl):
+        by_rank += np.sort(np.bincount(ids_h[:, l, :].reshape(-1), minlength=E))[::-1]
+    c = by_rank.astype(np.float64)
+    c = c[c > 0]
+    slope = float(np.polyfit(np.log(np.arange(1, c.size + 1)), np.log(c), 1)[0]) if c.size > 1 else None
+    gbs = (expert_bytes + router_bytes) / (ms_per_token * 1e-3) / 1e9
+
+    cpu, parity = None, None
+    if not args.no_cpu:
+        import oracle
+        # the oracle runs each layer on the GPU's input to that layer (n_chk tokens per call), so its outputs
+        # are also the per-layer check of the GPU chain
+        xin = x_in.view(torch.int16).cpu().numpy().view(np.uint16)
+        got = o_out.cpu().numpy()
+        gid, gw = ids_h[:n_chk], wts.cpu().numpy()[:n_chk]
+        want = np.empty_like(got)
+        rid = np.empty((n_chk, nl, K), np.int32)
+        rw = np.empty((n_chk, nl, K), np.float32)
+        c0 = time.time()
+        for l in range(nl):
+            inp = host[l]
+            want[:, l], rid[:, l], rw[:, l] = oracle.layer(xin[:, l], inp["gate_w"], inp["arena"], inp["shared"],
+                                                           K, F, shape.routed_scale, inp["bias"])
+        cs = time.time() - c0
+        used = min(oracle.threads(), n_chk)
+        cpu = oracle_rate(oracle, n_chk, cs, used, f"{n_chk} tokens through all {nl} layers, one oracle.layer call "
+                                                   f"of {n_chk} tokens per layer on the GPU chain's inputs")
+        parity = check.compare("stack", got.reshape(-1, H), want.reshape(-1, H), gid, rid, gw, rw)
+        parity["layers"] = nl
+    parity = parity or {}
+    parity["status_word"] = check.status("stack", word)
+    del layers, host
+    return {
+        "metric": METRIC,
+        "value": round(1e3 / ms_per_token, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps * S,
+        "warmup": args.warmup * S,
+        "ms_per_step": round(ms_per_token, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{nl}-layer MoE stack decode, T=1: each layer hidden 3584, 64 experts top-4 + 1 "
+                               "shared, ffn 1024, IQ4_NL, sigmoid router, scale 2.0; layer input = bf16(rmsnorm("
+                               "previous input + previous output)) by one fused kernel; Zipf(1.1) expert popularity",
+                   "layers": nl, "distinct_tokens": S, "zipf_lambda": lam, "graph": True},
+        "step_spread": spread(np.asarray(per_replay) / S),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("stack_traffic.json"),
+                     "kernel": "whole step: per layer k_decode_scores + k_decode_experts + k_residual_rmsnorm",
+                     "bytes_per_token": expert_bytes + router_bytes},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "expert_bytes_per_token": expert_bytes,
+        "moe_calls_ms_per_token": round(moe_ms_per_token, 4),
+        "moe_calls_gbs": round((expert_bytes + router_bytes) / (moe_ms_per_token * 1e-3) / 1e9, 1),
+        "popularity": {"rank_frequency_slope": slope, "routes_by_rank": [int(v) for v in by_rank[:16]],
+                       "routes": int(by_rank.sum())},
+        "setup_s": round(gen_s, 1),
+    }
+
+
+# ---------------------------------------------------------------- main
+
+LEGS = {"decode": run_decode, "prefill": run_prefill, "batch": run_batch, "stack": run_stack}
+NESTED = ("prefill", "batch", "stack")
+
+
+def brief(line):
+    """A nested leg: its own line without the keys the top level already carries."""
+    return {k: v for k, v in line.items() if k not in ("metric", "n_gpus", "higher_is_better", "scaling", "data")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "the benchmark measures one GPU (every workload here fits one MI355X); "
+                                   "--gpus must be 1"}))
+        sys.exit(2)
+    if args.copy_mb > 0:
+        copy_calibration(args.copy_mb)
+    check = Check()
+    if args.workload != "all":
+        line = LEGS[args.workload](args, check)
+    else:
+        import torch
+        line = run_decode(args, check)
+        torch.cuda.empty_cache()
+        for leg in NESTED:
+            print(f"[bench] {leg}", file=sys.stderr, flush=True)
+            try:
+                line[leg] = brief(LEGS[leg](args, check))
+            except Exception as e:  # the line is still printed; the exit status reports it
+                line[leg] = {"error": f"{type(e).__name__}: {e}"}
+                check.failures.append(f"{leg}: {type(e).__name__}: {e}")
+            torch.cuda.empty_cache()
+    line["checks"] = {"ok": not check.failures, "failures": check.failures}
+    print(json.dumps(line), flush=True)
+    if check.failures:
+        sys.exit(1)
 
 
 if __name__ == "__main__":

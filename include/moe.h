@@ -59,8 +59,13 @@ typedef enum {
 } moe_status;
 
 /* Arithmetic contract of the expert FFN.
- * FP32: weights are the exact IQ4_NL values d*level, the activation product
- *       silu(g)*u is kept in fp32, all sums in fp32 (decode-sized calls).
+ * FP32: weights are the exact IQ4_NL values d*level; g, u, y and the combine
+ *       are fp32 sums; h = silu(g)*u is formed in fp32 and handed to the down
+ *       projection as two bf16 terms, h_hi = bf16(h) and h_lo = bf16(h - h_hi)
+ *       (nearest even), whose sum is within 2^-16 * |h| of h (decode-sized
+ *       calls).  Against a double-precision evaluation with exact weights the
+ *       output then differs by fp32 summation order, the fp32 SiLU and this
+ *       split.
  * BF16: weights are the exact values rounded to bf16 (nearest even), the
  *       product silu(g)*u is rounded to bf16 before the down projection;
  *       products run on bf16 MFMA with fp32 accumulation (batched / prefill
@@ -110,6 +115,14 @@ size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
  * that gives up (which a correct launch never does) sets this word to 1.
  * Workspaces need no other preparation. */
 moe_status moe_workspace_init(const moe_config* cfg, int32_t T, void* ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* Copy the status word of a workspace (see moe_workspace_init: 0 = every wait
+ * of the decode path ended normally, 1 = one gave up and that call's outputs are
+ * not valid) to status_dev, a device int32, on `stream` (a kernel: no host
+ * synchronization, no readback).  The word is sticky until the next
+ * moe_workspace_init. */
+moe_status moe_workspace_status(const moe_config* cfg, int32_t T, const void* ws_dev, size_t ws_bytes,
+                                int32_t* status_dev, hipStream_t stream);
 
 /* ---- expert arena --------------------------------------------------------
  * GGUF order (input of moe_pack_experts): expert e starts at e*expert_bytes;
@@ -163,6 +176,15 @@ moe_status moe_dequant(const moe_config* cfg, const void* packed_expert_dev, int
 moe_status moe_route(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
                      const float* sel_bias_dev, int32_t* topk_ids_dev, float* topk_w_dev, void* ws_dev,
                      size_t ws_bytes, hipStream_t stream);
+
+/* The router's first half alone: scores_dev fp32 [T][E] receives
+ * s[t][e] = sigmoid(x[t] . gate_w[e]), the fp32 logit in the fixed order stated
+ * for moe_route and the sigmoid evaluated as stated there (model card
+ * xing4_0-29b-IQ4_NL_EPQ, "Model and routing": expert_gating_func = sigmoid).
+ * These are the scores moe_route selects from and normalises (before the
+ * selection bias).  Needs no workspace. */
+moe_status moe_router_scores(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
+                             float* scores_dev, hipStream_t stream);
 
 /* Token-to-expert bucketing (design record, section 4: routes sorted by
  * expert so each output has one writer).  Route r = t*K + k.

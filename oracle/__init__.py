@@ -60,6 +60,9 @@ def _load():
     lib.oracle_expert.argtypes = [i32, i32, vp, vp, i32, vp]
     lib.oracle_layer.argtypes = [i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_threads.restype = i32
+    lib.oracle_set_threads.argtypes = [i32]
+    lib.oracle_sigmoid_many.argtypes = [i64, vp, vp]
+    lib.oracle_residual_rmsnorm.argtypes = [i32, i32, vp, vp, f64, vp]
     _lib = lib
     return lib
 
@@ -74,6 +77,11 @@ def _c(a, dtype):
 
 def threads() -> int:
     return _load().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the token loop of layer() (0 = the OpenMP default); results do not depend on it."""
+    _load().oracle_set_threads(n)
 
 
 def codebook() -> list[int]:
@@ -99,6 +107,24 @@ def exp_spec(y: float) -> float:
 
 def sigmoid(l: float) -> float:
     return _load().oracle_sigmoid(l)
+
+
+def sigmoid_many(logits: np.ndarray) -> np.ndarray:
+    """sigmoid() over an array of fp32 logits."""
+    l = _c(logits, np.float32).reshape(-1)
+    out = np.empty(l.size, np.float32)
+    _load().oracle_sigmoid_many(l.size, _ptr(l), _ptr(out))
+    return out.reshape(np.shape(logits))
+
+
+def residual_rmsnorm(x: np.ndarray, out: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """Stack chaining glue (not the layer): bf16(rmsnorm(x + out)), x bf16 bits [T,H], out fp32 [T,H]."""
+    x = _c(x, np.uint16)
+    out = _c(out, np.float32)
+    T, H = x.shape
+    y = np.empty((T, H), np.uint16)
+    _load().oracle_residual_rmsnorm(T, H, _ptr(x), _ptr(out), eps, _ptr(y))
+    return y
 
 
 def dequant(blocks: np.ndarray, mode: int = FP32) -> np.ndarray:

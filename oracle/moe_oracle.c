@@ -327,3 +327,40 @@ void oracle_layer(int T, int H, int F, int E, int K, int n_shared, float scale, 
   free(ids);
   free(w);
 }
+
+/* ---- helpers for the test suite and the benchmark's CPU leg ------------ */
+
+/* oracle_sigmoid over n values (the same function, one call per element). */
+void oracle_sigmoid_many(int64_t n, const float* l, float* s) {
+  for (int64_t i = 0; i < n; i++) s[i] = oracle_sigmoid(l[i]);
+}
+
+/* Threads the token loop of oracle_layer may use (OpenMP); 0 keeps the
+ * default.  Results do not depend on it. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+/* Chaining between the layers of a stack (not part of the MoE layer; harness
+ * glue for the 38-layer workload): per row,
+ *   h = x + out, y = bf16(h / sqrt(mean(h^2) + eps))
+ * with x the layer's bf16 input and out its fp32 output, an unweighted RMS
+ * norm (the model card's attention-free stand-in for the rest of a decoder
+ * block), evaluated in double and rounded once to bf16 (nearest even). */
+void oracle_residual_rmsnorm(int T, int H, const uint16_t* x, const float* out, double eps, uint16_t* y) {
+  double* h = (double*)malloc(sizeof(double) * H);
+  for (int t = 0; t < T; t++) {
+    double ss = 0.0;
+    for (int i = 0; i < H; i++) {
+      h[i] = (double)oracle_bf16_value(x[(int64_t)t * H + i]) + (double)out[(int64_t)t * H + i];
+      ss += h[i] * h[i];
+    }
+    double r = 1.0 / sqrt(ss / H + eps);
+    for (int i = 0; i < H; i++) y[(int64_t)t * H + i] = oracle_to_bf16((float)(h[i] * r));
+  }
+  free(h);
+}

@@ -57,8 +57,10 @@ _SIGS = {
     "moe_resolved_precision": ([_cfgp, _i32], _i32),
     "moe_workspace_bytes": ([_cfgp, _i32], _sz),
     "moe_workspace_init": ([_cfgp, _i32, _vp, _sz, _vp], _i32),
+    "moe_workspace_status": ([_cfgp, _i32, _vp, _sz, _vp, _vp], _i32),
     "moe_pack_experts": ([_cfgp, _i32, _vp, _vp, _vp], _i32),
     "moe_dequant": ([_cfgp, _vp, _i32, _i32, _vp, _vp], _i32),
+    "moe_router_scores": ([_cfgp, _i32, _vp, _vp, _vp, _vp], _i32),
     "moe_route": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_bucket": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_expert_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
@@ -123,6 +125,13 @@ def moe_workspace_init(cfg, T, ws, ws_bytes=None, stream=None):
     _check(_lib.moe_workspace_init(ctypes.byref(cfg), T, _p(ws), ws_bytes, _stream(stream)), "moe_workspace_init")
 
 
+def moe_workspace_status(cfg, T, ws, status, ws_bytes=None, stream=None):
+    """Copy the workspace's status word (0 ok, 1 a decode wait gave up) into the device int32 tensor status."""
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.moe_workspace_status(ctypes.byref(cfg), T, _p(ws), ws_bytes, _p(status), _stream(stream)),
+           "moe_workspace_status")
+
+
 def moe_pack_experts(cfg, n_experts, src, dst, stream=None):
     _check(_lib.moe_pack_experts(ctypes.byref(cfg), n_experts, _p(src), _p(dst), _stream(stream)), "moe_pack_experts")
 
@@ -141,6 +150,11 @@ def moe_residual_rmsnorm(out, x, y, eps=1e-6, stream=None):
 def moe_dequant(cfg, packed_expert, matrix, precision, out, stream=None):
     _check(_lib.moe_dequant(ctypes.byref(cfg), _p(packed_expert), matrix, precision, _p(out), _stream(stream)),
            "moe_dequant")
+
+
+def moe_router_scores(cfg, T, x, gate_w, scores, stream=None):
+    _check(_lib.moe_router_scores(ctypes.byref(cfg), T, _p(x), _p(gate_w), _p(scores), _stream(stream)),
+           "moe_router_scores")
 
 
 def moe_route(cfg, T, x, gate_w, sel_bias, topk_ids, topk_w, ws, ws_bytes=None, stream=None):

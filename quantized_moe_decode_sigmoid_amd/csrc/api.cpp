@@ -55,9 +55,12 @@ int max_chunks(const moe_config* c, int T, int rows) {
 int max_chunks(const moe_config* c, int T) { return max_chunks(c, T, chunk_rows(resolve_precision(c, T))); }
 
 // The two-launch decode path covers one token with the exact-weight contract.
+// Its second kernel hands data between workgroups, so it is taken only when
+// the device holds that kernel's whole grid at once.
 bool decode_path(const moe_config* c, int T) {
   return T == 1 && c->top_k <= qmoe::kMaxDecodeK && c->ffn <= qmoe::kMaxDecodeFfn &&
-         c->hidden <= qmoe::kMaxDecodeHidden && resolve_precision(c, T) == MOE_PREC_FP32;
+         c->hidden <= qmoe::kMaxDecodeHidden && resolve_precision(c, T) == MOE_PREC_FP32 &&
+         qmoe::decode_grid_coresident(c->ffn, c->top_k, c->hidden, c->n_shared);
 }
 
 // Workspace plan: 256-byte aligned sub-buffers.
@@ -194,6 +197,17 @@ MOE_API moe_status moe_workspace_init(const moe_config* cfg, int32_t T, void* ws
   return launched(qmoe::launch_zero_words(at<uint32_t>(ws_dev, p.status), 1, stream));
 }
 
+MOE_API moe_status moe_workspace_status(const moe_config* cfg, int32_t T, const void* ws_dev, size_t ws_bytes,
+                                        int32_t* status_dev, hipStream_t stream) {
+  TRY(check_common(cfg, T));
+  TRY(need(ws_dev));
+  TRY(need(status_dev));
+  const Plan p = make_plan(cfg, T);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  return launched(qmoe::launch_copy_words(at<const uint32_t>(const_cast<void*>(ws_dev), p.status),
+                                          reinterpret_cast<uint32_t*>(status_dev), 1, stream));
+}
+
 MOE_API moe_status moe_pack_experts(const moe_config* cfg, int32_t n_experts, const void* src_dev, void* dst_dev,
                                     hipStream_t stream) {
   TRY(check_cfg(cfg));
@@ -258,6 +272,17 @@ MOE_API moe_status moe_route(const moe_config* cfg, int32_t T, const void* x_dev
   return launched(qmoe::launch_router(static_cast<const uint16_t*>(x_dev), gate_w_dev, sel_bias_dev, T, cfg->hidden,
                                       cfg->n_experts, cfg->top_k, cfg->routed_scale, at<float>(ws_dev, p.scores),
                                       topk_ids_dev, topk_w_dev, stream));
+}
+
+MOE_API moe_status moe_router_scores(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
+                                     float* scores_dev, hipStream_t stream) {
+  TRY(check_common(cfg, T));
+  if (T == 0) return MOE_OK;
+  TRY(need(x_dev));
+  TRY(need(gate_w_dev));
+  TRY(need(scores_dev));
+  return launched(qmoe::launch_router_scores(static_cast<const uint16_t*>(x_dev), gate_w_dev, T, cfg->hidden,
+                                             cfg->n_experts, scores_dev, stream));
 }
 
 MOE_API moe_status moe_bucket(const moe_config* cfg, int32_t T, const int32_t* topk_ids_dev, int32_t* counts_dev,

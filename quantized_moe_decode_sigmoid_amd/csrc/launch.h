@@ -8,6 +8,10 @@
 
 namespace qmoe {
 
+// The sigmoid scores [T][E] alone (the first half of launch_router).
+hipError_t launch_router_scores(const uint16_t* x, const float* wg, int T, int H, int E, float* scores,
+                                hipStream_t stream);
+
 hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
                          float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream);
 
@@ -64,6 +68,16 @@ struct DecodeArgs {
 hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream);
 
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
+
+// dst[i] = src[i] for i < n (device words; a kernel, so that it can sit in a captured graph)
+hipError_t launch_copy_words(const uint32_t* src, uint32_t* dst, int64_t n, hipStream_t stream);
+
+// Whether the k_decode_experts grid of this shape fits on the current device at
+// once (occupancy x compute units >= workgroups).  Its down workgroups wait for
+// data from its gate/up workgroups; co-residency makes every wait end whatever
+// the dispatch order.  Queried once per device and shape class; false if the
+// runtime cannot answer.
+bool decode_grid_coresident(int F, int K, int H, int n_shared);
 
 // ---- measurement (stream.hip) and the stack workload's chaining (chain.hip)
 

@@ -30,6 +30,8 @@
 // Operands shared by all wavefronts of a workgroup (x, block scales, h) are
 // staged once in LDS with coalesced loads.  Every wait is bounded: one that
 // exceeds the bound sets an error word and gives up, so a launch always ends.
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 #include "router_math.h"
@@ -461,6 +463,37 @@ __global__ __launch_bounds__(kDecThreads, 8) void k_decode_experts(DecodeArgs a)
   }
 }
 
+namespace {
+
+int decode_grid_size(int F, int K, int H, int n_shared) { return (n_shared ? F / 16 : 0) + K * (F / 16) + H / 32; }
+
+}  // namespace
+
+// Workgroups of k_decode_experts that one device holds at once (0 if unknown),
+// cached per device: the kernel's resources do not depend on the shape.
+static std::atomic<int> g_decode_capacity[64];
+
+bool decode_grid_coresident(int F, int K, int H, int n_shared) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    clear_last_error();
+    return false;
+  }
+  int cap = g_decode_capacity[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_decode_experts),
+                                                     kDecThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      clear_last_error();
+      return false;
+    }
+    cap = per_cu * cus > 0 ? per_cu * cus : -1;  // -1: known not to fit anything
+    g_decode_capacity[dev].store(cap, std::memory_order_relaxed);
+  }
+  return cap > 0 && decode_grid_size(F, K, H, n_shared) <= cap;
+}
+
 hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream) {
   a.n_router = a.E;  // one wavefront per expert
   a.n_shared_wg = a.n_shared ? a.F / 16 : 0;
@@ -479,6 +512,18 @@ hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream) {
 __global__ void k_fill_u32(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
+}
+
+__global__ void k_copy_u32(const uint32_t* src, uint32_t* dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+hipError_t launch_copy_words(const uint32_t* src, uint32_t* dst, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  clear_last_error();
+  hipLaunchKernelGGL(k_copy_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, src, dst, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream) {

@@ -217,8 +217,8 @@ constexpr int kRouterTiledMinTokens = 64;
 constexpr int64_t kRouterBigBlockWaves = 512;
 constexpr int64_t kRouterResidentWaves = 2048;
 
-hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
-                         float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream) {
+hipError_t launch_router_scores(const uint16_t* x, const float* wg, int T, int H, int E, float* scores,
+                                hipStream_t stream) {
   if (T == 0) return hipSuccess;
   int tpw = (int)(((int64_t)T * E) / 8192);
   tpw = tpw < 1 ? 1 : (tpw > 64 ? 64 : tpw);
@@ -227,21 +227,27 @@ hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, 
   clear_last_error();
   if (T >= kRouterTiledMinTokens) {
     if ((int64_t)((T + 7) / 8) * ((E + 7) / 8) > kRouterBigBlockWaves) {
-      launch_router_tiled<8, 8>(x, wg, T, H, E, scores_ws, stream);
+      launch_router_tiled<8, 8>(x, wg, T, H, E, scores, stream);
     } else if (H <= 16 * 256 && (int64_t)((T + 1) / 2) * ((E + 1) / 2) <= kRouterResidentWaves) {
       const dim3 grid((unsigned)((T + 3) / 4), (unsigned)((E + 3) / 4));
       if (H <= 8 * 256)
-        hipLaunchKernelGGL(k_router_scores_resident<8>, grid, dim3(256), 0, stream, x, wg, T, H, E, scores_ws);
+        hipLaunchKernelGGL(k_router_scores_resident<8>, grid, dim3(256), 0, stream, x, wg, T, H, E, scores);
       else
-        hipLaunchKernelGGL(k_router_scores_resident<16>, grid, dim3(256), 0, stream, x, wg, T, H, E, scores_ws);
+        hipLaunchKernelGGL(k_router_scores_resident<16>, grid, dim3(256), 0, stream, x, wg, T, H, E, scores);
     } else {
-      launch_router_tiled<4, 4>(x, wg, T, H, E, scores_ws, stream);
+      launch_router_tiled<4, 4>(x, wg, T, H, E, scores, stream);
     }
   } else if (H <= 16 * 256)
-    hipLaunchKernelGGL(k_router_scores<16>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores_ws);
+    hipLaunchKernelGGL(k_router_scores<16>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores);
   else
-    hipLaunchKernelGGL(k_router_scores<32>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores_ws);
-  hipError_t err = hipGetLastError();
+    hipLaunchKernelGGL(k_router_scores<32>, dim3(blocks), dim3(256), 0, stream, x, wg, T, H, E, tpw, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
+                         float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  hipError_t err = launch_router_scores(x, wg, T, H, E, scores_ws, stream);
   if (err != hipSuccess) return err;
   clear_last_error();
   hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, stream, scores_ws, bias, T, E, K, scale, ids, w);

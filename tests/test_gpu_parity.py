@@ -40,6 +40,13 @@ def log(msg):
     print(f"[case] {msg}", flush=True)
 
 
+def assert_status_ok(cfg, T, ws):
+    """The workspace's status word through the C ABI: 0 unless a wait of the decode path gave up."""
+    st = torch.full((4,), -1, dtype=torch.int32, device="cuda")
+    qm.moe_workspace_status(cfg, T, ws, st)
+    assert int(st[0].item()) == 0, "a wait of the decode path gave up"
+
+
 # ---------------------------------------------------------------- dequant (bit-exact)
 
 @pytest.mark.parametrize("name", ["tiny", "xing4", "prefill"])
@@ -112,6 +119,48 @@ def test_route_large_hidden_bit_exact():
     assert np.array_equal(w.cpu().numpy().view(np.uint32), rw.view(np.uint32))
 
 
+def sigmoid_grid(n):
+    """n fp32 logits in [-30, 30]: an even grid, plus powers of two and random bit patterns near 0."""
+    rng = np.random.default_rng(77)
+    k = np.arange(-126, 5, dtype=np.float64)
+    special = np.concatenate([2.0 ** k, -(2.0 ** k), [0.0, -0.0, 30.0, -30.0, 1e-45, -1e-45]]).astype(np.float32)
+    bits = rng.integers(0x30000000, 0x41F00000, 4096).astype(np.uint32)  # |l| from ~5e-10 to 30
+    rnd = bits.view(np.float32) * np.where(rng.integers(0, 2, 4096) > 0, 1.0, -1.0).astype(np.float32)
+    base = np.linspace(-30.0, 30.0, n - special.size - rnd.size).astype(np.float32)
+    return np.concatenate([base, special, rnd]).astype(np.float32)
+
+
+@pytest.mark.parametrize("T", [4096, 48])
+def test_router_sigmoid_dense_grid_bit_exact(T):
+    """The GPU sigmoid against the oracle's on a dense grid of 2^20 fp32 logits in [-30, 30], bit for bit.
+    Token t is one-hot at element t (H = 4096), so its logit for expert e is exactly gate_w[e][t]: every
+    other product is zero and the fixed-order sum adds only zeros to it.  T = 4096 runs the 8 x 8 tiled
+    router kernel over the whole grid, T = 48 the one-row-per-wavefront kernel over its first 48 columns."""
+    H, E = 4096, 256
+    grid = sigmoid_grid(H * E).reshape(E, H)
+    x = np.zeros((T, H), np.uint16)
+    x[np.arange(T), np.arange(T)] = 0x3F80  # bf16 1.0
+    cfg = qm.make_config(H, 128, E, 8)
+    scores = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    log(f"sigmoid grid T={T}")
+    qm.moe_router_scores(cfg, T, to_dev_bf16(x), torch.from_numpy(grid).cuda(), scores)
+    got = scores.cpu().numpy()
+    want = oracle.sigmoid_many(np.ascontiguousarray(grid[:, :T].T))
+    bad = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
+    assert bad.size == 0, (bad.size, grid[:, :T].T.reshape(-1)[bad[:5]])
+
+
+def test_router_scores_match_route_scores():
+    """moe_router_scores on real weights equals the oracle's scores bit for bit (prefill shape, T = 300)."""
+    s, inp, dl = device_layer("prefill")
+    x = synth.tokens(s, 300, first=31)
+    scores = torch.empty((300, s.n_experts), dtype=torch.float32, device="cuda")
+    log("router scores prefill T=300")
+    qm.moe_router_scores(dl.cfg, 300, to_dev_bf16(x), dl.gate_w, scores)
+    _, _, _, want = oracle.route(x, inp["gate_w"], s.top_k, s.routed_scale)
+    assert np.array_equal(scores.cpu().numpy().view(np.uint32), want.view(np.uint32))
+
+
 # ---------------------------------------------------------------- bucketing (bit-exact)
 
 @pytest.mark.parametrize("T,K,E", [(4, 2, 8), (1, 4, 64), (128, 4, 64), (2048, 8, 256), (1000, 3, 5), (0, 4, 64),
@@ -145,6 +194,7 @@ def layer_parity(name, T, first=0, sample=None, bias=None, precision=qm.PREC_AUT
     ids = torch.empty((T, s.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, s.top_k), dtype=torch.float32, device="cuda")
     out = dl.forward(to_dev_bf16(x), topk_ids=ids, topk_w=w).cpu().numpy()
+    assert_status_ok(cfg, T, dl.workspace(T))
     rows = np.arange(T) if sample is None else np.asarray(sample)
     mode = oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32
     ref, rid, rw = oracle.layer(x[rows], inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn,
@@ -184,6 +234,7 @@ def extra_layer_parity(name, T, first=0, precision=qm.PREC_AUTO):
     ids = torch.empty((T, s.top_k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, s.top_k), dtype=torch.float32, device="cuda")
     out = dl.forward(to_dev_bf16(x), topk_ids=ids, topk_w=w).cpu().numpy()
+    assert_status_ok(dl.cfg, T, dl.workspace(T))
     mode = oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32
     ref, rid, rw = oracle.layer(x, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn, s.routed_scale,
                                 None, mode)
@@ -231,8 +282,9 @@ def test_layer_xing4_small_batch():
     layer_parity("xing4", 5, first=40)
 
 
-def test_layer_batch_128_sampled():
-    layer_parity("batch", 128, sample=[0, 1, 17, 63, 64, 100, 127])
+def test_layer_batch_128_all_rows():
+    """The batch workload at its full size (T = 128, Xing4 layer, FP32 contract by AUTO): every row."""
+    layer_parity("batch", 128)
 
 
 @pytest.mark.parametrize("precision", [qm.PREC_AUTO, qm.PREC_FP32])
@@ -320,9 +372,7 @@ def test_decode_path_equals_multi_kernel_path(name, T, first):
     a = dl.forward(xd).cpu().numpy()
     b = multi_kernel_layer(dl, xd, T).cpu().numpy()
     assert_paths_agree(a, b, f"{name} T={T}")
-    torch.cuda.synchronize()
-    status = dl.workspace(T)[:4].view(torch.int32).cpu().numpy()
-    assert status[0] == 0, "a wait of the decode path gave up"
+    assert_status_ok(dl.cfg, T, dl.workspace(T))
 
 
 def test_decode_path_many_consecutive_calls_one_workspace():
@@ -332,6 +382,7 @@ def test_decode_path_many_consecutive_calls_one_workspace():
     log("decode path, 64 consecutive T=1 calls")
     outs = [dl.forward(xd[i:i + 1]) for i in range(64)]
     got = torch.cat(outs).cpu().numpy()
+    assert_status_ok(dl.cfg, 1, dl.workspace(1))
     ref = multi_kernel_layer(dl, xd, 64).cpu().numpy()
     assert_paths_agree(got, ref, "64 consecutive decode calls")
 
@@ -359,6 +410,7 @@ def test_decode_route_bit_exact(with_bias):
         ids, w = decode_route(dl, x[t:t + 1])
         assert np.array_equal(ids[0], rid[t]), t
         assert np.array_equal(w[0].view(np.uint32), rw[t].view(np.uint32)), t
+    assert_status_ok(dl.cfg, 1, dl.workspace(1))
 
 
 @pytest.mark.parametrize("path", ["decode", "multi-kernel"])
@@ -405,8 +457,7 @@ def test_decode_state_survives_batched_calls_on_the_same_workspace():
         big = torch.empty((T, s.hidden), dtype=torch.float32, device="cuda")
         qm.moe_layer_forward(cfg, T, xd[:T], dl.gate_w, None, dl.arena, dl.shared, big, ws=ws)
     assert_paths_agree(torch.cat(got).cpu().numpy(), ref, "decode calls between batched calls")
-    torch.cuda.synchronize()
-    assert ws[:4].view(torch.int32).cpu().numpy()[0] == 0, "a wait of the decode path gave up"
+    assert_status_ok(cfg, 300, ws)
 
 
 def test_graph_replay_of_decode_calls():
@@ -432,6 +483,7 @@ def test_graph_replay_of_decode_calls():
         _ = dl.forward(xd[rep:rep + 1])  # eager work between replays
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.view(np.uint32)), rep
+    assert_status_ok(dl.cfg, 1, ws)
 
 
 # ---------------------------------------------------------------- bf16 grouped MFMA path
@@ -450,8 +502,8 @@ def test_layer_bf16_tiles_past_128_rows():
     layer_parity("tiny", 300, first=3, bias=bias, precision=qm.PREC_BF16)
 
 
-def test_layer_batch_128_bf16_sampled():
-    layer_parity("batch", 128, sample=[0, 1, 17, 63, 64, 100, 127], precision=qm.PREC_BF16)
+def test_layer_batch_128_bf16_all_rows():
+    layer_parity("batch", 128, precision=qm.PREC_BF16)
 
 
 def prefill_bias():
@@ -459,11 +511,30 @@ def prefill_bias():
     return synth.zipf_bias(s, synth.zipf_lambda(s))
 
 
-def test_layer_prefill_full_size_sampled():
-    """T=2048, H=2048, 256 experts top-8 + shared, ffn 512, Zipf(1.0) popularity (AUTO -> bf16)."""
-    s, _ = workload("prefill")
+def prefill_rows_checked():
+    """Rows of the T = 2048 prefill call compared with the oracle: every token of the last tile of 128
+    routes of the most popular expert, every token of the shared expert's last tile (tokens 1920..2047),
+    the first and last tokens and a seeded sample (>= 256 rows)."""
+    s, inp = workload("prefill")
+    x = synth.tokens(s, 2048, first=0)
+    rid, _, _, _ = oracle.route(x, inp["gate_w"], s.top_k, s.routed_scale, prefill_bias())
+    counts, offsets, perm, _ = oracle.bucket(rid, s.n_experts)
+    hot = int(np.argmax(counts))
+    last_tile = offsets[hot] + 128 * ((counts[hot] - 1) // 128)
+    hot_rows = (perm[last_tile:offsets[hot + 1]] // s.top_k).tolist()
+    rows = set(hot_rows) | set(range(1920, 2048)) | {0, 1, 127, 128, 1023}
     rng = np.random.default_rng(11)
-    rows = sorted(set([0, 1, 127, 128, 1023, 2047] + rng.choice(2048, 18, replace=False).tolist()))
+    extra = [r for r in rng.permutation(2048).tolist() if r not in rows]
+    rows |= set(extra[:max(0, 256 - len(rows))])
+    return sorted(rows), hot, counts[hot], len(hot_rows)
+
+
+def test_layer_prefill_full_size_rows():
+    """T=2048, H=2048, 256 experts top-8 + shared, ffn 512, Zipf(1.0) popularity (AUTO -> bf16): the hottest
+    expert's last tile, one whole shared-expert tile and a sample, >= 256 rows against the oracle."""
+    rows, hot, n_hot, n_tile = prefill_rows_checked()
+    log(f"prefill rows: {len(rows)} (expert {hot}: {n_hot} routes, last tile {n_tile} rows)")
+    assert len(rows) >= 256
     out = layer_parity("prefill", 2048, first=0, sample=rows, bias=prefill_bias())
     assert np.all(np.isfinite(out))
 

@@ -467,3 +467,55 @@ def test_page_size_arithmetic():
     assert 3 * pre.hidden * pre.ffn == st["params"]
     assert st["params"] * (st["bits"] + st["group_overhead_bits"]) / 8 == pre.expert_bytes
     assert round(pre.expert_bytes / 1e6, 2) == st["mbytes"]
+
+
+# ---------------------------------------------------------------- stack chaining glue (not the layer)
+
+def _bf16_bits(v):
+    return (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_residual_rmsnorm_closed_forms():
+    H = 256
+    # a constant row normalises to +-1 exactly (eps = 0), from x or from out alike
+    for c in (3.0, -0.125, 1e-3):
+        x = np.tile(_bf16_bits([c]), (1, H))
+        y = oracle.residual_rmsnorm(x, np.zeros((1, H), np.float32), eps=0.0)
+        assert np.all(y == _bf16_bits([np.sign(c)])), c
+        y2 = oracle.residual_rmsnorm(np.zeros((1, H), np.uint16), np.full((1, H), np.float32(oracle.bf16_value(
+            int(_bf16_bits([c])[0])))), eps=0.0)
+        assert np.array_equal(y, y2)
+    # h = (3, 4, 0, ...): mean square 25/H, so y = (3, 4) * sqrt(H)/5 = (9.6, 12.8) -> nearest bf16 (spacing 1/16 in [8, 16)) 9.625, 12.8125
+    out = np.zeros((1, H), np.float32)
+    out[0, :2] = (3.0, 4.0)
+    y = oracle.residual_rmsnorm(np.zeros((1, H), np.uint16), out, eps=0.0)
+    assert oracle.bf16_value(int(y[0, 0])) == 9.625 and oracle.bf16_value(int(y[0, 1])) == 12.8125
+    assert np.all(y[0, 2:] == 0)
+    # the residual add uses both inputs: x = (3, 0, ...) and out = (0, 4, ...) give the same row
+    x = np.zeros((1, H), np.uint16)
+    x[0, 0] = _bf16_bits([3.0])[0]
+    out = np.zeros((1, H), np.float32)
+    out[0, 1] = 4.0
+    assert np.array_equal(oracle.residual_rmsnorm(x, out, eps=0.0), y)
+    # eps enters under the root: a row of ones with eps = 3 gives 1/sqrt(1 + 3) = 0.5
+    y = oracle.residual_rmsnorm(np.tile(_bf16_bits([1.0]), (1, H)), np.zeros((1, H), np.float32), eps=3.0)
+    assert np.all(y == _bf16_bits([0.5]))
+
+
+def test_residual_rmsnorm_scale_invariant_and_rowwise():
+    rng = np.random.default_rng(3)
+    H = 512
+    x = _bf16_bits(rng.standard_normal((3, H)))
+    out = rng.standard_normal((3, H)).astype(np.float32)
+    y = oracle.residual_rmsnorm(x, out, eps=0.0)
+    # scaling a row's inputs by a power of two leaves the normalised row unchanged (eps = 0)
+    xs = _bf16_bits(np.array([oracle.bf16_value(int(v)) for v in x[1]], np.float32) * 8.0)
+    ys = oracle.residual_rmsnorm(xs[None, :], out[1:2] * 8.0, eps=0.0)
+    assert np.array_equal(ys[0], y[1])
+    # rows are independent
+    assert np.array_equal(oracle.residual_rmsnorm(x[2:3], out[2:3], eps=0.0)[0], y[2])
+
+
+def test_sigmoid_many_is_sigmoid_elementwise():
+    l = np.array([-30.0, -1.5, 0.0, 2.0 ** -20, 7.25, 30.0], np.float32)
+    assert np.array_equal(oracle.sigmoid_many(l), np.array([oracle.sigmoid(float(v)) for v in l], np.float32))
