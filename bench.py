@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--workload", choices=["all", "decode", "prefill", "stack", "batch"], default="all",
                    help="all (default): decode line with prefill, batch and stack nested; or one leg alone")
     p.add_argument("--stack-layers", type=int, default=38, help="layers of the stack workload")
+    p.add_argument("--stack-distinct", type=int, default=4,
+                   help="stack: distinct expert weight sets drawn (placed once per layer at distinct addresses)")
     p.add_argument("--stack-tokens", type=int, default=20,
                    help="distinct tokens captured in the stack graph (steps per replay)")
     p.add_argument("--steps", type=int, default=5)
@@ -117,6 +119,11 @@ def stream_gbs(torch):
     del src, dst
     return {"read_gbs": round(nbytes / min(read_s) / 1e9, 1), "copy_gbs": round(2 * (1 << 30) / min(copy_s) / 1e9, 1),
             "read_kernel": "moe_stream_read, 4 GiB", "copy": "torch copy_, 1 GiB"}
+
+
+def log(msg):
+    """Progress on stderr (the JSON line is the only thing on stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def cpu_info():
@@ -294,9 +301,10 @@ def run_decode(args, check):
     cpu, parity = None, None
     if not args.no_cpu:
         import oracle
+        log("decode: CPU oracle")
         thr = oracle.threads()
         # tokens i < n use distinct layer i % distinct (placement i mod 32): one oracle call per distinct layer
-        n = 128 * distinct
+        n = 64 * distinct
         want = np.empty((n, H), np.float32)
         rid = np.empty((n, K), np.int32)
         rw = np.empty((n, K), np.float32)
@@ -318,7 +326,7 @@ def run_decode(args, check):
         one, _, _ = oracle.layer(x_bits[0:n1:distinct], layers[0]["gate_w"], layers[0]["arena"], layers[0]["shared"],
                                  K, F, shape.routed_scale)
         c1 = time.time() - c0
-        oracle.set_threads(0)
+        oracle.set_threads(thr)
         cpu["single_thread"] = {"value": round((n1 // distinct) / c1, 3), "unit": "tok/s", "cores": 1,
                                 "sample": f"{n1 // distinct} tokens of distinct layer 0, one call"}
         cpu["single_equals_all_cores"] = bool(np.array_equal(one.view(np.uint32),
@@ -432,7 +440,8 @@ def run_prefill(args, check):
     cpu, parity = None, None
     if not args.no_cpu:
         import oracle
-        n = 400
+        log("prefill: CPU oracle")
+        n = 256
         c0 = time.time()
         want, rid, rw = oracle.layer(x_bits[:n], inp["gate_w"], inp["arena"], inp["shared"], K, F,
                                      shape.routed_scale, inp["bias"], oracle.BF16 if prec == qm.PREC_BF16 else
@@ -602,12 +611,27 @@ def run_stack(args, check):
     lam = synth.zipf_lambda(shape)
     cfg = qm.make_config(H, F, E, K, shape.n_shared, shape.routed_scale)
     t0 = time.time()
+    # Router weights and selection biases are drawn per layer (each layer routes differently); expert
+    # weights are drawn for `stack_distinct` layers and placed once per layer at distinct addresses, so
+    # a token streams as many distinct HBM bytes as with 38 distinct draws (drawing 15 GB of IQ4_NL
+    # experts takes minutes on the host).
+    nd = max(1, min(args.stack_distinct, nl))
+    packed = []
+    for d in range(nd):
+        inp = synth.layer_inputs(shape, layer=d, lam=lam)
+        packed.append((inp["arena"], inp["shared"],
+                       qm.DeviceLayer(cfg, inp["gate_w"], None, inp["arena"], inp["shared"])))
+        log(f"stack: expert set {d + 1} of {nd} drawn, {time.time() - t0:.0f} s")
     layers, host = [], []
     for l in range(nl):
-        inp = synth.layer_inputs(shape, layer=l, lam=lam)
-        layers.append(qm.DeviceLayer(cfg, inp["gate_w"], inp["bias"], inp["arena"], inp["shared"]))
-        host.append(inp)
-    torch.cuda.synchronize()
+        arena_h, shared_h, src = packed[l % nd]
+        gate_w = synth.gate_weights(shape, layer=l)
+        bias = synth.zipf_bias(shape, lam, layer=l)
+        layers.append(qm.DeviceLayer.from_packed(cfg, torch.from_numpy(gate_w).to(dev),
+                                                 torch.from_numpy(bias).to(dev), src.arena.clone(),
+                                                 src.shared.clone()))
+        host.append({"gate_w": gate_w, "bias": bias, "arena": arena_h, "shared": shared_h})
+    del packed
     gen_s = time.time() - t0
     S = args.stack_tokens
     x_bits = synth.tokens(shape, S, first=7000)
@@ -662,7 +686,7 @@ def run_stack(args, check):
                 x = xs[l]
         torch.cuda.synchronize()
         # every layer's input and output of the first tokens, for the oracle (eager, same kernels)
-        n_chk = min(S, 16)
+        n_chk = min(S, 8)
         x_in = torch.empty((n_chk, nl, H), dtype=torch.bfloat16, device=dev)
         o_out = torch.empty((n_chk, nl, H), dtype=torch.float32, device=dev)
         for i in range(n_chk):
@@ -697,6 +721,8 @@ def run_stack(args, check):
         rw = np.empty((n_chk, nl, K), np.float32)
         c0 = time.time()
         for l in range(nl):
+            if l % 8 == 0:
+                log(f"stack: CPU oracle layer {l} of {nl}, {time.time() - c0:.0f} s")
             inp = host[l]
             want[:, l], rid[:, l], rw[:, l] = oracle.layer(xin[:, l], inp["gate_w"], inp["arena"], inp["shared"],
                                                            K, F, shape.routed_scale, inp["bias"])
@@ -725,7 +751,9 @@ def run_stack(args, check):
         "config": {"workload": f"{nl}-layer MoE stack decode, T=1: each layer hidden 3584, 64 experts top-4 + 1 "
                                "shared, ffn 1024, IQ4_NL, sigmoid router, scale 2.0; layer input = bf16(rmsnorm("
                                "previous input + previous output)) by one fused kernel; Zipf(1.1) expert popularity",
-                   "layers": nl, "distinct_tokens": S, "zipf_lambda": lam, "graph": True},
+                   "layers": nl, "distinct_tokens": S, "zipf_lambda": lam, "graph": True,
+                   "expert_sets": f"router weights and biases drawn per layer; expert weights drawn for {nd} "
+                                  f"layers, each layer's placed at its own address"},
         "step_spread": spread(np.asarray(per_replay) / S),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("stack_traffic.json"),
@@ -766,10 +794,11 @@ def main():
         line = LEGS[args.workload](args, check)
     else:
         import torch
+        log("decode")
         line = run_decode(args, check)
         torch.cuda.empty_cache()
         for leg in NESTED:
-            print(f"[bench] {leg}", file=sys.stderr, flush=True)
+            log(leg)
             try:
                 line[leg] = brief(LEGS[leg](args, check))
             except Exception as e:  # the line is still printed; the exit status reports it

@@ -80,7 +80,7 @@ def threads() -> int:
 
 
 def set_threads(n: int) -> None:
-    """Threads of the token loop of layer() (0 = the OpenMP default); results do not depend on it."""
+    """Threads of the token loop of layer() (n <= 0 leaves the setting unchanged); results do not depend on it."""
     _load().oracle_set_threads(n)
 
 

@@ -335,8 +335,8 @@ void oracle_sigmoid_many(int64_t n, const float* l, float* s) {
   for (int64_t i = 0; i < n; i++) s[i] = oracle_sigmoid(l[i]);
 }
 
-/* Threads the token loop of oracle_layer may use (OpenMP); 0 keeps the
- * default.  Results do not depend on it. */
+/* Threads the token loop of oracle_layer may use (OpenMP); n <= 0 leaves
+ * the setting unchanged.  Results do not depend on it. */
 void oracle_set_threads(int n) {
 #ifdef _OPENMP
   if (n > 0) omp_set_num_threads(n);

@@ -214,6 +214,14 @@ class DeviceLayer:
             moe_pack_experts(cfg, 1, ssrc, self.shared)
         self._ws = None
 
+    @classmethod
+    def from_packed(cls, cfg: moe_config, gate_w, bias, arena, shared, device="cuda"):
+        """A layer over device tensors already in packed order (moe_pack_experts), used as given."""
+        self = cls.__new__(cls)
+        self.cfg, self.device, self._ws = cfg, device, None
+        self.gate_w, self.bias, self.arena, self.shared = gate_w, bias, arena, shared
+        return self
+
     def workspace(self, T: int):
         import torch
         need = moe_workspace_bytes(self.cfg, T)
