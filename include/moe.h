@@ -218,6 +218,23 @@ moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev
                              float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
                              size_t ws_bytes, hipStream_t stream);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, validation, kernels and
+ * results as moe_layer_forward; the workspace is instead a device array of
+ * 64 MiB inside the library, one per GPU it runs on, held until the process
+ * ends.  Calls whose workspace (moe_workspace_bytes(cfg, T)) exceeds it return
+ * MOE_EWORKSPACE (the Xing4 layer fits up to a few hundred tokens per call).
+ * Allocates nothing: the array's address is looked up once per device, and the
+ * first call on a device also clears its status word (one small kernel on
+ * `stream`).  Every call on one GPU uses that GPU's array: calls that overlap
+ * in time on one GPU (other streams, other threads) race and give undefined
+ * results.  The array keeps the last call's contents. */
+moe_status moe_layer_forward_noalloc(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
+                                     const float* sel_bias_dev, const void* arena_dev, const void* shared_dev,
+                                     float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev,
+                                     hipStream_t stream);
+
 /* ---- measurement ----------------------------------------------------------
  * Not part of the layer: a kernel of known traffic for reporting achieved
  * bandwidth against this GPU's own streaming rate as well as the vendor peak.

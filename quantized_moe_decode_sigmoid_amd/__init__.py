@@ -65,6 +65,7 @@ _SIGS = {
     "moe_bucket": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_expert_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_layer_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_layer_forward_noalloc": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_stream_read": ([_vp, _sz, _vp, _vp], _i32),
     "moe_residual_rmsnorm": ([_vp, _vp, _i32, _i32, ctypes.c_float, _vp, _vp], _i32),
 }
@@ -180,6 +181,14 @@ def moe_layer_forward(cfg, T, x, gate_w, sel_bias, arena, shared, out, topk_ids=
     _check(_lib.moe_layer_forward(ctypes.byref(cfg), T, _p(x), _p(gate_w), _p(sel_bias), _p(arena), _p(shared),
                                   _p(out), _p(topk_ids), _p(topk_w), _p(ws), ws_bytes, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_noalloc(cfg, T, x, gate_w, sel_bias, arena, shared, out, topk_ids=None, topk_w=None,
+                              stream=None):
+    """moe_layer_forward on the library's own per-GPU scratch (no workspace argument, no allocation)."""
+    _check(_lib.moe_layer_forward_noalloc(ctypes.byref(cfg), T, _p(x), _p(gate_w), _p(sel_bias), _p(arena),
+                                          _p(shared), _p(out), _p(topk_ids), _p(topk_w), _stream(stream)),
+           "moe_layer_forward_noalloc")
 
 
 class DeviceLayer:
