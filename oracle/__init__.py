@@ -59,6 +59,7 @@ def _load():
     lib.oracle_bucket.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
     lib.oracle_expert.argtypes = [i32, i32, vp, vp, i32, vp]
     lib.oracle_layer.argtypes = [i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_layer_gated.argtypes = [i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_threads.restype = i32
     lib.oracle_set_threads.argtypes = [i32]
     lib.oracle_sigmoid_many.argtypes = [i64, vp, vp]
@@ -185,20 +186,27 @@ def expert(x_row: np.ndarray, expert_bytes: np.ndarray, hidden: int, ffn: int, m
     return y
 
 
-def layer(x: np.ndarray, gate_w: np.ndarray, arena: np.ndarray, shared: np.ndarray | None,
-          top_k: int, ffn: int, scale: float = 2.0, bias: np.ndarray | None = None, mode: int = FP32):
-    """Whole MoE layer.  Returns (out fp32 [T,H], ids int32 [T,K], weights fp32 [T,K])."""
+def layer(x: np.ndarray, gate_w: np.ndarray, arena: np.ndarray | None, shared: np.ndarray | None,
+          top_k: int, ffn: int, scale: float = 2.0, bias: np.ndarray | None = None, mode: int = FP32,
+          shared_gate: np.ndarray | None = None):
+    """Whole MoE layer.  Returns (out fp32 [T,H], ids int32 [T,K], weights fp32 [T,K]).
+
+    gate_w [E,H] (E may be 0 with top_k 0: a dense FFN block, the shared expert alone);
+    shared_gate fp32 [H] or None: the shared expert is scaled by sigmoid(x . shared_gate)."""
     x = _c(x, np.uint16)
-    gate_w = _c(gate_w, np.float32)
+    T, H = x.shape
+    gate_w = _c(gate_w, np.float32).reshape(-1, H)
     arena = _c(arena, np.uint8)
     shared = _c(shared, np.uint8)
     bias = _c(bias, np.float32)
-    T, H = x.shape
+    sg = _c(shared_gate, np.float32)
     E = gate_w.shape[0]
-    assert arena.size == E * 3 * ffn * H // 32 * 18
+    assert (arena.size if arena is not None else 0) == E * 3 * ffn * H // 32 * 18
+    assert sg is None or sg.size == H
     out = np.empty((T, H), np.float32)
     ids = np.empty((T, top_k), np.int32)
     w = np.empty((T, top_k), np.float32)
-    _load().oracle_layer(T, H, ffn, E, top_k, 1 if shared is not None else 0, scale, mode, _ptr(x), _ptr(gate_w),
-                         _ptr(bias), _ptr(arena), _ptr(shared), _ptr(out), _ptr(ids), _ptr(w))
+    _load().oracle_layer_gated(T, H, ffn, E, top_k, 1 if shared is not None else 0, scale, mode, _ptr(x),
+                               _ptr(gate_w), _ptr(bias), _ptr(sg), _ptr(arena), _ptr(shared), _ptr(out), _ptr(ids),
+                               _ptr(w))
     return out, ids, w

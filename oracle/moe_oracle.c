@@ -288,18 +288,36 @@ void oracle_expert(int H, int F, const uint8_t* expert, const uint16_t* x, int m
 /* ---- whole layer -------------------------------------------------------- */
 
 /* out[t] = sum over slots k (ascending) of w[t][k] * y_{ids[t][k]}(x_t)
- *          + y_shared(x_t)   (when n_shared == 1; weight 1, unscaled),
+ *          + g_t * y_shared(x_t)   (when n_shared == 1),
  * accumulated in double and rounded once to fp32 (design record section 2:
  * the routed + shared sum is carried in fp32 or wider).  Routing as in
  * oracle_route.  arena: E experts back to back, expert_bytes = 3*F*H/32*18.
+ *
+ * The shared expert's weight g_t is 1, or, when shared_gate (an fp32 [H]
+ * row) is given, the sigmoid of its logit: g_t = oracle_sigmoid(x_t . shared_gate)
+ * with the logit in the router's fixed fp32 order -- the sigmoid-gated shared
+ * expert (the research log's shared_expert_gate GEMV, "Where decode time
+ * actually goes"; an fp32 GEMV of width H like the router's, its fourth
+ * section's ffn_gate_inp_shexp).  Read as: the same sigmoid as the routed
+ * scores, no normalisation, no routed_scale.
+ *
+ * E == 0 with K == 0 and n_shared == 1 is a dense FFN block (model card,
+ * "Model and routing": hidden / dense FFN / expert FFN 3584 / 9216 / 1024, the
+ * two leading dense blocks): no routing, out[t] = y_shared(x_t).
  * ids_out / w_out may be NULL. */
-void oracle_layer(int T, int H, int F, int E, int K, int n_shared, float scale, int mode,
-                  const uint16_t* x, const float* Wg, const float* bias, const uint8_t* arena,
-                  const uint8_t* shared, float* out, int32_t* ids_out, float* w_out) {
+void oracle_layer_gated(int T, int H, int F, int E, int K, int n_shared, float scale, int mode,
+                        const uint16_t* x, const float* Wg, const float* bias, const float* shared_gate,
+                        const uint8_t* arena, const uint8_t* shared, float* out, int32_t* ids_out,
+                        float* w_out) {
   const int64_t eb = 3 * (int64_t)F * (H / 32) * 18;
-  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)T * K);
-  float* w = (float*)malloc(sizeof(float) * (size_t)T * K);
-  oracle_route(T, H, E, K, scale, x, Wg, bias, ids, w, NULL, NULL);
+  int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
+  float* w = (float*)malloc(sizeof(float) * ((size_t)T * K + 1));
+  float* g = (float*)malloc(sizeof(float) * ((size_t)T + 1));
+  if (K > 0) oracle_route(T, H, E, K, scale, x, Wg, bias, ids, w, NULL, NULL);
+  if (shared_gate) {
+    oracle_router_logits(T, H, 1, x, shared_gate, g);
+    for (int t = 0; t < T; t++) g[t] = oracle_sigmoid(g[t]);
+  }
   /* tokens are independent: the threads split them, each token's sum is
    * formed in the same order whatever the thread count */
 #pragma omp parallel for schedule(dynamic, 1)
@@ -315,17 +333,26 @@ void oracle_layer(int T, int H, int F, int E, int K, int n_shared, float scale, 
       for (int n = 0; n < H; n++) acc[n] += wk * y[n];
     }
     if (n_shared) {
+      const double gs = shared_gate ? (double)g[t] : 1.0;
       oracle_expert(H, F, shared, xt, mode, y);
-      for (int n = 0; n < H; n++) acc[n] += y[n];
+      for (int n = 0; n < H; n++) acc[n] += gs * y[n];
     }
     for (int n = 0; n < H; n++) out[(int64_t)t * H + n] = (float)acc[n];
     free(acc);
     free(y);
   }
-  if (ids_out) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)T * K);
-  if (w_out) memcpy(w_out, w, sizeof(float) * (size_t)T * K);
+  if (ids_out && K > 0) memcpy(ids_out, ids, sizeof(int32_t) * (size_t)T * K);
+  if (w_out && K > 0) memcpy(w_out, w, sizeof(float) * (size_t)T * K);
   free(ids);
   free(w);
+  free(g);
+}
+
+/* The layer with an ungated shared expert (weight 1). */
+void oracle_layer(int T, int H, int F, int E, int K, int n_shared, float scale, int mode,
+                  const uint16_t* x, const float* Wg, const float* bias, const uint8_t* arena,
+                  const uint8_t* shared, float* out, int32_t* ids_out, float* w_out) {
+  oracle_layer_gated(T, H, F, E, K, n_shared, scale, mode, x, Wg, bias, NULL, arena, shared, out, ids_out, w_out);
 }
 
 /* ---- helpers for the test suite and the benchmark's CPU leg ------------ */

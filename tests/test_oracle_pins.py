@@ -519,3 +519,54 @@ def test_residual_rmsnorm_scale_invariant_and_rowwise():
 def test_sigmoid_many_is_sigmoid_elementwise():
     l = np.array([-30.0, -1.5, 0.0, 2.0 ** -20, 7.25, 30.0], np.float32)
     assert np.array_equal(oracle.sigmoid_many(l), np.array([oracle.sigmoid(float(v)) for v in l], np.float32))
+
+
+# ---------------------------------------------------------------- sigmoid-gated shared expert, dense block
+
+def test_shared_gate_closed_forms():
+    """The shared expert scaled by sigmoid(x . g): g = 0 gives exactly 1/2; g = +x gives a logit of about
+    +H (sigmoid rounds to 1: the ungated layer, bit for bit); g = -x a logit below -200 (sigmoid is 0: the
+    layer without a shared expert, bit for bit); in between, the dense masked brute force with the gate."""
+    s, inp, x = _tiny()
+    base, ids, w = oracle.layer(x, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn)
+    routed, _, _ = oracle.layer(x, inp["gate_w"], inp["arena"], None, s.top_k, s.ffn)
+    for t in range(s.tokens):
+        xf = bf16_bits_to_f64(x[t]).astype(np.float32)
+        up, _, _ = oracle.layer(x[t:t + 1], inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn,
+                                shared_gate=xf)
+        assert np.array_equal(up[0].view(np.uint32), base[t].view(np.uint32))
+        down, _, _ = oracle.layer(x[t:t + 1], inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn,
+                                  shared_gate=-xf)
+        assert np.array_equal(down[0].view(np.uint32), routed[t].view(np.uint32))
+    half, hid, hw = oracle.layer(x, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn,
+                                 shared_gate=np.zeros(s.hidden, np.float32))
+    assert np.array_equal(hid, ids) and np.array_equal(hw, w)  # the gate does not touch the routing
+    eb = s.expert_bytes
+    rng = np.random.default_rng(8)
+    g = (rng.standard_normal(s.hidden) * 0.05).astype(np.float32)
+    gated, _, _ = oracle.layer(x, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn, shared_gate=g)
+    for t in range(s.tokens):
+        ysh = np_expert(x[t], inp["shared"], s.hidden, s.ffn)
+        yr = sum(float(w[t, k]) * np_expert(x[t], inp["arena"][ids[t, k] * eb:(ids[t, k] + 1) * eb], s.hidden,
+                                            s.ffn) for k in range(s.top_k))
+        assert np.allclose(half[t], yr + 0.5 * ysh, rtol=2 ** -22, atol=1e-12)
+        # the gate logit: the exact dot of the bf16 token with the fp32 row, within the fp32 dot bound
+        exact = float(sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(bf16_bits_to_f64(x[t]), g)))
+        sg = 1.0 / (1.0 + math.exp(-exact))
+        assert np.allclose(gated[t], yr + sg * ysh, rtol=1e-6, atol=1e-9)
+
+
+def test_dense_block_is_the_shared_ffn_alone():
+    """E = 0, K = 0, one always-on expert: the dense FFN block, out = FFN(x) per token (the expert FFN
+    itself is pinned above against an independent decode and closed forms)."""
+    s, inp, x = _tiny()
+    out, ids, w = oracle.layer(x, np.zeros((0, s.hidden), np.float32), None, inp["shared"], 0, s.ffn)
+    assert ids.shape == (s.tokens, 0)
+    for t in range(s.tokens):
+        want = oracle.expert(x[t], inp["shared"], s.hidden, s.ffn).astype(np.float32)
+        assert np.array_equal(out[t].view(np.uint32), want.view(np.uint32))
+    outb, _, _ = oracle.layer(x, np.zeros((0, s.hidden), np.float32), None, inp["shared"], 0, s.ffn,
+                              mode=oracle.BF16)
+    for t in range(s.tokens):
+        want = oracle.expert(x[t], inp["shared"], s.hidden, s.ffn, oracle.BF16).astype(np.float32)
+        assert np.array_equal(outb[t].view(np.uint32), want.view(np.uint32))
