@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum {
@@ -70,21 +70,37 @@ typedef enum {
  *       product silu(g)*u is rounded to bf16 before the down projection;
  *       products run on bf16 MFMA with fp32 accumulation (batched / prefill
  *       calls: tiles of up to 128 routes of one expert).
- * AUTO: FP32 when T*K <= 16*E (at most 16 routes per expert on average),
- *       else BF16.  The router and the combine are fp32 in every mode. */
+ * AUTO: FP32 when T*K <= 16*E (at most 16 routes per expert on average;
+ *       for a dense block, T <= 16), else BF16.  The router and the combine are fp32 in every mode. */
 typedef enum { MOE_PREC_AUTO = 0, MOE_PREC_FP32 = 1, MOE_PREC_BF16 = 2 } moe_precision;
 
 /* Layer shape.  Supported: hidden % 256 == 0, ffn % 128 == 0,
  * 1 <= n_experts <= 256, 1 <= top_k <= min(n_experts, 8), n_shared in {0, 1},
- * routed_scale finite.  Tokens per call: 0 <= T <= 65536. */
+ * routed_scale finite.  Tokens per call: 0 <= T <= 65536.
+ *
+ * shared_gate = 1 (needs n_shared = 1): the shared expert's output is scaled
+ * by g_t = sigmoid(x_t . gate_w[E]) -- a sigmoid-gated shared expert (the
+ * FlashNext research log's shared_expert_gate, "Where decode time actually
+ * goes") -- instead of 1.  gate_w then has E + 1 rows, row E being the gate;
+ * its logit and sigmoid are computed exactly like the routed scores (fixed
+ * fp32 order, see moe_route) and the routing weights carry it as one more
+ * value per token: topk_w is [T][K + 1] with topk_w[t][K] = g_t.
+ *
+ * n_experts = 0 (with top_k = 0, n_shared = 1, shared_gate = 0) is a dense
+ * FFN block (model card "Model and routing": the two leading dense blocks,
+ * hidden / dense FFN 3584 / 9216): out[t] = FFN(x_t) with the one always-on
+ * expert's weights in shared_dev; no router weight, routing or arena is read
+ * (those pointers may be NULL) and moe_route / moe_bucket / moe_router_scores
+ * refuse it (MOE_EINVAL). */
 typedef struct {
-  int32_t hidden;     /* H: model width */
-  int32_t ffn;        /* F: expert intermediate width */
-  int32_t n_experts;  /* E: routed experts */
-  int32_t top_k;      /* K: experts per token */
-  int32_t n_shared;   /* shared experts (0 or 1) */
-  float routed_scale; /* multiplies the normalised routed weights (2.0) */
-  int32_t precision;  /* moe_precision */
+  int32_t hidden;      /* H: model width */
+  int32_t ffn;         /* F: expert intermediate width */
+  int32_t n_experts;   /* E: routed experts (0: a dense FFN block) */
+  int32_t top_k;       /* K: experts per token */
+  int32_t n_shared;    /* shared experts (0 or 1) */
+  float routed_scale;  /* multiplies the normalised routed weights (2.0) */
+  int32_t precision;   /* moe_precision */
+  int32_t shared_gate; /* 1: the shared expert is scaled by sigmoid(x . gate_w[E]); 0: weight 1 */
 } moe_config;
 
 /* ---- queries (host only, no GPU work) ----------------------------------- */

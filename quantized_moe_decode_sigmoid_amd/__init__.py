@@ -29,12 +29,17 @@ class MoeError(RuntimeError):
 class moe_config(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("routed_scale", ctypes.c_float),
-                ("precision", ctypes.c_int32)]
+                ("precision", ctypes.c_int32), ("shared_gate", ctypes.c_int32)]
 
 
 def make_config(hidden: int, ffn: int, n_experts: int, top_k: int, n_shared: int = 1,
-                routed_scale: float = 2.0, precision: int = PREC_AUTO) -> moe_config:
-    return moe_config(hidden, ffn, n_experts, top_k, n_shared, routed_scale, precision)
+                routed_scale: float = 2.0, precision: int = PREC_AUTO, shared_gate: int = 0) -> moe_config:
+    return moe_config(hidden, ffn, n_experts, top_k, n_shared, routed_scale, precision, shared_gate)
+
+
+def weight_cols(cfg: moe_config) -> int:
+    """Values per token row of the routing weights: K, plus the shared expert's gate when it is gated."""
+    return cfg.top_k + cfg.shared_gate
 
 
 if not os.path.exists(LIB_PATH):
@@ -194,9 +199,10 @@ def moe_layer_forward_noalloc(cfg, T, x, gate_w, sel_bias, arena, shared, out, t
 class DeviceLayer:
     """Device copies of one layer's weights, the expert arena packed by moe_pack_experts.
 
-    gate_w fp32 [E, H], bias fp32 [E] or None, arena / shared uint8 in GGUF block order
-    (numpy or torch).  ``forward`` allocates the outputs and workspace with torch and
-    calls moe_layer_forward.
+    gate_w fp32 [E + shared_gate, H] (row E: the shared expert's gate), bias fp32 [E] or None,
+    arena / shared uint8 in GGUF block order (numpy or torch); a dense block (E = 0) has no
+    gate_w, bias or arena (None).  ``forward`` allocates the outputs and workspace with torch
+    and calls moe_layer_forward.
     """
 
     def __init__(self, cfg: moe_config, gate_w, bias, arena, shared, device="cuda"):
@@ -208,13 +214,17 @@ class DeviceLayer:
 
         self.cfg = cfg
         self.device = device
-        self.gate_w = dev(gate_w, torch.float32)
+        self.gate_w = None if gate_w is None or cfg.n_experts == 0 else dev(gate_w, torch.float32)
+        if self.gate_w is not None:
+            assert self.gate_w.shape[0] == cfg.n_experts + cfg.shared_gate
         self.bias = None if bias is None else dev(bias, torch.float32)
         eb = moe_expert_bytes(cfg)
-        src = dev(arena, torch.uint8)
-        assert src.numel() == eb * cfg.n_experts
-        self.arena = torch.empty_like(src)
-        moe_pack_experts(cfg, cfg.n_experts, src, self.arena)
+        self.arena = None
+        if cfg.n_experts:
+            src = dev(arena, torch.uint8)
+            assert src.numel() == eb * cfg.n_experts
+            self.arena = torch.empty_like(src)
+            moe_pack_experts(cfg, cfg.n_experts, src, self.arena)
         self.shared = None
         if cfg.n_shared:
             ssrc = dev(shared, torch.uint8)

@@ -23,21 +23,35 @@ size_t align_up(size_t v) { return (v + 255) & ~size_t(255); }
 
 moe_status check_cfg(const moe_config* c) {
   if (!c) return MOE_EINVAL;
-  if (c->hidden <= 0 || c->ffn <= 0 || c->n_experts <= 0 || c->top_k <= 0) return MOE_EINVAL;
+  if (c->hidden <= 0 || c->ffn <= 0 || c->n_experts < 0 || c->top_k < 0) return MOE_EINVAL;
   if (c->n_shared != 0 && c->n_shared != 1) return MOE_EUNSUPPORTED;
+  if (c->shared_gate != 0 && c->shared_gate != 1) return MOE_EINVAL;
   if (c->hidden % 256 != 0 || c->hidden > kMaxHidden) return MOE_EUNSUPPORTED;
   if (c->ffn % 128 != 0 || c->ffn > 65536) return MOE_EUNSUPPORTED;
   if (c->n_experts > 256) return MOE_EUNSUPPORTED;
-  if (c->top_k > 8 || c->top_k > c->n_experts) return MOE_EUNSUPPORTED;
+  if (c->n_experts == 0) {
+    // a dense FFN block: the always-on expert alone, nothing to route or gate
+    if (c->top_k != 0 || c->n_shared != 1 || c->shared_gate != 0) return MOE_EUNSUPPORTED;
+  } else {
+    if (c->top_k == 0) return MOE_EINVAL;
+    if (c->top_k > 8 || c->top_k > c->n_experts) return MOE_EUNSUPPORTED;
+    if (c->shared_gate && !c->n_shared) return MOE_EUNSUPPORTED;
+  }
   if (!isfinite(c->routed_scale)) return MOE_EINVAL;
   if (c->precision < MOE_PREC_AUTO || c->precision > MOE_PREC_BF16) return MOE_EINVAL;
   return MOE_OK;
 }
 
+// AUTO: the exact-weight contract while an expert serves at most 16 routes on
+// average (a dense block: its one expert at most 16 tokens), else bf16 tiles.
 int resolve_precision(const moe_config* c, int T) {
   if (c->precision != MOE_PREC_AUTO) return c->precision;
+  if (c->n_experts == 0) return T <= 16 ? MOE_PREC_FP32 : MOE_PREC_BF16;
   return (int64_t)T * c->top_k <= 16 * (int64_t)c->n_experts ? MOE_PREC_FP32 : MOE_PREC_BF16;
 }
+
+// Values per row of the routing weights: K, plus the shared expert's gate.
+int weight_cols(const moe_config* c) { return c->top_k + c->shared_gate; }
 
 int64_t expert_bytes(const moe_config* c) { return 3 * (int64_t)c->ffn * (c->hidden / 32) * 18; }
 
@@ -58,7 +72,7 @@ int max_chunks(const moe_config* c, int T) { return max_chunks(c, T, chunk_rows(
 // Its second kernel hands data between workgroups, so it is taken only when
 // the device holds that kernel's whole grid at once.
 bool decode_path(const moe_config* c, int T) {
-  return T == 1 && c->top_k <= qmoe::kMaxDecodeK && c->ffn <= qmoe::kMaxDecodeFfn &&
+  return T == 1 && c->n_experts > 0 && c->top_k <= qmoe::kMaxDecodeK && c->ffn <= qmoe::kMaxDecodeFfn &&
          c->hidden <= qmoe::kMaxDecodeHidden && resolve_precision(c, T) == MOE_PREC_FP32 &&
          qmoe::decode_grid_coresident(c->ffn, c->top_k, c->hidden, c->n_shared);
 }
@@ -85,9 +99,9 @@ Plan make_plan(const moe_config* c, int T) {
   };
   p.status = take(4);
   p.hw = take((size_t)(c->top_k + 1) * F * 4);
-  p.scores = take((size_t)T * E * 4);
+  p.scores = take((size_t)T * (E + c->shared_gate) * 4);
   p.ids = take(R * 4);
-  p.w = take(R * 4);
+  p.w = take((size_t)T * weight_cols(c) * 4);
   p.counts = take(E * 4);
   p.offsets = take((E + 1) * 4);
   p.perm = take(R * 4);
@@ -146,12 +160,12 @@ moe_status run_expert_forward(const moe_config* cfg, int32_t T, const void* x, c
                                    at<qmoe::Chunk>(ws, p.chunks), at<int32_t>(ws, p.n_chunks), stream)));
   if (prec == MOE_PREC_BF16)
     return launched(qmoe::launch_ffn_bf16(
-        static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, max_chunks(cfg, T),
+        static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, cfg->shared_gate, max_chunks(cfg, T),
         static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
         at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks),
         at<int32_t>(ws, p.n_chunks), at<uint16_t>(ws, p.h_hi), at<float>(ws, p.y), out, stream));
   return launched(qmoe::launch_ffn_exact(
-      static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, max_chunks(cfg, T),
+      static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, cfg->shared_gate, max_chunks(cfg, T),
       static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
       at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks), at<int32_t>(ws, p.n_chunks),
       at<uint16_t>(ws, p.h_hi), at<uint16_t>(ws, p.h_lo), at<float>(ws, p.y), out, stream));
@@ -260,6 +274,7 @@ MOE_API moe_status moe_route(const moe_config* cfg, int32_t T, const void* x_dev
                              const float* sel_bias_dev, int32_t* topk_ids_dev, float* topk_w_dev, void* ws_dev,
                              size_t ws_bytes, hipStream_t stream) {
   TRY(check_common(cfg, T));
+  if (cfg->n_experts == 0) return MOE_EINVAL;  // a dense block has nothing to route
   if (T == 0) return MOE_OK;  // nothing to read or write
   TRY(need(x_dev));
   TRY(need(gate_w_dev));
@@ -270,24 +285,26 @@ MOE_API moe_status moe_route(const moe_config* cfg, int32_t T, const void* x_dev
   const Plan p = make_plan(cfg, T);
   if (ws_bytes < p.total) return MOE_EWORKSPACE;
   return launched(qmoe::launch_router(static_cast<const uint16_t*>(x_dev), gate_w_dev, sel_bias_dev, T, cfg->hidden,
-                                      cfg->n_experts, cfg->top_k, cfg->routed_scale, at<float>(ws_dev, p.scores),
-                                      topk_ids_dev, topk_w_dev, stream));
+                                      cfg->n_experts, cfg->top_k, cfg->shared_gate, cfg->routed_scale,
+                                      at<float>(ws_dev, p.scores), topk_ids_dev, topk_w_dev, stream));
 }
 
 MOE_API moe_status moe_router_scores(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
                                      float* scores_dev, hipStream_t stream) {
   TRY(check_common(cfg, T));
+  if (cfg->n_experts == 0) return MOE_EINVAL;
   if (T == 0) return MOE_OK;
   TRY(need(x_dev));
   TRY(need(gate_w_dev));
   TRY(need(scores_dev));
   return launched(qmoe::launch_router_scores(static_cast<const uint16_t*>(x_dev), gate_w_dev, T, cfg->hidden,
-                                             cfg->n_experts, scores_dev, stream));
+                                             cfg->n_experts + cfg->shared_gate, scores_dev, stream));
 }
 
 MOE_API moe_status moe_bucket(const moe_config* cfg, int32_t T, const int32_t* topk_ids_dev, int32_t* counts_dev,
                               int32_t* offsets_dev, int32_t* perm_dev, int32_t* pos_dev, hipStream_t stream) {
   TRY(check_common(cfg, T));
+  if (cfg->n_experts == 0) return MOE_EINVAL;
   TRY(need(counts_dev));
   TRY(need(offsets_dev));
   if (T > 0) {  // with no routes only the (all-zero) counts and offsets are written
@@ -305,9 +322,11 @@ MOE_API moe_status moe_expert_forward(const moe_config* cfg, int32_t T, const vo
   TRY(check_common(cfg, T));
   if (T == 0) return MOE_OK;  // nothing to read or write
   TRY(need(x_dev));
-  TRY(need(topk_ids_dev));
-  TRY(need(topk_w_dev));
-  TRY(need(arena_dev));
+  if (cfg->n_experts > 0) {  // a dense block reads no routing and no routed arena
+    TRY(need(topk_ids_dev));
+    TRY(need(topk_w_dev));
+    TRY(need(arena_dev));
+  }
   if (cfg->n_shared) TRY(need(shared_dev));
   TRY(need(out_dev));
   TRY(need(ws_dev));
@@ -321,10 +340,13 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const voi
                                      size_t ws_bytes, hipStream_t stream) {
   TRY(check_common(cfg, T));
   if (T == 0) return MOE_OK;  // nothing to read or write
+  const bool dense = cfg->n_experts == 0;
   TRY(need(x_dev));
-  TRY(need(gate_w_dev));
-  TRY(optional_ptr(sel_bias_dev));
-  TRY(need(arena_dev));
+  if (!dense) {
+    TRY(need(gate_w_dev));
+    TRY(optional_ptr(sel_bias_dev));
+    TRY(need(arena_dev));
+  }
   if (cfg->n_shared) TRY(need(shared_dev));
   TRY(need(out_dev));
   TRY(optional_ptr(topk_ids_out_dev));
@@ -332,7 +354,8 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const voi
   TRY(need(ws_dev));
   const Plan p = make_plan(cfg, T);
   if (ws_bytes < p.total) return MOE_EWORKSPACE;
-  if (T == 0) return MOE_OK;
+  if (dense)
+    return run_expert_forward(cfg, T, x_dev, nullptr, nullptr, nullptr, shared_dev, out_dev, ws_dev, stream);
   int32_t* ids = topk_ids_out_dev ? topk_ids_out_dev : at<int32_t>(ws_dev, p.ids);
   float* w = topk_w_out_dev ? topk_w_out_dev : at<float>(ws_dev, p.w);
   if (decode_path(cfg, T)) {
@@ -348,6 +371,7 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const voi
     a.E = cfg->n_experts;
     a.K = cfg->top_k;
     a.n_shared = cfg->n_shared;
+    a.gated = cfg->shared_gate;
     a.scale = cfg->routed_scale;
     a.scores = at<float>(ws_dev, p.scores);
     a.ids = ids;
@@ -358,7 +382,7 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const voi
     return launched(qmoe::launch_layer_decode(a, stream));
   }
   TRY(launched(qmoe::launch_router(static_cast<const uint16_t*>(x_dev), gate_w_dev, sel_bias_dev, T, cfg->hidden,
-                                   cfg->n_experts, cfg->top_k, cfg->routed_scale, at<float>(ws_dev, p.scores), ids, w,
-                                   stream)));
+                                   cfg->n_experts, cfg->top_k, cfg->shared_gate, cfg->routed_scale,
+                                   at<float>(ws_dev, p.scores), ids, w, stream)));
   return run_expert_forward(cfg, T, x_dev, ids, w, arena_dev, shared_dev, out_dev, ws_dev, stream);
 }

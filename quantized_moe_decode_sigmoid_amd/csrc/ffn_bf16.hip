@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kBfThreads) void k_down_bf16(
 
 // ---------------------------------------------------------------- launcher
 
-hipError_t launch_ffn_bf16(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_tiles,
+hipError_t launch_ffn_bf16(const uint16_t* x, int T, int H, int F, int K, int n_shared, int gated, int max_tiles,
                            const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
                            const int32_t* pos, const float* w, const Chunk* tiles, const int32_t* n_tiles,
                            uint16_t* h, float* y, float* out, hipStream_t stream) {
@@ -383,7 +383,7 @@ hipError_t launch_ffn_bf16(const uint16_t* x, int T, int H, int F, int K, int n_
                      arena, shared, expert_bytes, tiles, n_tiles, max_tiles, h, y);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_combine(y, pos, w, T, K, H, n_shared, out, stream);
+  return launch_combine(y, pos, w, T, K, H, n_shared, gated, out, stream);
 }
 
 }  // namespace qmoe

@@ -414,17 +414,19 @@ __global__ __launch_bounds__(kExThreads) __attribute__((amdgpu_waves_per_eu(4)))
 
 // ---------------------------------------------------------------- combine
 
-// out[t][n] = sum_k w[t][k] * y[pos[t*K+k]][n]  (slot order)  + y[TK + t][n]
+// out[t][n] = sum_k w[t][k] * y[pos[t*K+k]][n]  (slot order)  + g_t * y[TK + t][n],
+// w rows of K + gated values, g_t = w[t][K] for a gated shared expert, else 1.
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, const int32_t* __restrict__ pos,
                                                  const float* __restrict__ w, int T, int K, int H, int n_shared,
-                                                 float* __restrict__ out) {
+                                                 int gated, float* __restrict__ out) {
   const int t = blockIdx.y;
   const int n = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
   if (n >= H) return;
   const int TK = T * K;
+  const int WK = K + gated;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < K; k++) {
-    const float wk = w[(size_t)t * K + k];
+    const float wk = w[(size_t)t * WK + k];
     const float4 v = *reinterpret_cast<const float4*>(y + (size_t)pos[(size_t)t * K + k] * H + n);
     acc.x = __builtin_fmaf(wk, v.x, acc.x);
     acc.y = __builtin_fmaf(wk, v.y, acc.y);
@@ -433,10 +435,18 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ y, co
   }
   if (n_shared) {
     const float4 v = *reinterpret_cast<const float4*>(y + ((size_t)TK + t) * H + n);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+    if (gated) {
+      const float g = w[(size_t)t * WK + K];
+      acc.x = __builtin_fmaf(g, v.x, acc.x);
+      acc.y = __builtin_fmaf(g, v.y, acc.y);
+      acc.z = __builtin_fmaf(g, v.z, acc.z);
+      acc.w = __builtin_fmaf(g, v.w, acc.w);
+    } else {
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
   }
   *reinterpret_cast<float4*>(out + (size_t)t * H + n) = acc;
 }
@@ -471,7 +481,7 @@ hipError_t launch_dequant(const uint8_t* mat, int rows, int cols, int bf16, floa
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_chunks,
+hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n_shared, int gated, int max_chunks,
                             const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
                             const int32_t* pos, const float* w, const Chunk* chunks, const int32_t* n_chunks,
                             uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream) {
@@ -486,14 +496,14 @@ hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n
                      H, F, K, T, arena, shared, expert_bytes, chunks, n_chunks, h_hi, h_lo, y);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  return launch_combine(y, pos, w, T, K, H, n_shared, out, stream);
+  return launch_combine(y, pos, w, T, K, H, n_shared, gated, out, stream);
 }
 
 hipError_t launch_combine(const float* y, const int32_t* pos, const float* w, int T, int K, int H, int n_shared,
-                          float* out, hipStream_t stream) {
+                          int gated, float* out, hipStream_t stream) {
   clear_last_error();
   hipLaunchKernelGGL(k_combine, dim3((unsigned)((H / 4 + 255) / 256), (unsigned)T), dim3(256), 0, stream, y, pos, w, T,
-                     K, H, n_shared, out);
+                     K, H, n_shared, gated, out);
   return hipGetLastError();
 }
 

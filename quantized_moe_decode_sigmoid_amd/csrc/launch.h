@@ -12,8 +12,10 @@ namespace qmoe {
 hipError_t launch_router_scores(const uint16_t* x, const float* wg, int T, int H, int E, float* scores,
                                 hipStream_t stream);
 
+// Scores of E + gated router rows ([T][E + gated] in scores_ws), top-K of the
+// first E into ids [T][K] and w [T][K + gated] (w[t][K] = the gate's score).
 hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
-                         float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream);
+                         int gated, float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream);
 
 // chunk_rows: routes per work chunk (16 for the exact-weight kernels, kBfRows for the bf16 kernels)
 hipError_t launch_bucket(const int32_t* ids, int T, int K, int E, int n_shared, int chunk_rows, int32_t* counts,
@@ -24,19 +26,21 @@ hipError_t launch_pack(const uint8_t* src, uint8_t* dst, int n_experts, int H, i
 
 hipError_t launch_dequant(const uint8_t* mat, int rows, int cols, int bf16, float* out, hipStream_t stream);
 
+// out[t] = sum_k w[t][k] y[pos[t K + k]] + g_t y[T K + t]; w rows of K + gated
+// values, g_t = w[t][K] when gated, else 1.
 hipError_t launch_combine(const float* y, const int32_t* pos, const float* w, int T, int K, int H, int n_shared,
-                          float* out, hipStream_t stream);
+                          int gated, float* out, hipStream_t stream);
 
 // ---- bf16 grouped MFMA path (ffn_bf16.hip)
 
 constexpr int kBfRows = 128;  // routes per tile
 
-hipError_t launch_ffn_bf16(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_tiles,
+hipError_t launch_ffn_bf16(const uint16_t* x, int T, int H, int F, int K, int n_shared, int gated, int max_tiles,
                            const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
                            const int32_t* pos, const float* w, const Chunk* tiles, const int32_t* n_tiles,
                            uint16_t* h, float* y, float* out, hipStream_t stream);
 
-hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n_shared, int max_chunks,
+hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n_shared, int gated, int max_chunks,
                             const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
                             const int32_t* pos, const float* w, const Chunk* chunks, const int32_t* n_chunks,
                             uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream);
@@ -55,10 +59,11 @@ struct DecodeArgs {
   const uint8_t* shared;
   int64_t expert_bytes;
   int H, F, E, K, n_shared;
+  int gated;           // the shared expert scaled by the sigmoid of router row E
   float scale;
-  float* scores;       // [E] sigmoid scores (first kernel -> second)
+  float* scores;       // [E + gated] sigmoid scores (first kernel -> second)
   int32_t* ids;        // [K] routing outputs
-  float* w;            // [K]
+  float* w;            // [K + gated]
   uint32_t* hw;        // [(K + 1) * F] h words: bf16(h) | bf16(h - bf16(h)) << 16
   float* out;          // [H]
   uint32_t* err;       // set to 1 if a wait gave up

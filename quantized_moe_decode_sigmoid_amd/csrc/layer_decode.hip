@@ -5,8 +5,9 @@
 // for latency.  Routing is bit-identical to it; the FFN sums are split over
 // 8 wavefronts per row tile instead of 4, so outputs agree to fp32 rounding:
 //
-//   k_decode_scores   one wavefront (workgroup) per expert: fp32 logit and
-//                     sigmoid score.
+//   k_decode_scores   one wavefront (workgroup) per router row: fp32 logit and
+//                     sigmoid score (row E: the shared expert's gate, when
+//                     the shared expert is sigmoid-gated).
 //                     It also writes the "not ready" pattern into the words
 //                     through which the next kernel hands h from its gate/up
 //                     workgroups to its down workgroups; the previous token's
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(64) void k_decode_scores(DecodeArgs a) {
   // reset the h hand-off words of k_decode_experts
   const int n_words = (a.K + 1) * a.F;
   for (int i = blockIdx.x * 64 + threadIdx.x; i < n_words; i += gridDim.x * 64) a.hw[i] = kNotReady;
-  if (e < a.E) {
+  if (e < a.E + a.gated) {  // row E: the shared expert's gate
     float4 w[MMAX];
     load_router_row<MMAX>(a.wg + (size_t)e * a.H, a.H, lane, w);
     const float p = router_logit<MMAX>(a.x, a.H, lane, w);
@@ -387,8 +388,10 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
     return ex + 2 * mat_bytes + (int64_t)rtile * nkg * kTileBytes;
   };
   u32x4 nib[kDnSlots];
-  // 1. the router scores, then the shared expert's tiles (they need no routing)
+  // 1. the router scores (and the shared expert's gate), then the shared
+  //    expert's tiles (they need no routing)
   const RouteIn rin = route_fetch(a);
+  const float gate = a.gated ? a.scores[a.E] : 1.0f;
   const uint8_t* shx = a.n_shared ? a.shared : a.arena;
   nib[kMaxDecodeK] = ld16(down_tiles(shx, rt) + (int64_t)kgc * kTileBytes + 16 * lane);
   if (wave < 2) dma_slot_scales(d, down_tiles(shx, 2 * blk), nkg, kMaxDecodeK, wave);
@@ -430,14 +433,15 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
     const int row = threadIdx.x;
     float acc = 0.0f;
     for (int k = 0; k < a.K; k++) acc = __builtin_fmaf(r.w[k], d.y[k][row], acc);
-    if (a.n_shared) acc += d.y[kMaxDecodeK][row];
+    if (a.n_shared) acc = a.gated ? __builtin_fmaf(gate, d.y[kMaxDecodeK][row], acc) : acc + d.y[kMaxDecodeK][row];
     a.out[32 * blk + row] = acc;
   }
-  // the routing outputs, written once
+  // the routing outputs, written once (w[K]: the shared expert's gate)
   if (blk == 0 && (int)threadIdx.x < a.K) {
     a.ids[threadIdx.x] = r.ids[threadIdx.x];
     a.w[threadIdx.x] = r.w[threadIdx.x];
   }
+  if (blk == 0 && a.gated && (int)threadIdx.x == a.K) a.w[a.K] = gate;
 }
 
 // ---------------------------------------------------------------- kernel 2: experts
@@ -495,7 +499,7 @@ bool decode_grid_coresident(int F, int K, int H, int n_shared) {
 }
 
 hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream) {
-  a.n_router = a.E;  // one wavefront per expert
+  a.n_router = a.E + a.gated;  // one wavefront per router row
   a.n_shared_wg = a.n_shared ? a.F / 16 : 0;
   a.n_routed_wg = a.K * (a.F / 16);
   a.n_down_wg = a.H / 32;

@@ -87,7 +87,8 @@ MOE_API moe_status moe_layer_forward_noalloc(const moe_config* cfg, int32_t T, c
   };
   const void* args[] = {x_dev, gate_w_dev, sel_bias_dev, arena_dev, shared_dev, out_dev, topk_ids_out_dev,
                         topk_w_out_dev};
-  const bool required[] = {true, true, false, true, cfg->n_shared != 0, true, false, false};
+  const bool routed = cfg->n_experts > 0;  // a dense block reads no router weight or arena
+  const bool required[] = {true, routed, false, routed, cfg->n_shared != 0, true, false, false};
   for (int i = 0; i < 8; i++) {
     const moe_status s = bad(args[i], required[i]);
     if (s != MOE_OK) return s;

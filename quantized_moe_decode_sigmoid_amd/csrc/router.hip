@@ -197,14 +197,16 @@ void launch_router_tiled(const uint16_t* x, const float* wg, int T, int H, int E
   hipLaunchKernelGGL((k_router_scores_tiled<TT, TE>), grid, dim3(256), 0, stream, x, wg, T, H, E, scores_ws);
 }
 
-// One wavefront per token.
+// One wavefront per token.  scores rows hold E + gated values (the last one
+// the shared expert's gate); weight rows K + gated.
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, const float* __restrict__ bias, int T,
-                                              int E, int K, float scale, int32_t* __restrict__ ids,
+                                              int E, int K, int gated, float scale, int32_t* __restrict__ ids,
                                               float* __restrict__ wout) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  topk_wave(scores + (size_t)t * E, bias, E, K, scale, lane, ids + (size_t)t * K, wout + (size_t)t * K);
+  topk_wave(scores + (size_t)t * (E + gated), bias, E, K, scale, lane, ids + (size_t)t * K,
+            wout + (size_t)t * (K + gated), gated);
 }
 
 // Below this many tokens a wavefront per (expert, run of tokens) has more
@@ -245,12 +247,13 @@ hipError_t launch_router_scores(const uint16_t* x, const float* wg, int T, int H
 }
 
 hipError_t launch_router(const uint16_t* x, const float* wg, const float* bias, int T, int H, int E, int K,
-                         float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream) {
+                         int gated, float scale, float* scores_ws, int32_t* ids, float* w, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  hipError_t err = launch_router_scores(x, wg, T, H, E, scores_ws, stream);
+  hipError_t err = launch_router_scores(x, wg, T, H, E + gated, scores_ws, stream);
   if (err != hipSuccess) return err;
   clear_last_error();
-  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, stream, scores_ws, bias, T, E, K, scale, ids, w);
+  hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, stream, scores_ws, bias, T, E, K, gated, scale, ids,
+                     w);
   return hipGetLastError();
 }
 

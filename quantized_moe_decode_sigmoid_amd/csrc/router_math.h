@@ -123,9 +123,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
 // index (first set bit of the first non-empty ballot, in expert order), then
 // retiring it.  Lane 0 writes the slots to ids[0..K) and the weights
 // scale * s_k / (((s_0 + s_1) + s_2) + ...) to w (either may point to global
-// or LDS memory).
+// or LDS memory); with a sigmoid-gated shared expert (gated != 0) also
+// w[K] = scores[E], the gate's own sigmoid score (not normalised or scaled).
 __device__ __forceinline__ void topk_wave(const float* scores, const float* bias, int E, int K, float scale,
-                                          int lane, int32_t* ids, float* wout) {
+                                          int lane, int32_t* ids, float* wout, int gated = 0) {
 #pragma clang fp contract(off)
   float s[4];
   uint32_t key[4];
@@ -167,6 +168,7 @@ __device__ __forceinline__ void topk_wave(const float* scores, const float* bias
       ids[k] = chosen[k];
       wout[k] = (chosen_s[k] / S) * scale;
     }
+    if (gated) wout[K] = scores[E];
   }
 }
 

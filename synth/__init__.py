@@ -133,6 +133,8 @@ WORKLOADS = {
     "stack": Shape("stack", 1, 3584, 64, 4, 1024, seed=2, layers=38, zipf_s=1.1),
     "batch": Shape("batch", 128, 3584, 64, 4, 1024, seed=3),
     "prefill": Shape("prefill", 2048, 2048, 256, 8, 512, seed=4, zipf_s=1.0),
+    # a dense FFN block of the same model (no routing: one always-on expert of width 9216)
+    "dense": Shape("dense", 1, 3584, 0, 0, 9216, seed=5),
 }
 
 
@@ -150,6 +152,12 @@ def gate_weights(shape: Shape, layer: int = 0, seed: int | None = None) -> np.nd
     seed = shape.seed if seed is None else seed
     g = normal_f32(seed, stream_id(KIND_GATE, layer), shape.n_experts * shape.hidden, 0.0, WEIGHT_STD)
     return g.reshape(shape.n_experts, shape.hidden)
+
+
+def shared_gate_row(shape: Shape, layer: int = 0, seed: int | None = None) -> np.ndarray:
+    """The shared expert's gate row [hidden] fp32 ~ N(0, 0.02) (router row E of a gated layer)."""
+    seed = shape.seed if seed is None else seed
+    return normal_f32(seed, stream_id(KIND_GATE, layer, 1), shape.hidden, 0.0, WEIGHT_STD)
 
 
 def expert_arena(shape: Shape, layer: int = 0, seed: int | None = None,
@@ -197,7 +205,7 @@ def layer_inputs(shape: Shape, layer: int = 0, seed: int | None = None, lam: flo
     """Everything one layer consumes except the activations."""
     bias = zipf_bias(shape, lam, layer, seed) if shape.zipf_s and lam else None
     return {
-        "gate_w": gate_weights(shape, layer, seed),
+        "gate_w": gate_weights(shape, layer, seed) if shape.n_experts else None,
         "bias": bias,
         "arena": expert_arena(shape, layer, seed),
         "shared": shared_arena(shape, layer, seed) if shape.n_shared else None,

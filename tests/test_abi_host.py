@@ -36,7 +36,7 @@ def test_exports_nothing_else():
 
 
 def test_version_and_status_strings():
-    assert qm.moe_abi_version() == 1
+    assert qm.moe_abi_version() == 2
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(qm.status_string(s), str) and qm.status_string(s)
 
@@ -54,6 +54,33 @@ def test_sizes_and_precision_rule():
     assert qm.moe_workspace_bytes(cfg, 1) > 0
     assert qm.moe_workspace_bytes(cfg, 128) > qm.moe_workspace_bytes(cfg, 1)
     assert qm.moe_workspace_bytes(cfg, 0) > 0
+
+
+def test_dense_and_gated_configs():
+    """A dense FFN block (E = 0, K = 0, one always-on expert) and a sigmoid-gated shared expert are valid
+    shapes; their neighbours are refused, and the routing-only calls refuse a dense block."""
+    dense = qm.make_config(3584, 9216, 0, 0, 1)
+    assert qm.moe_check_config(dense) == 0
+    assert qm.moe_expert_bytes(dense) == 3 * 9216 * 3584 // 32 * 18
+    assert qm.moe_resolved_precision(dense, 16) == qm.PREC_FP32
+    assert qm.moe_resolved_precision(dense, 17) == qm.PREC_BF16
+    gated = qm.make_config(**XING4, shared_gate=1)
+    assert qm.moe_check_config(gated) == 0
+    assert qm.moe_workspace_bytes(gated, 4) >= qm.moe_workspace_bytes(qm.make_config(**XING4), 4)
+    for bad, code in [(dict(n_experts=0, top_k=0, n_shared=0), qm.MOE_EUNSUPPORTED),
+                      (dict(n_experts=0, top_k=2), qm.MOE_EUNSUPPORTED),
+                      (dict(n_experts=0, top_k=0, shared_gate=1), qm.MOE_EUNSUPPORTED),
+                      (dict(top_k=0), qm.MOE_EINVAL),
+                      (dict(n_shared=0, shared_gate=1), qm.MOE_EUNSUPPORTED),
+                      (dict(shared_gate=2), qm.MOE_EINVAL)]:
+        assert qm.moe_check_config(qm.make_config(**{**XING4, **bad})) == code, bad
+    ws = qm.moe_workspace_bytes(dense, 4)
+    with pytest.raises(qm.MoeError) as ei:
+        qm.moe_route(dense, 4, A, A, None, A, A, A, ws_bytes=ws, stream=0)
+    assert ei.value.status == qm.MOE_EINVAL
+    with pytest.raises(qm.MoeError) as ei:  # the dense block still needs its expert
+        qm.moe_layer_forward(dense, 4, A, None, None, None, None, A, ws=A, ws_bytes=ws, stream=0)
+    assert ei.value.status == qm.MOE_EINVAL
 
 
 @pytest.mark.parametrize("bad,code", [

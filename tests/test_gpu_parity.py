@@ -566,6 +566,93 @@ def test_bf16_and_fp32_contracts_agree_on_a_batch():
     assert 0 < r < 2e-2
 
 
+# ---------------------------------------------------------------- gated shared expert, dense FFN block
+
+def gated_inputs(name):
+    s, inp = workload(name)
+    row = synth.shared_gate_row(s)
+    return s, inp, np.concatenate([inp["gate_w"], row[None, :]]), row
+
+
+@pytest.mark.parametrize("name,T,precision", [("tiny", 1, qm.PREC_AUTO), ("tiny", 4, qm.PREC_AUTO),
+                                              ("tiny", 37, qm.PREC_BF16), ("tiny", 300, qm.PREC_AUTO),
+                                              ("xing4", 1, qm.PREC_AUTO), ("xing4", 5, qm.PREC_AUTO),
+                                              ("batch", 128, qm.PREC_BF16)])
+def test_layer_gated_shared_expert(name, T, precision):
+    """The shared expert scaled by sigmoid(x . gate_w[E]): decode plan (T = 1), FP32 and BF16 multi-kernel
+    plans.  Routing bit-exact, the gate value (topk_w[:, K]) bit-exact against the oracle's sigmoid of the
+    fixed-order logit, outputs within tolerance."""
+    s, inp, gw, row = gated_inputs(name)
+    cfg = cfg_of(s, precision)
+    cfg.shared_gate = 1
+    dl = qm.DeviceLayer(cfg, gw, None, inp["arena"], inp["shared"])
+    x = synth.tokens(s, T, first=611)
+    prec = qm.moe_resolved_precision(cfg, T)
+    log(f"gated {name} T={T} precision={prec}")
+    ids = torch.empty((T, s.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.top_k + 1), dtype=torch.float32, device="cuda")
+    out = dl.forward(to_dev_bf16(x), topk_ids=ids, topk_w=w).cpu().numpy()
+    assert_status_ok(cfg, T, dl.workspace(T))
+    mode = oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32
+    ref, rid, rw = oracle.layer(x, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn, s.routed_scale,
+                                None, mode, shared_gate=row)
+    wg = w.cpu().numpy()
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.array_equal(wg[:, :s.top_k].view(np.uint32), rw.view(np.uint32))
+    g = oracle.sigmoid_many(oracle.router_logits(x, row[None, :])[:, 0])
+    assert np.array_equal(wg[:, s.top_k].view(np.uint32), g.view(np.uint32))
+    assert_close(out, ref, f"gated {name} T={T}")
+
+
+def test_gated_expert_forward_takes_the_gate_from_the_weights():
+    """moe_expert_forward of a gated layer reads the gate from topk_w[:, K]: with the router's own weights
+    it equals moe_layer_forward bit for bit; with the gate column zeroed it equals the ungated layer without
+    the shared expert's contribution (the oracle with no shared expert)."""
+    s, inp, gw, row = gated_inputs("tiny")
+    cfg = cfg_of(s)
+    cfg.shared_gate = 1
+    dl = qm.DeviceLayer(cfg, gw, None, inp["arena"], inp["shared"])
+    T = 9
+    x = synth.tokens(s, T, first=50)
+    xd = to_dev_bf16(x)
+    ids = torch.empty((T, s.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.top_k + 1), dtype=torch.float32, device="cuda")
+    full = dl.forward(xd, topk_ids=ids, topk_w=w).cpu().numpy()
+    out = torch.empty((T, s.hidden), dtype=torch.float32, device="cuda")
+    log("gated expert_forward tiny T=9")
+    qm.moe_expert_forward(cfg, T, xd, ids, w, dl.arena, dl.shared, out, dl.workspace(T))
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), full.view(np.uint32))
+    w[:, s.top_k] = 0.0
+    qm.moe_expert_forward(cfg, T, xd, ids, w, dl.arena, dl.shared, out, dl.workspace(T))
+    ref, _, _ = oracle.layer(x, inp["gate_w"], inp["arena"], None, s.top_k, s.ffn, s.routed_scale)
+    assert_close(out.cpu().numpy(), ref, "gated, gate column zero")
+
+
+@pytest.mark.parametrize("name,T,precision", [("tiny", 1, qm.PREC_AUTO), ("tiny", 16, qm.PREC_AUTO),
+                                              ("tiny", 37, qm.PREC_AUTO), ("dense", 1, qm.PREC_AUTO),
+                                              ("dense", 16, qm.PREC_AUTO), ("dense", 64, qm.PREC_AUTO),
+                                              ("dense", 3, qm.PREC_BF16)])
+def test_dense_ffn_block(name, T, precision):
+    """A dense FFN block (E = 0: the always-on expert alone), the tiny width and the model's dense width
+    (H = 3584, F = 9216): FP32 plan for T <= 16 and BF16 tiles above (AUTO), against the oracle."""
+    s = synth.WORKLOADS[name]
+    if name == "tiny":
+        s = synth.Shape("tiny_dense", 1, s.hidden, 0, 0, s.ffn, seed=s.seed)
+    key = (s.name, 0)
+    if key not in _CACHE:
+        _CACHE[key] = (s, synth.layer_inputs(s))
+    inp = _CACHE[key][1]
+    cfg = qm.make_config(s.hidden, s.ffn, 0, 0, 1, 1.0, precision)
+    dl = qm.DeviceLayer(cfg, None, None, None, inp["shared"])
+    x = synth.tokens(s, T, first=21)
+    prec = qm.moe_resolved_precision(cfg, T)
+    log(f"dense {s.name} T={T} precision={prec}")
+    out = dl.forward(to_dev_bf16(x)).cpu().numpy()
+    mode = oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32
+    ref, _, _ = oracle.layer(x, np.zeros((0, s.hidden), np.float32), None, inp["shared"], 0, s.ffn, 1.0, None, mode)
+    assert_close(out, ref, f"dense {s.name} T={T}")
+
+
 # ---------------------------------------------------------------- the 38-layer stack workload
 
 def test_stack_layers_chained_with_zipf_bias():
