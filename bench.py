@@ -596,8 +596,8 @@ def run_batch(args, check):
 
 def run_stack(args, check):
     """38 MoE layers of the Xing4 shape resident in HBM, one token per step (T=1) through all of them,
-    each layer's input chained from the previous layer's output by bf16(rmsnorm(x + out)) (one fused
-    kernel of the library); Zipf(1.1) expert popularity."""
+    each layer's input chained from the previous layer's input and output by bf16(rmsnorm(x + out)),
+    formed inside the next layer's router kernel (moe_layer_forward_chained); Zipf(1.1) expert popularity."""
     import torch
 
     import quantized_moe_decode_sigmoid_amd as qm
@@ -638,22 +638,29 @@ def run_stack(args, check):
     x0 = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
     ws = torch.empty(qm.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device=dev)
     qm.moe_workspace_init(cfg, 1, ws)
-    outs = [torch.empty((1, H), dtype=torch.float32, device=dev) for _ in range(nl)]
-    xs = [torch.empty((1, H), dtype=torch.bfloat16, device=dev) for _ in range(nl)]
+    outs = torch.empty((nl, H), dtype=torch.float32, device=dev)
+    xl = torch.empty((nl, H), dtype=torch.bfloat16, device=dev)  # each layer's input
     ids = torch.empty((S, nl, K), dtype=torch.int32, device=dev)
     wts = torch.empty((S, nl, K), dtype=torch.float32, device=dev)
 
+    def layer_call(i, l):
+        """Layer l of token i: layer 0 on the token itself, every later layer chained (its input
+        bf16(rmsnorm(previous input + previous output)) formed inside the call)."""
+        dl = layers[l]
+        if l == 0:
+            qm.moe_layer_forward(cfg, 1, xl[0:1], dl.gate_w, dl.bias, dl.arena, dl.shared, outs[0:1], ids[i, 0],
+                                 wts[i, 0], ws)
+        else:
+            qm.moe_layer_forward_chained(cfg, 1, xl[l - 1:l], outs[l - 1:l], xl[l:l + 1], dl.gate_w, dl.bias, dl.arena,
+                                         dl.shared, outs[l:l + 1], ids[i, l], wts[i, l], ws)
+
     def token(i, x_in=None, o_out=None):
-        x = x0[i:i + 1]
-        for l, dl in enumerate(layers):
-            if x_in is not None:
-                x_in[l].copy_(x[0])
-            qm.moe_layer_forward(cfg, 1, x, dl.gate_w, dl.bias, dl.arena, dl.shared, outs[l], ids[i, l],
-                                 wts[i, l], ws)
-            if o_out is not None:
-                o_out[l].copy_(outs[l][0])
-            qm.moe_residual_rmsnorm(outs[l], x, xs[l], eps=1e-6)
-            x = xs[l]
+        xl[0].copy_(x0[i])
+        for l in range(nl):
+            layer_call(i, l)
+        if x_in is not None:
+            x_in.copy_(xl)
+            o_out.copy_(outs)
 
     def steps():
         for i in range(S):
@@ -670,20 +677,17 @@ def run_stack(args, check):
             graph.replay()
         torch.cuda.synchronize()
         total_ms, per_replay = timed_steps(torch, stream, graph.replay, args.steps)
-        # the MoE layer calls alone: events around each call of one eager pass over the S tokens, the
-        # queue kept busy by a spin kernel so that host launch gaps do not enter
+        # the layer calls alone: events around each call of one eager pass over the S tokens, the queue kept
+        # busy by a spin kernel so that host launch gaps do not enter
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
         torch.cuda._sleep(200_000_000)
         for i in range(S):
-            x = x0[i:i + 1]
-            for l, dl in enumerate(layers):
+            xl[0].copy_(x0[i])
+            for l in range(nl):
                 starts[i * nl + l].record(stream)
-                qm.moe_layer_forward(cfg, 1, x, dl.gate_w, dl.bias, dl.arena, dl.shared, outs[l], ids[i, l],
-                                     wts[i, l], ws)
+                layer_call(i, l)
                 ends[i * nl + l].record(stream)
-                qm.moe_residual_rmsnorm(outs[l], x, xs[l], eps=1e-6)
-                x = xs[l]
         torch.cuda.synchronize()
         # every layer's input and output of the first tokens, for the oracle (eager, same kernels)
         n_chk = min(S, 8)
@@ -752,12 +756,13 @@ def run_stack(args, check):
                                "shared, ffn 1024, IQ4_NL, sigmoid router, scale 2.0; layer input = bf16(rmsnorm("
                                "previous input + previous output)) by one fused kernel; Zipf(1.1) expert popularity",
                    "layers": nl, "distinct_tokens": S, "zipf_lambda": lam, "graph": True,
+                   "chaining": "layers 1..37 by moe_layer_forward_chained (the norm inside the router kernel)",
                    "expert_sets": f"router weights and biases drawn per layer; expert weights drawn for {nd} "
                                   f"layers, each layer's placed at its own address"},
         "step_spread": spread(np.asarray(per_replay) / S),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("stack_traffic.json"),
-                     "kernel": "whole step: per layer k_decode_scores + k_decode_experts + k_residual_rmsnorm",
+                     "kernel": "whole step: per layer k_decode_scores (with the chaining norm) + k_decode_experts",
                      "bytes_per_token": expert_bytes + router_bytes},
         "cpu_baseline": cpu,
         "parity": parity,

@@ -234,6 +234,26 @@ moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev
                              float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
                              size_t ws_bytes, hipStream_t stream);
 
+/* A layer of a stack of MoE layers, its input formed in the same call from
+ * the previous layer's input and output:
+ *   x = bf16(h / sqrt(mean(h^2) + eps)) with h = fp32(x_prev) + out_prev
+ * per token row (an unweighted RMS norm after the residual add: the chaining
+ * that stands in for the rest of a decoder block between two MoE layers of
+ * Xing4.0-29B-A4B, design record section 1), then moe_layer_forward on x.
+ *   x_prev_dev   bf16 [T][H]   the previous layer's input
+ *   out_prev_dev fp32 [T][H]   the previous layer's output
+ *   x_dev        bf16 [T][H]   out: this layer's input (the next call's
+ *                x_prev); must not overlap x_prev_dev or out_prev_dev
+ * x is bit-identical to moe_residual_rmsnorm(out_prev, x_prev, T, H, eps, x)
+ * and the outputs to moe_layer_forward on that x.  On the decode plan
+ * (T = 1) the norm runs inside the router kernel (no extra launch).  Other
+ * arguments as moe_layer_forward; eps >= 0 and finite. */
+moe_status moe_layer_forward_chained(const moe_config* cfg, int32_t T, const void* x_prev_dev,
+                                     const float* out_prev_dev, float eps, void* x_dev, const float* gate_w_dev,
+                                     const float* sel_bias_dev, const void* arena_dev, const void* shared_dev,
+                                     float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
+                                     size_t ws_bytes, hipStream_t stream);
+
 /* moe_layer_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under graph capture, tight serving loops,
  * harnesses that forbid allocation).  Same arguments, validation, kernels and

@@ -70,6 +70,8 @@ _SIGS = {
     "moe_bucket": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_expert_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "moe_layer_forward": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_layer_forward_chained": ([_cfgp, _i32, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, _sz, _vp], _i32),
     "moe_layer_forward_noalloc": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
     "moe_stream_read": ([_vp, _sz, _vp, _vp], _i32),
     "moe_residual_rmsnorm": ([_vp, _vp, _i32, _i32, ctypes.c_float, _vp, _vp], _i32),
@@ -186,6 +188,15 @@ def moe_layer_forward(cfg, T, x, gate_w, sel_bias, arena, shared, out, topk_ids=
     _check(_lib.moe_layer_forward(ctypes.byref(cfg), T, _p(x), _p(gate_w), _p(sel_bias), _p(arena), _p(shared),
                                   _p(out), _p(topk_ids), _p(topk_w), _p(ws), ws_bytes, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_layer_forward_chained(cfg, T, x_prev, out_prev, x, gate_w, sel_bias, arena, shared, out, topk_ids=None,
+                              topk_w=None, ws=None, ws_bytes=None, eps=1e-6, stream=None):
+    """A stacked layer whose input x = bf16(rmsnorm(x_prev + out_prev)) is formed (and written to x) in the call."""
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check(_lib.moe_layer_forward_chained(ctypes.byref(cfg), T, _p(x_prev), _p(out_prev), eps, _p(x), _p(gate_w),
+                                          _p(sel_bias), _p(arena), _p(shared), _p(out), _p(topk_ids), _p(topk_w),
+                                          _p(ws), ws_bytes, _stream(stream)), "moe_layer_forward_chained")
 
 
 def moe_layer_forward_noalloc(cfg, T, x, gate_w, sel_bias, arena, shared, out, topk_ids=None, topk_w=None,

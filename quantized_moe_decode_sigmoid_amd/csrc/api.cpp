@@ -148,6 +148,36 @@ moe_status launched(hipError_t e) {
   return MOE_ELAUNCH;
 }
 
+// Arguments of the two-launch decode plan (plain input x).
+qmoe::DecodeArgs decode_args(const moe_config* cfg, const void* x_dev, const float* gate_w_dev,
+                             const float* sel_bias_dev, const void* arena_dev, const void* shared_dev, float* out_dev,
+                             int32_t* ids, float* w, void* ws_dev, const Plan& p) {
+  qmoe::DecodeArgs a;
+  a.x = static_cast<const uint16_t*>(x_dev);
+  a.wg = gate_w_dev;
+  a.bias = sel_bias_dev;
+  a.arena = static_cast<const uint8_t*>(arena_dev);
+  a.shared = static_cast<const uint8_t*>(shared_dev);
+  a.expert_bytes = expert_bytes(cfg);
+  a.H = cfg->hidden;
+  a.F = cfg->ffn;
+  a.E = cfg->n_experts;
+  a.K = cfg->top_k;
+  a.n_shared = cfg->n_shared;
+  a.gated = cfg->shared_gate;
+  a.scale = cfg->routed_scale;
+  a.scores = at<float>(ws_dev, p.scores);
+  a.ids = ids;
+  a.w = w;
+  a.hw = at<uint32_t>(ws_dev, p.hw);
+  a.out = out_dev;
+  a.err = at<uint32_t>(ws_dev, p.status);
+  a.x_prev = nullptr;
+  a.out_prev = nullptr;
+  a.eps = 0.0f;
+  return a;
+}
+
 // Expert FFN + combine after validation; ids and w are device pointers.
 moe_status run_expert_forward(const moe_config* cfg, int32_t T, const void* x, const int32_t* ids, const float* w,
                               const void* arena, const void* shared, float* out, void* ws, hipStream_t stream) {
@@ -334,6 +364,57 @@ MOE_API moe_status moe_expert_forward(const moe_config* cfg, int32_t T, const vo
   return run_expert_forward(cfg, T, x_dev, topk_ids_dev, topk_w_dev, arena_dev, shared_dev, out_dev, ws_dev, stream);
 }
 
+namespace {
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* p = static_cast<const char*>(a);
+  const char* q = static_cast<const char*>(b);
+  return p < q + nb && q < p + na;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_layer_forward_chained(const moe_config* cfg, int32_t T, const void* x_prev_dev,
+                                             const float* out_prev_dev, float eps, void* x_dev,
+                                             const float* gate_w_dev, const float* sel_bias_dev,
+                                             const void* arena_dev, const void* shared_dev, float* out_dev,
+                                             int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
+                                             size_t ws_bytes, hipStream_t stream) {
+  TRY(check_common(cfg, T));
+  if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_EINVAL;
+  if (T == 0) return MOE_OK;
+  TRY(need(x_prev_dev));
+  TRY(need(out_prev_dev));
+  TRY(need(x_dev));
+  const size_t xb = (size_t)T * cfg->hidden * 2;
+  if (overlaps(x_dev, xb, x_prev_dev, xb) || overlaps(x_dev, xb, out_prev_dev, 2 * xb)) return MOE_EINVAL;
+  if (cfg->n_experts > 0) {
+    TRY(need(gate_w_dev));
+    TRY(optional_ptr(sel_bias_dev));
+    TRY(need(arena_dev));
+  }
+  if (cfg->n_shared) TRY(need(shared_dev));
+  TRY(need(out_dev));
+  TRY(optional_ptr(topk_ids_out_dev));
+  TRY(optional_ptr(topk_w_out_dev));
+  TRY(need(ws_dev));
+  const Plan p = make_plan(cfg, T);
+  if (ws_bytes < p.total) return MOE_EWORKSPACE;
+  if (decode_path(cfg, T)) {
+    qmoe::DecodeArgs a = decode_args(cfg, x_dev, gate_w_dev, sel_bias_dev, arena_dev, shared_dev, out_dev,
+                                     topk_ids_out_dev ? topk_ids_out_dev : at<int32_t>(ws_dev, p.ids),
+                                     topk_w_out_dev ? topk_w_out_dev : at<float>(ws_dev, p.w), ws_dev, p);
+    a.x_prev = static_cast<const uint16_t*>(x_prev_dev);
+    a.out_prev = out_prev_dev;
+    a.eps = eps;
+    return launched(qmoe::launch_layer_decode(a, stream));
+  }
+  TRY(launched(qmoe::launch_residual_rmsnorm(out_prev_dev, static_cast<const uint16_t*>(x_prev_dev), T, cfg->hidden,
+                                             eps, static_cast<uint16_t*>(x_dev), stream)));
+  return moe_layer_forward(cfg, T, x_dev, gate_w_dev, sel_bias_dev, arena_dev, shared_dev, out_dev, topk_ids_out_dev,
+                           topk_w_out_dev, ws_dev, ws_bytes, stream);
+}
+
 MOE_API moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
                                      const float* sel_bias_dev, const void* arena_dev, const void* shared_dev,
                                      float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
@@ -358,29 +439,9 @@ MOE_API moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const voi
     return run_expert_forward(cfg, T, x_dev, nullptr, nullptr, nullptr, shared_dev, out_dev, ws_dev, stream);
   int32_t* ids = topk_ids_out_dev ? topk_ids_out_dev : at<int32_t>(ws_dev, p.ids);
   float* w = topk_w_out_dev ? topk_w_out_dev : at<float>(ws_dev, p.w);
-  if (decode_path(cfg, T)) {
-    qmoe::DecodeArgs a;
-    a.x = static_cast<const uint16_t*>(x_dev);
-    a.wg = gate_w_dev;
-    a.bias = sel_bias_dev;
-    a.arena = static_cast<const uint8_t*>(arena_dev);
-    a.shared = static_cast<const uint8_t*>(shared_dev);
-    a.expert_bytes = expert_bytes(cfg);
-    a.H = cfg->hidden;
-    a.F = cfg->ffn;
-    a.E = cfg->n_experts;
-    a.K = cfg->top_k;
-    a.n_shared = cfg->n_shared;
-    a.gated = cfg->shared_gate;
-    a.scale = cfg->routed_scale;
-    a.scores = at<float>(ws_dev, p.scores);
-    a.ids = ids;
-    a.w = w;
-    a.hw = at<uint32_t>(ws_dev, p.hw);
-    a.out = out_dev;
-    a.err = at<uint32_t>(ws_dev, p.status);
-    return launched(qmoe::launch_layer_decode(a, stream));
-  }
+  if (decode_path(cfg, T))
+    return launched(qmoe::launch_layer_decode(
+        decode_args(cfg, x_dev, gate_w_dev, sel_bias_dev, arena_dev, shared_dev, out_dev, ids, w, ws_dev, p), stream));
   TRY(launched(qmoe::launch_router(static_cast<const uint16_t*>(x_dev), gate_w_dev, sel_bias_dev, T, cfg->hidden,
                                    cfg->n_experts, cfg->top_k, cfg->shared_gate, cfg->routed_scale,
                                    at<float>(ws_dev, p.scores), ids, w, stream)));

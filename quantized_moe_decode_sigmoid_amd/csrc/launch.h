@@ -67,6 +67,11 @@ struct DecodeArgs {
   uint32_t* hw;        // [(K + 1) * F] h words: bf16(h) | bf16(h - bf16(h)) << 16
   float* out;          // [H]
   uint32_t* err;       // set to 1 if a wait gave up
+  // chained input (x_prev non-null): the first kernel forms x = bf16(rmsnorm(x_prev + out_prev)) itself (the
+  // arithmetic of k_residual_rmsnorm) and writes it to x (which must not overlap x_prev or out_prev)
+  const uint16_t* x_prev;
+  const float* out_prev;
+  float eps;
   int n_router, n_shared_wg, n_routed_wg, n_down_wg;  // grid partition (set by the launcher)
 };
 

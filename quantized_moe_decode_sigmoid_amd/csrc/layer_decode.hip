@@ -115,6 +115,65 @@ struct ExpertsLds {
 
 // ---------------------------------------------------------------- kernel 1: scores
 
+// The layer's input formed from the previous layer's input and output,
+// x = bf16(h * r), h = fp32(x_prev) + out_prev, r = 1 / sqrt(mean(h^2) + eps),
+// with exactly the operations and order of k_residual_rmsnorm (chain.hip):
+// there, thread v of 256 sums h_i^2 over i = v, v + 256, ... with fused
+// multiply-adds, each wavefront's 64 sums meet in an xor butterfly and the 4
+// wavefront sums are added in order; here lane j plays threads j, j + 64,
+// j + 128, j + 192.  The lane loads its router elements 256m + 4j + c (vector
+// loads, all issued at once), passes h through LDS to the lanes that sum it,
+// and gets its router elements of x back in xv.
+template <int MMAX>
+__device__ __forceinline__ void chained_input(const DecodeArgs& a, int lane, float* hbuf, uint2 (&xv)[MMAX]) {
+  const int H = a.H, M = H >> 8;
+  uint2 xp[MMAX];
+  float4 op[MMAX];
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    const int i0 = 256 * (m < M ? m : M - 1) + 4 * lane;
+    xp[m] = *reinterpret_cast<const uint2*>(a.x_prev + i0);
+    op[m] = *reinterpret_cast<const float4*>(a.out_prev + i0);
+  }
+  float4 h[MMAX];
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    h[m].x = bf16_bits_to_f32(xp[m].x & 0xffffu) + op[m].x;
+    h[m].y = bf16_bits_to_f32(xp[m].x >> 16) + op[m].y;
+    h[m].z = bf16_bits_to_f32(xp[m].y & 0xffffu) + op[m].z;
+    h[m].w = bf16_bits_to_f32(xp[m].y >> 16) + op[m].w;
+    if (m < M) *reinterpret_cast<float4*>(hbuf + 256 * m + 4 * lane) = h[m];
+  }
+  __syncthreads();
+  float part[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int n = 0; n < MMAX; n++) {
+      if (n < M) {
+        const float hv = hbuf[lane + 64 * q + 256 * n];
+        ss = __builtin_fmaf(hv, hv, ss);
+      }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) ss += __shfl_xor(ss, s, 64);
+    part[q] = ss;
+  }
+  float tot = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; q++) tot += part[q];
+  const float r = 1.0f / __builtin_sqrtf(tot / (float)H + a.eps);
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    const uint32_t y0 = f32_to_bf16_rne(h[m].x * r);
+    const uint32_t y1 = f32_to_bf16_rne(h[m].y * r);
+    const uint32_t y2 = f32_to_bf16_rne(h[m].z * r);
+    const uint32_t y3 = f32_to_bf16_rne(h[m].w * r);
+    xv[m] = make_uint2(y0 | (y1 << 16), y2 | (y3 << 16));
+  }
+}
+
 template <int MMAX>
 __global__ __launch_bounds__(64) void k_decode_scores(DecodeArgs a) {
   const int lane = threadIdx.x;
@@ -125,7 +184,21 @@ __global__ __launch_bounds__(64) void k_decode_scores(DecodeArgs a) {
   if (e < a.E + a.gated) {  // row E: the shared expert's gate
     float4 w[MMAX];
     load_router_row<MMAX>(a.wg + (size_t)e * a.H, a.H, lane, w);
-    const float p = router_logit<MMAX>(a.x, a.H, lane, w);
+    float p;
+    if (a.x_prev) {
+      __shared__ float hbuf[256 * MMAX];
+      uint2 xv[MMAX];
+      chained_input<MMAX>(a, lane, hbuf, xv);
+      if (e == 0) {  // the layer's input, for the second kernel and the caller
+        uint16_t* xo = const_cast<uint16_t*>(a.x);
+#pragma unroll
+        for (int m = 0; m < MMAX; m++)
+          if (m < (a.H >> 8)) *reinterpret_cast<uint2*>(xo + 256 * m + 4 * lane) = xv[m];
+      }
+      p = router_logit_vals<MMAX>(xv, a.H, w);
+    } else {
+      p = router_logit<MMAX>(a.x, a.H, lane, w);
+    }
     if (lane == 0) a.scores[e] = sigmoid_fixed(p);
   }
 }

@@ -59,17 +59,12 @@ __device__ __forceinline__ void load_router_row(const float* wrow, int H, int la
 
 // fp32 logit in the fixed order: lane j accumulates its elements with fused
 // multiply-adds in (m, c) order, then p_j + p_{j xor s} for s = 32..1.  Every
-// lane returns the same value.
+// lane returns the same value.  xv[m] holds the lane's 4 bf16 activations
+// 256m + 4j .. 256m + 4j + 3.
 template <int MMAX>
-__device__ __forceinline__ float router_logit(const uint16_t* xrow, int H, int lane, const float4 (&w)[MMAX]) {
+__device__ __forceinline__ float router_logit_vals(const uint2 (&xv)[MMAX], int H, const float4 (&w)[MMAX]) {
 #pragma clang fp contract(off)
   const int M = H >> 8;
-  uint2 xv[MMAX];
-#pragma unroll
-  for (int m = 0; m < MMAX; m++) {
-    const int mm = m < M ? m : M - 1;
-    xv[m] = *reinterpret_cast<const uint2*>(xrow + 256 * mm + 4 * lane);
-  }
   float p = 0.0f;
 #pragma unroll
   for (int m = 0; m < MMAX; m++) {
@@ -83,6 +78,19 @@ __device__ __forceinline__ float router_logit(const uint16_t* xrow, int H, int l
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_xor(p, s, 64);
   return p;
+}
+
+// The same with the lane's activations read from the row xrow.
+template <int MMAX>
+__device__ __forceinline__ float router_logit(const uint16_t* xrow, int H, int lane, const float4 (&w)[MMAX]) {
+  const int M = H >> 8;
+  uint2 xv[MMAX];
+#pragma unroll
+  for (int m = 0; m < MMAX; m++) {
+    const int mm = m < M ? m : M - 1;
+    xv[m] = *reinterpret_cast<const uint2*>(xrow + 256 * mm + 4 * lane);
+  }
+  return router_logit_vals<MMAX>(xv, H, w);
 }
 
 // The (selection score, expert) order: a precedes b when its score is larger,

@@ -56,6 +56,26 @@ def test_sizes_and_precision_rule():
     assert qm.moe_workspace_bytes(cfg, 0) > 0
 
 
+def test_chained_layer_argument_errors():
+    cfg = qm.make_config(**XING4)
+    ws = qm.moe_workspace_bytes(cfg, 2)
+    H = XING4["hidden"]
+
+    def call(x_prev=A, out_prev=A + 0x100000, x=A + 0x200000, eps=1e-6, wsb=ws):
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_layer_forward_chained(cfg, 2, x_prev, out_prev, x, A, None, A, A, A, ws=A + 0x400000, ws_bytes=wsb,
+                                         eps=eps, stream=0)
+        return ei.value.status
+
+    assert call(x_prev=None) == qm.MOE_EINVAL
+    assert call(out_prev=A + 8) == qm.MOE_EALIGN
+    assert call(x=A + 2 * H) == qm.MOE_EINVAL              # overlaps x_prev's second row
+    assert call(x=A + 0x100000 + 4 * H) == qm.MOE_EINVAL   # overlaps out_prev
+    assert call(eps=-1.0) == qm.MOE_EINVAL
+    assert call(eps=float("inf")) == qm.MOE_EINVAL
+    assert call(wsb=ws - 1) == qm.MOE_EWORKSPACE
+
+
 def test_dense_and_gated_configs():
     """A dense FFN block (E = 0, K = 0, one always-on expert) and a sigmoid-gated shared expert are valid
     shapes; their neighbours are refused, and the routing-only calls refuse a dense block."""

@@ -680,6 +680,112 @@ def test_stack_layers_chained_with_zipf_bias():
         x = torch.nn.functional.rms_norm(h, (s.hidden,), eps=1e-6).to(torch.bfloat16)
 
 
+@pytest.mark.parametrize("T", [1, 5])
+def test_chained_layer_equals_norm_then_layer(T):
+    """moe_layer_forward_chained (the stack's norm folded into the router kernel on the decode plan, T = 1; a
+    separate norm kernel on the multi-kernel plan, T = 5) against moe_residual_rmsnorm + moe_layer_forward:
+    the formed input, the routing and the output are identical bit for bit."""
+    s, inp, dl = device_layer("xing4")
+    g = torch.Generator().manual_seed(T)
+    x_prev = torch.randn(T, s.hidden, generator=g).to(torch.bfloat16).cuda()
+    out_prev = torch.randn(T, s.hidden, generator=g).cuda()
+    cfg = dl.cfg
+    ws = dl.workspace(T)
+    log(f"chained layer xing4 T={T}")
+    x_a = torch.empty_like(x_prev)
+    out_a = torch.empty((T, s.hidden), dtype=torch.float32, device="cuda")
+    ids_a = torch.empty((T, s.top_k), dtype=torch.int32, device="cuda")
+    w_a = torch.empty((T, s.top_k), dtype=torch.float32, device="cuda")
+    qm.moe_layer_forward_chained(cfg, T, x_prev, out_prev, x_a, dl.gate_w, None, dl.arena, dl.shared, out_a, ids_a,
+                                 w_a, ws)
+    x_b = torch.empty_like(x_prev)
+    qm.moe_residual_rmsnorm(out_prev, x_prev, x_b, eps=1e-6)
+    out_b = torch.empty_like(out_a)
+    ids_b = torch.empty_like(ids_a)
+    w_b = torch.empty_like(w_a)
+    qm.moe_layer_forward(cfg, T, x_b, dl.gate_w, None, dl.arena, dl.shared, out_b, ids_b, w_b, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(x_a.view(torch.int16), x_b.view(torch.int16))
+    assert torch.equal(ids_a, ids_b) and torch.equal(w_a.view(torch.int32), w_b.view(torch.int32))
+    assert torch.equal(out_a.view(torch.int32), out_b.view(torch.int32))
+    assert_status_ok(cfg, T, ws)
+
+
+def test_stack_38_layers_captured_step():
+    """The 38-layer T = 1 step of the stack workload (Zipf(1.1) selection bias, router weights per layer,
+    expert weights of 2 drawn layers each placed per layer) captured as one HIP graph of chained layer calls
+    for two tokens and replayed 3 times with eager work in between: every replay equals the eager run bit for
+    bit; every layer's routing equals the oracle's on the GPU's input to that layer bit for bit, its output is
+    within tolerance of the oracle's, and every formed input is within one bf16 step of the oracle's norm of
+    the previous layer's input and output."""
+    s = synth.WORKLOADS["stack"]
+    lam = synth.zipf_lambda(s)
+    cfg = cfg_of(s)
+    nl, nt = 38, 2
+    sets = [synth.layer_inputs(s, layer=d, lam=lam) for d in range(2)]
+    packed = [qm.DeviceLayer(cfg, st["gate_w"], None, st["arena"], st["shared"]) for st in sets]
+    layers, host = [], []
+    for l in range(nl):
+        gw, b = synth.gate_weights(s, layer=l), synth.zipf_bias(s, lam, layer=l)
+        src = packed[l % 2]
+        layers.append(qm.DeviceLayer.from_packed(cfg, torch.from_numpy(gw).cuda(), torch.from_numpy(b).cuda(),
+                                                 src.arena.clone(), src.shared.clone()))
+        host.append((gw, b, sets[l % 2]))
+    x0 = to_dev_bf16(synth.tokens(s, nt, first=9000))
+    xs = torch.empty((nt, nl, s.hidden), dtype=torch.bfloat16, device="cuda")
+    outs = torch.empty((nt, nl, s.hidden), dtype=torch.float32, device="cuda")
+    ids = torch.empty((nt, nl, s.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((nt, nl, s.top_k), dtype=torch.float32, device="cuda")
+    ws = layers[0].workspace(1)
+
+    def step():
+        for t in range(nt):
+            xs[t, 0].copy_(x0[t])
+            for l, dl in enumerate(layers):
+                if l == 0:
+                    qm.moe_layer_forward(cfg, 1, xs[t, 0:1], dl.gate_w, dl.bias, dl.arena, dl.shared, outs[t, 0:1],
+                                         ids[t, 0], w[t, 0], ws)
+                else:
+                    qm.moe_layer_forward_chained(cfg, 1, xs[t, l - 1:l], outs[t, l - 1:l], xs[t, l:l + 1], dl.gate_w,
+                                                 dl.bias, dl.arena, dl.shared, outs[t, l:l + 1], ids[t, l], w[t, l],
+                                                 ws)
+
+    log("stack 38 layers: eager")
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step()
+        torch.cuda.synchronize()
+        eager = [a.clone() for a in (xs, outs, ids, w)]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        for rep in range(3):
+            for a in (xs, outs, w):
+                a.fill_(float("nan"))
+            ids.fill_(-1)
+            graph.replay()
+            torch.cuda.synchronize()
+            for got, want in zip((xs, outs, ids, w), eager):
+                assert torch.equal(got.view(torch.int8), want.view(torch.int8)), rep
+            _ = layers[rep].forward(x0[0:1])  # eager work between replays
+            torch.cuda.synchronize()
+    assert_status_ok(cfg, 1, ws)
+    xin = xs.view(torch.int16).cpu().numpy().view(np.uint16)
+    got, gid, gw_ = outs.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    for l in range(nl):
+        if l % 8 == 0:
+            log(f"stack 38 layers: oracle layer {l}")
+        gwl, bl, st = host[l]
+        ref, rid, rw = oracle.layer(xin[:, l], gwl, st["arena"], st["shared"], s.top_k, s.ffn, s.routed_scale, bl)
+        assert np.array_equal(gid[:, l], rid), l
+        assert np.array_equal(gw_[:, l].view(np.uint32), rw.view(np.uint32)), l
+        assert_close(got[:, l], ref, f"stack layer {l}")
+        if l + 1 < nl:
+            y = oracle.residual_rmsnorm(xin[:, l], got[:, l])
+            diff = np.abs(xin[:, l + 1].astype(np.int32) - y.astype(np.int32))
+            assert int(diff.max()) <= 1, l
+
+
 def test_stream_read_reads_and_writes_nothing():
     """The measurement kernel: a zero buffer XORs to zero, so the sink keeps its value; a ragged size
     (not a multiple of the grid's stride) ends without touching memory past the buffer (the buffer sits
