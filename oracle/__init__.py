@@ -17,7 +17,7 @@ import subprocess
 
 import numpy as np
 
-FP32, BF16 = 1, 2  # precision modes (see moe_oracle.c)
+FP32, BF16, W4A8 = 1, 2, 3  # precision modes (see moe_oracle.c)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -49,6 +49,9 @@ def _load():
     lib.oracle_bf16_value.restype = f32
     lib.oracle_to_bf16.argtypes = [f32]
     lib.oracle_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_to_f16.argtypes = [f32]
+    lib.oracle_to_f16.restype = ctypes.c_uint16
+    lib.oracle_quantize_q8_0.argtypes = [i64, vp, vp, vp]
     lib.oracle_dequant.argtypes = [vp, i64, i32, vp]
     lib.oracle_router_logits.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.oracle_exp_spec.argtypes = [f64]
@@ -100,6 +103,20 @@ def bf16_value(b: int) -> float:
 
 def to_bf16(f: float) -> int:
     return _load().oracle_to_bf16(f)
+
+
+def to_f16(f: float) -> int:
+    return _load().oracle_to_f16(f)
+
+
+def quantize_q8_0(x: np.ndarray):
+    """fp32 values (a multiple of 32, blocks in order) -> (int8 codes, fp16 scale bits per block)."""
+    x = _c(x, np.float32).reshape(-1)
+    assert x.size % 32 == 0
+    q = np.empty(x.size, np.int8)
+    d = np.empty(x.size // 32, np.uint16)
+    _load().oracle_quantize_q8_0(x.size // 32, _ptr(x), _ptr(q), _ptr(d))
+    return q, d
 
 
 def exp_spec(y: float) -> float:

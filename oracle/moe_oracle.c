@@ -47,6 +47,7 @@
 
 #define ORACLE_FP32 1
 #define ORACLE_BF16 2
+#define ORACLE_W4A8 3
 
 /* IQ4_NL's 16-entry non-linear codebook (model card: IQ4_NL, 4.5 bpw). */
 static const int kIQ4NL[16] = {-127, -104, -83, -65, -49, -35, -22, -10,
@@ -87,6 +88,62 @@ uint16_t oracle_to_bf16(float f) {
   uint32_t pick = lower;
   if (rem > 0x8000u || (rem == 0x8000u && ((lower >> 16) & 1u))) pick = lower + 0x10000u;
   return (uint16_t)(pick >> 16);
+}
+
+/* fp32 -> IEEE binary16, round to nearest, ties to even, by the format's
+ * definition: the representable neighbours are multiples of the spacing of
+ * f's binade (2^(e-10) for normal results, 2^-24 for subnormal ones);
+ * results above the largest finite value round to infinity. */
+uint16_t oracle_to_f16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  double a = fabs((double)f);
+  if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);               /* a = m * 2^e, 0.5 <= m < 1: leading bit 2^(e-1) */
+  int lead = e - 1;           /* exponent of the leading bit */
+  if (lead < -14) lead = -14; /* subnormal range: spacing 2^-24 */
+  double spacing = ldexp(1.0, lead - 10);
+  double k = a / spacing;     /* exact: a is an fp32 value, spacing a power of two */
+  double kf = floor(k);
+  double rem = k - kf;
+  if (rem > 0.5 || (rem == 0.5 && fmod(kf, 2.0) != 0.0)) kf += 1.0;
+  double r = kf * spacing;    /* the rounded magnitude */
+  if (r >= 65536.0 - 16.0) return (uint16_t)(sign | 0x7c00u); /* above 65504 + half a spacing: infinity */
+  /* encode r */
+  if (r < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+  frexp(r, &e);
+  lead = e - 1;
+  uint16_t mant = (uint16_t)(r / ldexp(1.0, lead - 10) - 1024.0);
+  return (uint16_t)(sign | ((uint16_t)(lead + 15) << 10) | mant);
+}
+
+/* ---- Q8_0 activations (the model card's CPU expert path quantizes each
+ * matrix product's activation to Q8_0 -- the ggml block format: 32 values,
+ * one fp16 scale, 32 int8 codes -- and attributes the residual of its
+ * pure-NumPy checks to it; "對純 NumPy：單一 expert" and 整層).  The pages give
+ * the format by name only; the reading here: per block, amax = max |x_j| in
+ * fp32, d32 = amax / 127 (fp32), stored scale d = fp16(d32) (nearest even),
+ * id = 1 / d32 (0 when d32 == 0), q_j = x_j * id rounded to the nearest
+ * integer, halves away from zero (|q_j| <= 127 by construction); the value a
+ * code stands for is d * q_j. */
+void oracle_quantize_q8_0(int64_t n_blocks, const float* x, int8_t* q, uint16_t* d) {
+  for (int64_t b = 0; b < n_blocks; b++) {
+    float amax = 0.0f;
+    for (int j = 0; j < 32; j++) {
+      float v = fabsf(x[32 * b + j]);
+      if (v > amax) amax = v;
+    }
+    float d32 = amax / 127.0f;
+    float id = d32 != 0.0f ? 1.0f / d32 : 0.0f;
+    d[b] = oracle_to_f16(d32);
+    for (int j = 0; j < 32; j++) {
+      float t = x[32 * b + j] * id;
+      q[32 * b + j] = (int8_t)roundf(t);
+    }
+  }
 }
 
 /* ---- IQ4_NL dequantization (model card, parity section: 16-entry lookup
@@ -249,7 +306,68 @@ void oracle_bucket(int T, int K, int E, const int32_t* ids, int32_t* counts, int
  * [gate F x H | up F x H | down H x F] in IQ4_NL blocks, rows in order.
  * Sums in double.  Mode 1: h kept in double.  Mode 2: weights rounded to bf16
  * and h rounded to fp32 then bf16.  y is [H] doubles. */
+/* IQ4_NL block in parts: its scale d (exact, double) and its 32 levels. */
+static double block_levels(const uint8_t* blk, int levels[32]) {
+  uint16_t dh = (uint16_t)(blk[0] | (blk[1] << 8));
+  for (int k = 0; k < 32; k++) {
+    uint8_t byte = blk[2 + (k & 15)];
+    levels[k] = kIQ4NL[k < 16 ? (byte & 15) : (byte >> 4)];
+  }
+  return oracle_f16_value(dh);
+}
+
+/* Row of IQ4_NL blocks dotted with a Q8_0 vector, block by block: the integer
+ * sum s = sum_j level_j * q_j (exact), times d_w * d_x, summed in double. */
+static double dot_w4a8(const uint8_t* row, const int8_t* q, const uint16_t* dq, int n_blocks) {
+  double acc = 0.0;
+  int levels[32];
+  for (int b = 0; b < n_blocks; b++) {
+    double dw = block_levels(row + 18 * b, levels);
+    int64_t s = 0;
+    for (int j = 0; j < 32; j++) s += (int64_t)levels[j] * q[32 * b + j];
+    acc += dw * oracle_f16_value(dq[b]) * (double)s;
+  }
+  return acc;
+}
+
+/* The W4A8 variant of one expert (mode 3): x (bf16, as fp32) quantized to
+ * Q8_0 for gate and up; h = silu(g) * u formed in double, rounded to fp32
+ * and quantized to Q8_0 for down; every product an integer block dot as in
+ * dot_w4a8. */
+static void expert_w4a8(int H, int F, const uint8_t* expert, const uint16_t* x, double* y) {
+  if (H < 32 || F < 32) return;
+  const int64_t mat_bytes = (int64_t)F * (H / 32) * 18;
+  const uint8_t* gate = expert;
+  const uint8_t* up = expert + mat_bytes;
+  const uint8_t* down = expert + 2 * mat_bytes;
+  float* xf = (float*)malloc(sizeof(float) * H);
+  int8_t* xq = (int8_t*)malloc((size_t)H);
+  uint16_t* xd = (uint16_t*)malloc(sizeof(uint16_t) * (H / 32));
+  float* h = (float*)malloc(sizeof(float) * F);
+  int8_t* hq = (int8_t*)malloc((size_t)F);
+  uint16_t* hd = (uint16_t*)malloc(sizeof(uint16_t) * (F / 32));
+  for (int i = 0; i < H; i++) xf[i] = oracle_bf16_value(x[i]);
+  oracle_quantize_q8_0(H / 32, xf, xq, xd);
+  for (int f = 0; f < F; f++) {
+    double g = dot_w4a8(gate + (int64_t)f * (H / 32) * 18, xq, xd, H / 32);
+    double u = dot_w4a8(up + (int64_t)f * (H / 32) * 18, xq, xd, H / 32);
+    h[f] = (float)(g / (1.0 + exp(-g)) * u);
+  }
+  oracle_quantize_q8_0(F / 32, h, hq, hd);
+  for (int n = 0; n < H; n++) y[n] = dot_w4a8(down + (int64_t)n * (F / 32) * 18, hq, hd, F / 32);
+  free(xf);
+  free(xq);
+  free(xd);
+  free(h);
+  free(hq);
+  free(hd);
+}
+
 void oracle_expert(int H, int F, const uint8_t* expert, const uint16_t* x, int mode, double* y) {
+  if (mode == ORACLE_W4A8) {
+    expert_w4a8(H, F, expert, x, y);
+    return;
+  }
   const int64_t mat_bytes = (int64_t)F * (H / 32) * 18;
   const uint8_t* gate = expert;
   const uint8_t* up = expert + mat_bytes;
