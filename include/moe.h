@@ -70,9 +70,17 @@ typedef enum {
  *       product silu(g)*u is rounded to bf16 before the down projection;
  *       products run on bf16 MFMA with fp32 accumulation (batched / prefill
  *       calls: tiles of up to 128 routes of one expert).
+ * W4A8: the exact IQ4_NL weights against activations quantized to Q8_0 --
+ *       the model card's CPU expert path, whose pure-NumPy checks attribute
+ *       their ~1 % residual to this quantization: x and h are quantized per
+ *       token row in blocks of 32 (fp16 scale d = fp16(max|v| / 127), int8
+ *       codes round(v * 127 / max|v|) with halves away from zero), every
+ *       32-weight block is an exact integer dot of levels and codes on int8
+ *       MFMA, scaled by d_w * d_x and accumulated in fp32.  Only when asked
+ *       for (AUTO never picks it); takes the multi-kernel plan at every T.
  * AUTO: FP32 when T*K <= 16*E (at most 16 routes per expert on average;
  *       for a dense block, T <= 16), else BF16.  The router and the combine are fp32 in every mode. */
-typedef enum { MOE_PREC_AUTO = 0, MOE_PREC_FP32 = 1, MOE_PREC_BF16 = 2 } moe_precision;
+typedef enum { MOE_PREC_AUTO = 0, MOE_PREC_FP32 = 1, MOE_PREC_BF16 = 2, MOE_PREC_W4A8 = 3 } moe_precision;
 
 /* Layer shape.  Supported: hidden % 256 == 0, ffn % 128 == 0,
  * 1 <= n_experts <= 256, 1 <= top_k <= min(n_experts, 8), n_shared in {0, 1},
@@ -172,6 +180,12 @@ moe_status moe_pack_experts(const moe_config* cfg, int32_t n_experts, const void
  * lookup times one fp16 scale). */
 moe_status moe_dequant(const moe_config* cfg, const void* packed_expert_dev, int32_t matrix, int32_t precision,
                        float* out_dev, hipStream_t stream);
+
+/* The W4A8 contract's activation quantizer alone: n values (a multiple of 32,
+ * src_bf16 = 1: bf16, 0: fp32) -> Q8_0 blocks of 32: q_dev int8 [n] codes and
+ * d_dev fp16 [n/32] scales, as stated for MOE_PREC_W4A8. */
+moe_status moe_quantize_q8_0(const void* src_dev, int32_t src_bf16, int64_t n, int8_t* q_dev, uint16_t* d_dev,
+                             hipStream_t stream);
 
 /* ---- the layer's steps ---------------------------------------------------- */
 

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3, -4, -5
-PREC_AUTO, PREC_FP32, PREC_BF16 = 0, 1, 2
+PREC_AUTO, PREC_FP32, PREC_BF16, PREC_W4A8 = 0, 1, 2, 3
 MATRIX_GATE, MATRIX_UP, MATRIX_DOWN = 0, 1, 2
 
 
@@ -73,6 +73,7 @@ _SIGS = {
     "moe_layer_forward_chained": ([_cfgp, _i32, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _vp, _sz, _vp], _i32),
     "moe_layer_forward_noalloc": ([_cfgp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp], _i32),
+    "moe_quantize_q8_0": ([_vp, _i32, ctypes.c_int64, _vp, _vp, _vp], _i32),
     "moe_stream_read": ([_vp, _sz, _vp, _vp], _i32),
     "moe_residual_rmsnorm": ([_vp, _vp, _i32, _i32, ctypes.c_float, _vp, _vp], _i32),
 }
@@ -142,6 +143,14 @@ def moe_workspace_status(cfg, T, ws, status, ws_bytes=None, stream=None):
 
 def moe_pack_experts(cfg, n_experts, src, dst, stream=None):
     _check(_lib.moe_pack_experts(ctypes.byref(cfg), n_experts, _p(src), _p(dst), _stream(stream)), "moe_pack_experts")
+
+
+def moe_quantize_q8_0(src, q, d, stream=None):
+    """Q8_0 of a bf16 or fp32 tensor (numel a multiple of 32) into int8 codes q and fp16-bit scales d (int16)."""
+    import torch
+    bf16 = 1 if src.dtype == torch.bfloat16 else 0
+    assert bf16 or src.dtype == torch.float32
+    _check(_lib.moe_quantize_q8_0(_p(src), bf16, src.numel(), _p(q), _p(d), _stream(stream)), "moe_quantize_q8_0")
 
 
 def moe_stream_read(src, nbytes, sink, stream=None):

@@ -38,7 +38,7 @@ moe_status check_cfg(const moe_config* c) {
     if (c->shared_gate && !c->n_shared) return MOE_EUNSUPPORTED;
   }
   if (!isfinite(c->routed_scale)) return MOE_EINVAL;
-  if (c->precision < MOE_PREC_AUTO || c->precision > MOE_PREC_BF16) return MOE_EINVAL;
+  if (c->precision < MOE_PREC_AUTO || c->precision > MOE_PREC_W4A8) return MOE_EINVAL;
   return MOE_OK;
 }
 
@@ -55,7 +55,8 @@ int weight_cols(const moe_config* c) { return c->top_k + c->shared_gate; }
 
 int64_t expert_bytes(const moe_config* c) { return 3 * (int64_t)c->ffn * (c->hidden / 32) * 18; }
 
-// Routes per work chunk of the FFN kernels of each contract.
+// Routes per work chunk of the FFN kernels of each contract (W4A8 uses the
+// exact-weight kernels' chunks).
 int chunk_rows(int precision) { return precision == MOE_PREC_BF16 ? qmoe::kBfRows : 16; }
 
 // Upper bound on the chunks of T tokens: at most one partial chunk per
@@ -84,6 +85,7 @@ struct Plan {
   size_t scores, ids, w;                       // router
   size_t counts, offsets, perm, pos, chunks, n_chunks;  // bucketing
   size_t h_hi, h_lo, y;                        // exact-weight FFN
+  size_t xq, xd, h32, hq, hd;                  // W4A8: Q8_0 x, fp32 h, Q8_0 h
   size_t total;
 };
 
@@ -109,9 +111,16 @@ Plan make_plan(const moe_config* c, int T) {
   const size_t nch = (size_t)max_chunks(c, T);
   p.chunks = take(nch * sizeof(qmoe::Chunk));
   p.n_chunks = take(4);
-  p.h_hi = take((R + S) * F * 2);  // h (bf16 contract) or its high half (exact contract)
-  p.h_lo = take(resolve_precision(c, T) == MOE_PREC_BF16 ? 0 : (R + S) * F * 2);
+  const int prec = resolve_precision(c, T);
+  const bool w4a8 = prec == MOE_PREC_W4A8;
+  p.h_hi = take(w4a8 ? 0 : (R + S) * F * 2);  // h (bf16 contract) or its high half (exact contract)
+  p.h_lo = take(prec == MOE_PREC_FP32 ? (R + S) * F * 2 : 0);
   p.y = take((R + S) * H * 4);
+  p.xq = take(w4a8 ? (size_t)T * H : 0);
+  p.xd = take(w4a8 ? (size_t)T * H / 16 : 0);
+  p.h32 = take(w4a8 ? (R + S) * F * 4 : 0);
+  p.hq = take(w4a8 ? (R + S) * F : 0);
+  p.hd = take(w4a8 ? (R + S) * F / 16 : 0);
   p.total = at;
   return p;
 }
@@ -188,6 +197,13 @@ moe_status run_expert_forward(const moe_config* cfg, int32_t T, const void* x, c
   TRY(launched(qmoe::launch_bucket(ids, T, K, E, cfg->n_shared, chunk_rows(prec), at<int32_t>(ws, p.counts),
                                    at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos),
                                    at<qmoe::Chunk>(ws, p.chunks), at<int32_t>(ws, p.n_chunks), stream)));
+  if (prec == MOE_PREC_W4A8)
+    return launched(qmoe::launch_ffn_w4a8(
+        static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, cfg->shared_gate, max_chunks(cfg, T),
+        static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
+        at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks),
+        at<int32_t>(ws, p.n_chunks), at<int8_t>(ws, p.xq), at<uint16_t>(ws, p.xd), at<float>(ws, p.h32),
+        at<int8_t>(ws, p.hq), at<uint16_t>(ws, p.hd), at<float>(ws, p.y), out, stream));
   if (prec == MOE_PREC_BF16)
     return launched(qmoe::launch_ffn_bf16(
         static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, cfg->shared_gate, max_chunks(cfg, T),
@@ -279,6 +295,16 @@ MOE_API moe_status moe_dequant(const moe_config* cfg, const void* packed_expert_
   const int cols = matrix < 2 ? cfg->hidden : cfg->ffn;
   return launched(qmoe::launch_dequant(static_cast<const uint8_t*>(packed_expert_dev) + matrix * mat_bytes, rows,
                                        cols, precision == MOE_PREC_BF16 ? 1 : 0, out_dev, stream));
+}
+
+MOE_API moe_status moe_quantize_q8_0(const void* src_dev, int32_t src_bf16, int64_t n, int8_t* q_dev,
+                                     uint16_t* d_dev, hipStream_t stream) {
+  if (n < 0 || n % 32 != 0 || (src_bf16 != 0 && src_bf16 != 1)) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  TRY(need(src_dev));
+  TRY(need(q_dev));
+  TRY(need(d_dev));
+  return launched(qmoe::launch_quantize_q8_0(src_dev, src_bf16, n, q_dev, d_dev, stream));
 }
 
 MOE_API moe_status moe_stream_read(const void* src_dev, size_t bytes, uint32_t* sink_dev, hipStream_t stream) {

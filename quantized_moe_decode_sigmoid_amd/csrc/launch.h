@@ -45,6 +45,18 @@ hipError_t launch_ffn_exact(const uint16_t* x, int T, int H, int F, int K, int n
                             const int32_t* pos, const float* w, const Chunk* chunks, const int32_t* n_chunks,
                             uint16_t* h_hi, uint16_t* h_lo, float* y, float* out, hipStream_t stream);
 
+// ---- Q8_0 activations (ffn_w4a8.hip)
+
+// n values (a multiple of 32; bf16 when src_bf16, else fp32) -> Q8_0 codes q [n] and fp16 scales d [n/32]
+hipError_t launch_quantize_q8_0(const void* src, int src_bf16, int64_t n, int8_t* q, uint16_t* d,
+                                hipStream_t stream);
+
+hipError_t launch_ffn_w4a8(const uint16_t* x, int T, int H, int F, int K, int n_shared, int gated, int max_chunks,
+                           const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes, const int32_t* perm,
+                           const int32_t* pos, const float* w, const Chunk* chunks, const int32_t* n_chunks,
+                           int8_t* xq, uint16_t* xd, float* h, int8_t* hq, uint16_t* hd, float* y, float* out,
+                           hipStream_t stream);
+
 // ---- one decode token in two launches (layer_decode.hip)
 
 constexpr int kMaxDecodeK = 4;          // experts per token

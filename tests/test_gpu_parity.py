@@ -196,7 +196,7 @@ def layer_parity(name, T, first=0, sample=None, bias=None, precision=qm.PREC_AUT
     out = dl.forward(to_dev_bf16(x), topk_ids=ids, topk_w=w).cpu().numpy()
     assert_status_ok(cfg, T, dl.workspace(T))
     rows = np.arange(T) if sample is None else np.asarray(sample)
-    mode = oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32
+    mode = {qm.PREC_BF16: oracle.BF16, qm.PREC_W4A8: oracle.W4A8}.get(prec, oracle.FP32)
     ref, rid, rw = oracle.layer(x[rows], inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn,
                                 s.routed_scale, bias, mode)
     assert np.array_equal(ids.cpu().numpy()[rows], rid)
@@ -651,6 +651,71 @@ def test_dense_ffn_block(name, T, precision):
     mode = oracle.BF16 if prec == qm.PREC_BF16 else oracle.FP32
     ref, _, _ = oracle.layer(x, np.zeros((0, s.hidden), np.float32), None, inp["shared"], 0, s.ffn, 1.0, None, mode)
     assert_close(out, ref, f"dense {s.name} T={T}")
+
+
+# ---------------------------------------------------------------- W4A8: Q8_0 activations
+
+def test_quantize_q8_0_bit_exact():
+    """The Q8_0 quantizer against the oracle's, codes and fp16 scales bit for bit: bf16 activations (x) and fp32
+    values (h) of several magnitudes, a zero block, and blocks whose values sit exactly on halfway points."""
+    s, _ = workload("xing4")
+    x = synth.tokens(s, 7, first=77)
+    xd = to_dev_bf16(x)
+    q = torch.empty(x.size, dtype=torch.int8, device="cuda")
+    d = torch.empty(x.size // 32, dtype=torch.int16, device="cuda")
+    log("quantize q8_0 bf16")
+    qm.moe_quantize_q8_0(xd, q, d)
+    xf = (x.astype(np.uint32) << 16).view(np.float32)
+    rq, rd = oracle.quantize_q8_0(xf)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(d.cpu().numpy().view(np.uint16), rd)
+    rng = np.random.default_rng(3)
+    h = (rng.standard_normal(32 * 4096) * np.repeat(10.0 ** rng.uniform(-6, 3, 4096), 32)).astype(np.float32)
+    h[:32] = 0.0
+    h[32:64] = np.arange(32) - 15.5  # every value a half-integer: codes of a non-trivial scale
+    h[64:96] = 0.0
+    h[64] = 127.0
+    h[65:69] = (2.5, -2.5, 0.5, -126.5)  # amax 127: x * (1/1) lands exactly on halves
+    hd = torch.from_numpy(h).cuda()
+    q = torch.empty(h.size, dtype=torch.int8, device="cuda")
+    d = torch.empty(h.size // 32, dtype=torch.int16, device="cuda")
+    log("quantize q8_0 fp32")
+    qm.moe_quantize_q8_0(hd, q, d)
+    rq, rd = oracle.quantize_q8_0(h)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(d.cpu().numpy().view(np.uint16), rd)
+    assert list(rq[64:69]) == [127, 3, -3, 1, -127]
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 37), ("xing4", 1), ("xing4", 5), ("batch", 128),
+                                    ("prefill", 300)])
+def test_layer_w4a8(name, T):
+    """The W4A8 contract (Q8_0 x and h, integer block dots on int8 MFMA) against the oracle's W4A8 mode: routing
+    bit-exact, outputs within tolerance."""
+    layer_parity(name, T, first=40, precision=qm.PREC_W4A8)
+
+
+def test_layer_w4a8_gated_and_dense():
+    s, inp, gw, row = gated_inputs("tiny")
+    cfg = cfg_of(s, qm.PREC_W4A8)
+    cfg.shared_gate = 1
+    dl = qm.DeviceLayer(cfg, gw, None, inp["arena"], inp["shared"])
+    x = synth.tokens(s, 20, first=5)
+    log("w4a8 gated tiny T=20")
+    out = dl.forward(to_dev_bf16(x)).cpu().numpy()
+    ref, _, _ = oracle.layer(x, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn, s.routed_scale, None,
+                             oracle.W4A8, shared_gate=row)
+    assert_close(out, ref, "w4a8 gated tiny T=20")
+    d = synth.WORKLOADS["dense"]
+    dinp = synth.layer_inputs(d)
+    cfg = qm.make_config(d.hidden, d.ffn, 0, 0, 1, 1.0, qm.PREC_W4A8)
+    dl = qm.DeviceLayer(cfg, None, None, None, dinp["shared"])
+    x = synth.tokens(d, 3, first=8)
+    log("w4a8 dense T=3")
+    out = dl.forward(to_dev_bf16(x)).cpu().numpy()
+    ref, _, _ = oracle.layer(x, np.zeros((0, d.hidden), np.float32), None, dinp["shared"], 0, d.ffn, 1.0, None,
+                             oracle.W4A8)
+    assert_close(out, ref, "w4a8 dense T=3")
 
 
 # ---------------------------------------------------------------- the 38-layer stack workload
