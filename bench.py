@@ -13,6 +13,9 @@ Default run (no flags): the four measured workloads in one process, one JSON lin
   * batch (nested): one T=128 call of the Xing4 layer per step.
   * stack (nested): 38 Xing4 layers resident in HBM, T=1 per step through all of them, each
     layer's input chained from the previous one; Zipf(1.1) popularity.
+  * variants (nested): the sigmoid-gated shared expert (decode), the W4A8 contract (Q8_0
+    activations: T=1, T=128, the T=2048 prefill call) and a dense FFN block (hidden 3584,
+    FFN 9216, T=1), each timed and checked against the oracle.
 Every leg times its steps with HIP events on the stream it launches on (median and spread
 over the steps), runs the CPU oracle on a bounded sample of its own inputs (the cpu_baseline),
 compares the GPU rows of those tokens with the oracle's (routing bit-exact, outputs within
@@ -44,7 +47,7 @@ CPU_LABEL = "CPU oracle (reference semantics, double-precision sums), not an opt
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--workload", choices=["all", "decode", "prefill", "stack", "batch"], default="all",
+    p.add_argument("--workload", choices=["all", "decode", "prefill", "stack", "batch", "variants"], default="all",
                    help="all (default): decode line with prefill, batch and stack nested; or one leg alone")
     p.add_argument("--stack-layers", type=int, default=38, help="layers of the stack workload")
     p.add_argument("--stack-distinct", type=int, default=4,
@@ -775,10 +778,215 @@ def run_stack(args, check):
     }
 
 
+# ---------------------------------------------------------------- variants of the layer
+
+MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, vendor figure
+
+
+def run_variants(args, check):
+    """The layer's variants on the Xing4 and prefill shapes, each timed and checked against the oracle:
+    the sigmoid-gated shared expert (decode, T=1), the W4A8 contract (Q8_0 activations; T=1, T=128 and the
+    T=2048 prefill call) and a dense FFN block of the same model (hidden 3584, FFN 9216; T=1)."""
+    import torch
+
+    import quantized_moe_decode_sigmoid_amd as qm
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream()
+    res = {}
+    oracle = None
+    if not args.no_cpu:
+        import oracle
+    n_place, n_tok = 16, 400
+
+    def timed_graph(fn, reps):
+        """Capture fn() once, replay it `reps` times with events on the launching stream; ms per replay."""
+        with torch.cuda.stream(stream):
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn()
+            g.replay()
+            torch.cuda.synchronize()
+            total, per = timed_steps(torch, stream, g.replay, reps)
+        return total / reps, per
+
+    t0 = time.time()
+    shape = synth.WORKLOADS["xing4"]
+    H, E, K, F = shape.hidden, shape.n_experts, shape.top_k, shape.ffn
+    inp = synth.layer_inputs(shape)
+    row = synth.shared_gate_row(shape)
+    x_bits = synth.tokens(shape, n_tok, first=20000)
+    x = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    base = qm.DeviceLayer(qm.make_config(H, F, E, K), inp["gate_w"], None, inp["arena"], inp["shared"])
+    gw1 = torch.from_numpy(np.concatenate([inp["gate_w"], row[None, :]])).to(dev)
+    places = [(gw1.clone(), base.arena.clone(), base.shared.clone()) for _ in range(n_place)]
+    eb = qm.moe_expert_bytes(base.cfg)
+    log(f"variants: inputs ready, {time.time() - t0:.0f} s")
+
+    def decode_sweep(cfg, out, ids, wts, ws, gate_rows):
+        def fn():
+            for i in range(n_tok):
+                g, a, sh = places[i % n_place]
+                qm.moe_layer_forward(cfg, 1, x[i:i + 1], g[:gate_rows], None, a, sh, out[i:i + 1], ids[i:i + 1],
+                                     wts[i], ws)
+        return fn
+
+    n_chk = 16
+    # 1. gated shared expert, decode plan
+    cfg = qm.make_config(H, F, E, K, shared_gate=1)
+    out = torch.empty((n_tok, H), dtype=torch.float32, device=dev)
+    ids = torch.empty((n_tok, K), dtype=torch.int32, device=dev)
+    wts = torch.empty((n_tok, 8), dtype=torch.float32, device=dev)  # K + 1 values per token, rows 16-byte aligned
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device=dev)
+    qm.moe_workspace_init(cfg, 1, ws)
+    ms, per = timed_graph(decode_sweep(cfg, out, ids, wts, ws, E + 1), args.steps)
+    call_us = ms * 1e3 / n_tok
+    nbytes = (K + 1) * eb + (E + 1) * H * 4 + H * 6
+    gated = {"workload": "xing4 decode, T=1, shared expert scaled by sigmoid(x . gate_w[E])",
+             "tok_s": round(n_tok / (ms * 1e-3), 1), "avg_us": round(call_us, 3), "step_spread": spread(per),
+             "roofline": {"bound": "hbm", "achieved": round(nbytes / call_us / 1e3, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(nbytes / call_us / 1e3 / HBM_PEAK_GBS, 4),
+                          "bytes_per_launch": nbytes}}
+    if oracle is not None:
+        want, rid, rw = oracle.layer(x_bits[:n_chk], inp["gate_w"], inp["arena"], inp["shared"], K, F, 2.0,
+                                     shared_gate=row)
+        gated["parity"] = check.compare("variants.gated", out[:n_chk].cpu().numpy(), want, ids[:n_chk].cpu().numpy(),
+                                        rid, wts[:n_chk, :K].cpu().numpy(), rw)
+    gated["parity"] = dict(gated.get("parity") or {}, status_word=check.status("variants.gated",
+                                                                              status_word(torch, qm, cfg, 1, ws)))
+    res["gated_shared_expert"] = gated
+    log("variants: gated done")
+
+    # 2. W4A8, T = 1 (multi-kernel plan) and T = 128
+    w8 = {}
+    cfg = qm.make_config(H, F, E, K, precision=qm.PREC_W4A8)
+    wts = torch.empty((n_tok, K), dtype=torch.float32, device=dev)
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, 128), dtype=torch.uint8, device=dev)
+    ms, per = timed_graph(decode_sweep(cfg, out, ids, wts, ws, E), args.steps)
+    call_us = ms * 1e3 / n_tok
+    nbytes = (K + 1) * eb + E * H * 4 + H * 6
+    w8["decode_t1"] = {"tok_s": round(n_tok / (ms * 1e-3), 1), "avg_us": round(call_us, 3),
+                       "step_spread": spread(per),
+                       "roofline": {"bound": "hbm", "achieved": round(nbytes / call_us / 1e3, 1),
+                                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(nbytes / call_us / 1e3 / HBM_PEAK_GBS, 4)}}
+    if oracle is not None:
+        want, rid, rw = oracle.layer(x_bits[:n_chk], inp["gate_w"], inp["arena"], inp["shared"], K, F, 2.0,
+                                     mode=oracle.W4A8)
+        w8["decode_t1"]["parity"] = check.compare("variants.w4a8_t1", out[:n_chk].cpu().numpy(), want,
+                                                  ids[:n_chk].cpu().numpy(), rid, wts[:n_chk].cpu().numpy(), rw)
+    Tb = 128
+    it = [0]
+
+    def batch_call():
+        g, a, sh = places[it[0] % n_place]
+        it[0] += 1
+        qm.moe_layer_forward(cfg, Tb, x[:Tb], g[:E], None, a, sh, out[:Tb], ids[:Tb], wts[:Tb], ws)
+
+    with torch.cuda.stream(stream):
+        for _ in range(4):
+            batch_call()
+        torch.cuda.synchronize()
+        total, per = timed_steps(torch, stream, batch_call, max(args.steps, 8))
+    call_us = total * 1e3 / max(args.steps, 8)
+    touched = int((np.bincount(ids[:Tb].cpu().numpy().reshape(-1), minlength=E) > 0).sum())
+    nbytes = (touched + 1) * eb + E * H * 4 + Tb * H * 6
+    w8["batch_t128"] = {"tok_s": round(Tb / (call_us * 1e-6), 1), "avg_us": round(call_us, 3),
+                        "step_spread": spread(per),
+                        "roofline": {"bound": "hbm", "achieved": round(nbytes / call_us / 1e3, 1),
+                                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": round(nbytes / call_us / 1e3 / HBM_PEAK_GBS, 4)}}
+    if oracle is not None:
+        want, rid, rw = oracle.layer(x_bits[:Tb], inp["gate_w"], inp["arena"], inp["shared"], K, F, 2.0,
+                                     mode=oracle.W4A8)
+        w8["batch_t128"]["parity"] = check.compare("variants.w4a8_t128", out[:Tb].cpu().numpy(), want,
+                                                   ids[:Tb].cpu().numpy(), rid, wts[:Tb].cpu().numpy(), rw)
+    del places, base
+    torch.cuda.empty_cache()
+    log("variants: w4a8 decode and batch done")
+
+    # W4A8 at the prefill shape, T = 2048
+    pshape = synth.WORKLOADS["prefill"]
+    lam = synth.zipf_lambda(pshape)
+    pin = synth.layer_inputs(pshape, lam=lam)
+    Tp, Hp, Ep, Kp, Fp = pshape.tokens, pshape.hidden, pshape.n_experts, pshape.top_k, pshape.ffn
+    px_bits = synth.tokens(pshape, Tp)
+    px = torch.from_numpy(px_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    pcfg = qm.make_config(Hp, Fp, Ep, Kp, precision=qm.PREC_W4A8)
+    pdl = qm.DeviceLayer(pcfg, pin["gate_w"], pin["bias"], pin["arena"], pin["shared"])
+    pout = torch.empty((Tp, Hp), dtype=torch.float32, device=dev)
+    pids = torch.empty((Tp, Kp), dtype=torch.int32, device=dev)
+    pw = torch.empty((Tp, Kp), dtype=torch.float32, device=dev)
+    pws = pdl.workspace(Tp)
+    with torch.cuda.stream(stream):
+        qm.moe_layer_forward(pcfg, Tp, px, pdl.gate_w, pdl.bias, pdl.arena, pdl.shared, pout, pids, pw, pws)
+        torch.cuda.synchronize()
+
+        def pffn():
+            qm.moe_expert_forward(pcfg, Tp, px, pids, pw, pdl.arena, pdl.shared, pout, pws)
+        pffn()
+        torch.cuda.synchronize()
+        total, per = timed_steps(torch, stream, pffn, max(args.steps, 5))
+    ffn_us = total * 1e3 / max(args.steps, 5)
+    ops = 2.0 * 3 * Hp * Fp * (Tp * Kp + Tp)
+    w8["prefill_t2048"] = {"ffn_us": round(ffn_us, 3), "tops": round(ops / (ffn_us * 1e-6) / 1e12, 2),
+                           "int8_mfma_frac": round(ops / (ffn_us * 1e-6) / 1e12 / MFMA_I8_PEAK_TOPS, 4),
+                           "step_spread": spread(per),
+                           "note": "moe_expert_forward W4A8 (quantize x, gate/up, quantize h, down, combine); int8 "
+                                   "MFMA peak 5.0 POP/s"}
+    if oracle is not None:
+        n = 64
+        want, rid, rw = oracle.layer(px_bits[:n], pin["gate_w"], pin["arena"], pin["shared"], Kp, Fp, 2.0, pin["bias"],
+                                     oracle.W4A8)
+        w8["prefill_t2048"]["parity"] = check.compare("variants.w4a8_prefill", pout[:n].cpu().numpy(), want,
+                                                      pids[:n].cpu().numpy(), rid, pw[:n].cpu().numpy(), rw)
+    res["w4a8"] = w8
+    del pdl, pws
+    torch.cuda.empty_cache()
+    log("variants: w4a8 prefill done")
+
+    # 3. dense FFN block, T = 1 (exact weights, multi-kernel plan)
+    dshape = synth.WORKLOADS["dense"]
+    dinp = synth.layer_inputs(dshape)
+    dcfg = qm.make_config(dshape.hidden, dshape.ffn, 0, 0, 1, 1.0)
+    ddl = qm.DeviceLayer(dcfg, None, None, None, dinp["shared"])
+    dplaces = [ddl.shared.clone() for _ in range(8)]
+    dx_bits = synth.tokens(dshape, 200, first=30000)
+    dx = torch.from_numpy(dx_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    dout = torch.empty((200, dshape.hidden), dtype=torch.float32, device=dev)
+    dws = ddl.workspace(1)
+
+    def dense_sweep():
+        for i in range(200):
+            qm.moe_layer_forward(dcfg, 1, dx[i:i + 1], None, None, None, dplaces[i % 8], dout[i:i + 1], ws=dws)
+
+    ms, per = timed_graph(dense_sweep, args.steps)
+    call_us = ms * 1e3 / 200
+    deb = qm.moe_expert_bytes(dcfg)
+    nbytes = deb + dshape.hidden * 6
+    dense = {"workload": "dense FFN block, T=1: hidden 3584, FFN 9216, IQ4_NL, 8 placements cycled",
+             "tok_s": round(200 / (ms * 1e-3), 1), "avg_us": round(call_us, 3), "step_spread": spread(per),
+             "roofline": {"bound": "hbm", "achieved": round(nbytes / call_us / 1e3, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(nbytes / call_us / 1e3 / HBM_PEAK_GBS, 4),
+                          "bytes_per_launch": nbytes}}
+    if oracle is not None:
+        want, _, _ = oracle.layer(dx_bits[:8], np.zeros((0, dshape.hidden), np.float32), None, dinp["shared"], 0,
+                                  dshape.ffn, 1.0)
+        dense["parity"] = check.compare("variants.dense", dout[:8].cpu().numpy(), want)
+    res["dense_ffn"] = dense
+    log("variants: dense done")
+    return res
+
+
 # ---------------------------------------------------------------- main
 
-LEGS = {"decode": run_decode, "prefill": run_prefill, "batch": run_batch, "stack": run_stack}
-NESTED = ("prefill", "batch", "stack")
+LEGS = {"decode": run_decode, "prefill": run_prefill, "batch": run_batch, "stack": run_stack,
+        "variants": run_variants}
+NESTED = ("prefill", "batch", "stack", "variants")
 
 
 def brief(line):
@@ -795,7 +1003,9 @@ def main():
     if args.copy_mb > 0:
         copy_calibration(args.copy_mb)
     check = Check()
-    if args.workload != "all":
+    if args.workload == "variants":
+        line = {"variants": run_variants(args, check)}
+    elif args.workload != "all":
         line = LEGS[args.workload](args, check)
     else:
         import torch
@@ -805,7 +1015,8 @@ def main():
         for leg in NESTED:
             log(leg)
             try:
-                line[leg] = brief(LEGS[leg](args, check))
+                r = LEGS[leg](args, check)
+                line[leg] = r if leg == "variants" else brief(r)
             except Exception as e:  # the line is still printed; the exit status reports it
                 line[leg] = {"error": f"{type(e).__name__}: {e}"}
                 check.failures.append(f"{leg}: {type(e).__name__}: {e}")
