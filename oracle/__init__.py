@@ -18,6 +18,7 @@ import subprocess
 import numpy as np
 
 FP32, BF16, W4A8 = 1, 2, 3  # precision modes (see moe_oracle.c)
+IQ4_NL, IQ4_XS, Q3_AFFINE = 0, 1, 2  # expert codecs
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
@@ -62,6 +63,13 @@ def _load():
     lib.oracle_bucket.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp]
     lib.oracle_expert.argtypes = [i32, i32, vp, vp, i32, vp]
     lib.oracle_layer.argtypes = [i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.oracle_codec_row_bytes.argtypes = [i32, i32]
+    lib.oracle_codec_row_bytes.restype = i64
+    lib.oracle_codec_expert_bytes.argtypes = [i32, i32, i32]
+    lib.oracle_codec_expert_bytes.restype = i64
+    lib.oracle_dequant_codec.argtypes = [i32, vp, i32, vp]
+    lib.oracle_expert_codec.argtypes = [i32, i32, i32, vp, vp, vp]
+    lib.oracle_layer_codec.argtypes = [i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_layer_gated.argtypes = [i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.oracle_threads.restype = i32
     lib.oracle_set_threads.argtypes = [i32]
@@ -203,9 +211,35 @@ def expert(x_row: np.ndarray, expert_bytes: np.ndarray, hidden: int, ffn: int, m
     return y
 
 
+def codec_row_bytes(codec: int, cols: int) -> int:
+    return _load().oracle_codec_row_bytes(codec, cols)
+
+
+def codec_expert_bytes(codec: int, hidden: int, ffn: int) -> int:
+    return _load().oracle_codec_expert_bytes(codec, hidden, ffn)
+
+
+def dequant_codec(codec: int, row: np.ndarray, cols: int) -> np.ndarray:
+    """One row of `cols` weights in a codec -> float64 (exact)."""
+    row = _c(row, np.uint8).reshape(-1)
+    assert row.size == codec_row_bytes(codec, cols)
+    out = np.empty(cols, np.float64)
+    _load().oracle_dequant_codec(codec, _ptr(row), cols, _ptr(out))
+    return out
+
+
+def expert_codec(x_row: np.ndarray, expert_bytes: np.ndarray, hidden: int, ffn: int, codec: int) -> np.ndarray:
+    x_row = _c(x_row, np.uint16).reshape(-1)
+    expert_bytes = _c(expert_bytes, np.uint8)
+    assert expert_bytes.size == codec_expert_bytes(codec, hidden, ffn)
+    y = np.empty(hidden, np.float64)
+    _load().oracle_expert_codec(hidden, ffn, codec, _ptr(expert_bytes), _ptr(x_row), _ptr(y))
+    return y
+
+
 def layer(x: np.ndarray, gate_w: np.ndarray, arena: np.ndarray | None, shared: np.ndarray | None,
           top_k: int, ffn: int, scale: float = 2.0, bias: np.ndarray | None = None, mode: int = FP32,
-          shared_gate: np.ndarray | None = None):
+          shared_gate: np.ndarray | None = None, codec: int = IQ4_NL):
     """Whole MoE layer.  Returns (out fp32 [T,H], ids int32 [T,K], weights fp32 [T,K]).
 
     gate_w [E,H] (E may be 0 with top_k 0: a dense FFN block, the shared expert alone);
@@ -218,11 +252,16 @@ def layer(x: np.ndarray, gate_w: np.ndarray, arena: np.ndarray | None, shared: n
     bias = _c(bias, np.float32)
     sg = _c(shared_gate, np.float32)
     E = gate_w.shape[0]
-    assert (arena.size if arena is not None else 0) == E * 3 * ffn * H // 32 * 18
+    assert (arena.size if arena is not None else 0) == E * codec_expert_bytes(codec, H, ffn)
     assert sg is None or sg.size == H
     out = np.empty((T, H), np.float32)
     ids = np.empty((T, top_k), np.int32)
     w = np.empty((T, top_k), np.float32)
+    if codec != IQ4_NL:
+        _load().oracle_layer_codec(T, H, ffn, E, top_k, 1 if shared is not None else 0, scale, codec, _ptr(x),
+                                   _ptr(gate_w), _ptr(bias), _ptr(sg), _ptr(arena), _ptr(shared), _ptr(out),
+                                   _ptr(ids), _ptr(w))
+        return out, ids, w
     _load().oracle_layer_gated(T, H, ffn, E, top_k, 1 if shared is not None else 0, scale, mode, _ptr(x),
                                _ptr(gate_w), _ptr(bias), _ptr(sg), _ptr(arena), _ptr(shared), _ptr(out), _ptr(ids),
                                _ptr(w))

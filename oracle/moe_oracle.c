@@ -403,6 +403,125 @@ void oracle_expert(int H, int F, const uint8_t* expert, const uint16_t* x, int m
   free(wd);
 }
 
+/* ---- other expert codecs ------------------------------------------------ */
+
+#define CODEC_IQ4_NL 0
+#define CODEC_IQ4_XS 1
+#define CODEC_Q3_AFFINE 2
+
+/* IQ4_XS (the zLLM feed's "Quantization Is Not a Zip File" and the W7900D
+ * article name it beside IQ4_NL: the same 16-entry non-linear table with a
+ * finer scale hierarchy).  The pages name the format only; the reading is
+ * ggml's definition: a super-block of 256 weights = fp16 d (2 bytes), the
+ * high 2 bits of eight 6-bit sub-block scales (uint16, sub-block i at bits
+ * 2i..2i+1), their low 4 bits (4 bytes, sub-block i in nibble i % 2 of byte
+ * i / 2, low nibble first), then 8 x 16 bytes of indices, each 16 bytes laid
+ * out as an IQ4_NL block (byte j: weight j low nibble, weight j + 16 high).
+ * Weight = d * (ls - 32) * level, with ls the 6-bit sub-block scale: an
+ * 11-bit times a 6-bit times a 7-bit integer, exact in fp32. */
+static void dequant_iq4xs_row(const uint8_t* row, int cols, double* out) {
+  for (int sb = 0; sb < cols / 256; sb++) {
+    const uint8_t* s = row + 136 * sb;
+    double d = oracle_f16_value((uint16_t)(s[0] | (s[1] << 8)));
+    unsigned sh = (unsigned)(s[2] | (s[3] << 8));
+    for (int ib = 0; ib < 8; ib++) {
+      int lo = (s[4 + ib / 2] >> (4 * (ib % 2))) & 15;
+      int hi = (sh >> (2 * ib)) & 3;
+      double dl = d * (double)((lo | (hi << 4)) - 32);
+      const uint8_t* qs = s + 8 + 16 * ib;
+      for (int j = 0; j < 32; j++) {
+        int q = j < 16 ? (qs[j] & 15) : (qs[j - 16] >> 4);
+        out[256 * sb + 32 * ib + j] = dl * (double)kIQ4NL[q];
+      }
+    }
+  }
+}
+
+/* Packed 3-bit affine (the SSD streaming page, section on packed 3-bit
+ * experts: w = scale * q + bias, eight codes in three bytes instead of four,
+ * the same element order as the 4-bit layout; its expert-bytes formula
+ * E = P (b + g) / 8 with g = 0.5 bit of scale data per weight).  Reading: a
+ * group of 64 weights = fp16 scale, fp16 bias, then 24 bytes holding the 64
+ * 3-bit codes q in [0, 7], weight j in bits 3j .. 3j + 2 of the bytes read as
+ * one little-endian bit string (so each 3 bytes hold 8 consecutive weights).
+ * 28 bytes per 64 weights: 3.5 bits per weight. */
+static void dequant_q3_row(const uint8_t* row, int cols, double* out) {
+  for (int g = 0; g < cols / 64; g++) {
+    const uint8_t* s = row + 28 * g;
+    double scale = oracle_f16_value((uint16_t)(s[0] | (s[1] << 8)));
+    double bias = oracle_f16_value((uint16_t)(s[2] | (s[3] << 8)));
+    for (int j = 0; j < 64; j++) {
+      int bit = 3 * j;
+      unsigned two = (unsigned)s[4 + bit / 8] | ((bit / 8 + 1 < 24) ? (unsigned)s[4 + bit / 8 + 1] << 8 : 0u);
+      int q = (two >> (bit % 8)) & 7;
+      out[64 * g + j] = scale * (double)q + bias;
+    }
+  }
+}
+
+/* Bytes of one row of `cols` weights in a codec. */
+int64_t oracle_codec_row_bytes(int codec, int cols) {
+  if (codec == CODEC_IQ4_XS) return (int64_t)cols / 256 * 136;
+  if (codec == CODEC_Q3_AFFINE) return (int64_t)cols / 64 * 28;
+  return (int64_t)cols / 32 * 18;
+}
+
+/* Bytes of one expert ([gate F x H | up F x H | down H x F], rows in order). */
+int64_t oracle_codec_expert_bytes(int codec, int H, int F) {
+  return 2 * (int64_t)F * oracle_codec_row_bytes(codec, H) + (int64_t)H * oracle_codec_row_bytes(codec, F);
+}
+
+/* Weights of one row, exact, in double. */
+void oracle_dequant_codec(int codec, const uint8_t* row, int cols, double* out) {
+  if (codec == CODEC_IQ4_XS) {
+    dequant_iq4xs_row(row, cols, out);
+  } else if (codec == CODEC_Q3_AFFINE) {
+    dequant_q3_row(row, cols, out);
+  } else {
+    for (int b = 0; b < cols / 32; b++)
+      for (int k = 0; k < 32; k++) out[32 * b + k] = block_weight(row + 18 * b, k, ORACLE_FP32);
+  }
+}
+
+/* One expert in another codec (FP32 contract: exact weights, h in double). */
+static void expert_codec(int H, int F, int codec, const uint8_t* expert, const uint16_t* x, double* y) {
+  const int64_t rbh = oracle_codec_row_bytes(codec, H), rbf = oracle_codec_row_bytes(codec, F);
+  const uint8_t* gate = expert;
+  const uint8_t* up = expert + F * rbh;
+  const uint8_t* down = expert + 2 * F * rbh;
+  double* xv = (double*)malloc(sizeof(double) * H);
+  double* h = (double*)malloc(sizeof(double) * F);
+  double* wg = (double*)malloc(sizeof(double) * H);
+  double* wu = (double*)malloc(sizeof(double) * H);
+  double* wd = (double*)malloc(sizeof(double) * F);
+  for (int i = 0; i < H; i++) xv[i] = oracle_bf16_value(x[i]);
+  for (int f = 0; f < F; f++) {
+    oracle_dequant_codec(codec, gate + f * rbh, H, wg);
+    oracle_dequant_codec(codec, up + f * rbh, H, wu);
+    double g = 0.0, u = 0.0;
+    for (int i = 0; i < H; i++) {
+      g += wg[i] * xv[i];
+      u += wu[i] * xv[i];
+    }
+    h[f] = g / (1.0 + exp(-g)) * u;
+  }
+  for (int n = 0; n < H; n++) {
+    oracle_dequant_codec(codec, down + n * rbf, F, wd);
+    double acc = 0.0;
+    for (int f = 0; f < F; f++) acc += wd[f] * h[f];
+    y[n] = acc;
+  }
+  free(xv);
+  free(h);
+  free(wg);
+  free(wu);
+  free(wd);
+}
+
+void oracle_expert_codec(int H, int F, int codec, const uint8_t* expert, const uint16_t* x, double* y) {
+  expert_codec(H, F, codec, expert, x, y);
+}
+
 /* ---- whole layer -------------------------------------------------------- */
 
 /* out[t] = sum over slots k (ascending) of w[t][k] * y_{ids[t][k]}(x_t)
@@ -423,11 +542,32 @@ void oracle_expert(int H, int F, const uint8_t* expert, const uint16_t* x, int m
  * "Model and routing": hidden / dense FFN / expert FFN 3584 / 9216 / 1024, the
  * two leading dense blocks): no routing, out[t] = y_shared(x_t).
  * ids_out / w_out may be NULL. */
+static void layer_any(int T, int H, int F, int E, int K, int n_shared, float scale, int mode, int codec,
+                      const uint16_t* x, const float* Wg, const float* bias, const float* shared_gate,
+                      const uint8_t* arena, const uint8_t* shared, float* out, int32_t* ids_out, float* w_out);
+
 void oracle_layer_gated(int T, int H, int F, int E, int K, int n_shared, float scale, int mode,
                         const uint16_t* x, const float* Wg, const float* bias, const float* shared_gate,
                         const uint8_t* arena, const uint8_t* shared, float* out, int32_t* ids_out,
                         float* w_out) {
-  const int64_t eb = 3 * (int64_t)F * (H / 32) * 18;
+  layer_any(T, H, F, E, K, n_shared, scale, mode, CODEC_IQ4_NL, x, Wg, bias, shared_gate, arena, shared, out, ids_out,
+            w_out);
+}
+
+/* The layer with experts in another codec (codec 1 IQ4_XS, 2 packed 3-bit
+ * affine; FP32 contract only: mode is ignored). */
+void oracle_layer_codec(int T, int H, int F, int E, int K, int n_shared, float scale, int codec,
+                        const uint16_t* x, const float* Wg, const float* bias, const float* shared_gate,
+                        const uint8_t* arena, const uint8_t* shared, float* out, int32_t* ids_out,
+                        float* w_out) {
+  layer_any(T, H, F, E, K, n_shared, scale, ORACLE_FP32, codec, x, Wg, bias, shared_gate, arena, shared, out, ids_out,
+            w_out);
+}
+
+static void layer_any(int T, int H, int F, int E, int K, int n_shared, float scale, int mode, int codec,
+                      const uint16_t* x, const float* Wg, const float* bias, const float* shared_gate,
+                      const uint8_t* arena, const uint8_t* shared, float* out, int32_t* ids_out, float* w_out) {
+  const int64_t eb = oracle_codec_expert_bytes(codec, H, F);
   int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * ((size_t)T * K + 1));
   float* w = (float*)malloc(sizeof(float) * ((size_t)T * K + 1));
   float* g = (float*)malloc(sizeof(float) * ((size_t)T + 1));
@@ -447,12 +587,18 @@ void oracle_layer_gated(int T, int H, int F, int E, int K, int n_shared, float s
     for (int k = 0; k < K; k++) {
       int e = ids[(int64_t)t * K + k];
       double wk = w[(int64_t)t * K + k];
-      oracle_expert(H, F, arena + e * eb, xt, mode, y);
+      if (codec == CODEC_IQ4_NL)
+        oracle_expert(H, F, arena + e * eb, xt, mode, y);
+      else
+        expert_codec(H, F, codec, arena + e * eb, xt, y);
       for (int n = 0; n < H; n++) acc[n] += wk * y[n];
     }
     if (n_shared) {
       const double gs = shared_gate ? (double)g[t] : 1.0;
-      oracle_expert(H, F, shared, xt, mode, y);
+      if (codec == CODEC_IQ4_NL)
+        oracle_expert(H, F, shared, xt, mode, y);
+      else
+        expert_codec(H, F, codec, shared, xt, y);
       for (int n = 0; n < H; n++) acc[n] += gs * y[n];
     }
     for (int n = 0; n < H; n++) out[(int64_t)t * H + n] = (float)acc[n];

@@ -679,3 +679,124 @@ def test_w4a8_residual_matches_the_pages_range():
         corr = float(np.corrcoef(a, b)[0, 1])
         assert lo <= max_rel <= hi, max_rel
         assert corr >= 0.9999, corr
+
+
+# ---------------------------------------------------------------- other codecs: IQ4_XS, packed 3-bit affine
+
+def _iq4xs_superblock(d, ls, nib):
+    """Build a 136-byte IQ4_XS super-block by hand from the format's description: fp16 d, the high 2 bits of
+    each 6-bit sub-block scale at bits 2i of a uint16, the low 4 bits in nibble i%2 of byte i/2, then 8 blocks
+    of 16 bytes of indices (IQ4_NL order)."""
+    out = np.zeros(136, np.uint8)
+    out[:2] = np.frombuffer(np.float16(d).tobytes(), np.uint8)
+    sh = sum(((int(v) >> 4) & 3) << (2 * i) for i, v in enumerate(ls))
+    out[2:4] = (sh & 255, sh >> 8)
+    for i, v in enumerate(ls):
+        out[4 + i // 2] |= (int(v) & 15) << (4 * (i % 2))
+    for ib in range(8):
+        q = np.asarray(nib[ib], np.uint8)
+        out[8 + 16 * ib: 24 + 16 * ib] = q[:16] | (q[16:] << 4)
+    return out
+
+
+def test_iq4xs_hand_built_superblock():
+    """Eight distinct sub-block scales (each bit of the split 6-bit field used) and known indices: every weight
+    is d * (ls - 32) * level, exact in fp32."""
+    levels = golden("iq4nl_codebook.json")["levels"]
+    rng = np.random.default_rng(9)
+    ls = [0, 63, 32, 1, 17, 40, 50, 9]
+    nib = [rng.integers(0, 16, 32) for _ in range(8)]
+    blk = _iq4xs_superblock(0.5, ls, nib)
+    w = oracle.dequant_codec(oracle.IQ4_XS, blk, 256)
+    want = np.array([0.5 * (ls[ib] - 32) * levels[nib[ib][j]] for ib in range(8) for j in range(32)])
+    assert np.array_equal(w, want)
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)  # exact in fp32
+    # 136 bytes per 256 weights: 4.25 bits per weight
+    assert oracle.codec_row_bytes(oracle.IQ4_XS, 256) * 8 / 256 == 4.25
+
+
+def test_iq4xs_expert_equals_iq4nl_expert_when_scales_coincide():
+    """An IQ4_XS expert whose sub-block scales d * (ls - 32) are fp16 values gives exactly the IQ4_NL expert
+    with those scales and the same indices (the IQ4_NL expert is pinned above)."""
+    rng = np.random.default_rng(10)
+    H, F = 256, 256
+    x = _bf16_bits(rng.standard_normal(H))
+
+    def rows(n, cols):
+        xs, nl = [], []
+        for _ in range(n):
+            for sb in range(cols // 256):
+                ls = rng.integers(20, 45, 8)
+                nib = [rng.integers(0, 16, 32) for _ in range(8)]
+                d = 2.0 ** -9
+                xs.append(_iq4xs_superblock(d, ls, nib))
+                for ib in range(8):
+                    nl.append(pack_block(np.float16(d * (int(ls[ib]) - 32)), nib[ib]))
+        return np.concatenate(xs), np.concatenate(nl)
+
+    gx, gn = rows(F, H)
+    ux, un = rows(F, H)
+    dx, dn = rows(H, F)
+    y_xs = oracle.expert_codec(x, np.concatenate([gx, ux, dx]), H, F, oracle.IQ4_XS)
+    y_nl = oracle.expert(x, np.concatenate([gn, un, dn]), H, F)
+    assert np.allclose(y_xs, y_nl, rtol=1e-12, atol=1e-15)
+
+
+def _q3_group(scale, bias, codes):
+    """A 28-byte packed 3-bit group: fp16 scale, fp16 bias, the 64 codes as one little-endian bit string."""
+    out = np.zeros(28, np.uint8)
+    out[:2] = np.frombuffer(np.float16(scale).tobytes(), np.uint8)
+    out[2:4] = np.frombuffer(np.float16(bias).tobytes(), np.uint8)
+    bits = np.zeros(192, np.uint8)
+    for j, c in enumerate(codes):
+        bits[3 * j:3 * j + 3] = [(int(c) >> k) & 1 for k in range(3)]
+    out[4:] = np.packbits(bits, bitorder="little")
+    return out
+
+
+def test_q3_affine_group_and_size():
+    """Hand-built groups (codes in every position and value, both signs of scale and bias): weight =
+    scale * q + bias; 28 bytes per 64 weights, and an expert is 7/9 of an IQ4_NL expert -- the SSD streaming
+    page's packed-3-bit factor for E = P (b + g) / 8 with b = 3 instead of 4 and g = 0.5."""
+    rng = np.random.default_rng(11)
+    for scale, bias in ((0.25, -1.0), (-0.0078125, 0.5), (3.0, 0.0)):
+        codes = rng.integers(0, 8, 64)
+        codes[:8] = np.arange(8)
+        w = oracle.dequant_codec(oracle.Q3_AFFINE, _q3_group(scale, bias, codes), 64)
+        assert np.array_equal(w, scale * codes.astype(np.float64) + bias)
+    assert oracle.codec_row_bytes(oracle.Q3_AFFINE, 64) == 28
+    nl = oracle.codec_expert_bytes(oracle.IQ4_NL, 3584, 1024)
+    q3 = oracle.codec_expert_bytes(oracle.Q3_AFFINE, 3584, 1024)
+    assert Fraction(q3, nl) == Fraction(7, 9)
+
+
+def test_q3_affine_expert_against_independent_decode():
+    """A packed 3-bit expert against a numpy evaluation of the same FFN with weights unpacked here by numpy's
+    own bit routine (np.unpackbits, little bit order)."""
+    rng = np.random.default_rng(12)
+    H, F = 256, 128
+
+    def mat(rows, cols):
+        g = []
+        for _ in range(rows * cols // 64):
+            g.append(_q3_group(float(rng.uniform(0.001, 0.01)), float(rng.uniform(-0.02, 0.02)),
+                               rng.integers(0, 8, 64)))
+        return np.concatenate(g)
+
+    def unpack(m, rows, cols):
+        gr = m.reshape(-1, 28)
+        sc = gr[:, :2].copy().view(np.float16).astype(np.float64)
+        bi = gr[:, 2:4].copy().view(np.float16).astype(np.float64)
+        bits = np.unpackbits(gr[:, 4:], axis=1, bitorder="little").reshape(-1, 64, 3).astype(np.int64)
+        q = bits[:, :, 0] + 2 * bits[:, :, 1] + 4 * bits[:, :, 2]
+        return (sc * q + bi).reshape(rows, cols)
+
+    gate, up, down = mat(F, H), mat(F, H), mat(H, F)
+    x = _bf16_bits(rng.standard_normal(H))
+    xv = bf16_bits_to_f64(x)
+    g = unpack(gate, F, H) @ xv
+    u = unpack(up, F, H) @ xv
+    h = g / (1.0 + np.exp(-g)) * u
+    want = unpack(down, H, F) @ h
+    got = oracle.expert_codec(x, np.concatenate([gate, up, down]), H, F, oracle.Q3_AFFINE)
+    assert np.allclose(got, want, rtol=1e-10, atol=1e-13)
