@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Status codes. */
 typedef enum {
@@ -82,6 +82,23 @@ typedef enum {
  *       for a dense block, T <= 16), else BF16.  The router and the combine are fp32 in every mode. */
 typedef enum { MOE_PREC_AUTO = 0, MOE_PREC_FP32 = 1, MOE_PREC_BF16 = 2, MOE_PREC_W4A8 = 3 } moe_precision;
 
+/* Expert weight codecs (input layout of moe_pack_experts, per expert
+ * [gate F x H | up F x H | down H x F], rows in order):
+ * IQ4_NL    18-byte blocks of 32 weights (see "expert arena" below).
+ * IQ4_XS    136-byte super-blocks of 256 weights: fp16 d, uint16 with the high
+ *           2 bits of eight 6-bit sub-block scales ls (sub-block i at bits 2i),
+ *           4 bytes with their low 4 bits (nibble i % 2 of byte i / 2, low
+ *           first), then 8 x 16 index bytes in IQ4_NL order; weight =
+ *           d * (ls - 32) * level (named beside IQ4_NL by the zLLM feed,
+ *           "Quantization Is Not a Zip File"; ggml's layout).  Needs ffn % 256.
+ * Q3_AFFINE 28-byte groups of 64 weights: fp16 scale, fp16 bias, then 24 bytes
+ *           of 3-bit codes q, weight j in bits 3j..3j+2 of the little-endian
+ *           bit string; weight = scale * q + bias (the SSD streaming page,
+ *           packed 3-bit section: 8 codes in 3 bytes, 3.5 bits per weight).
+ * IQ4_XS and Q3_AFFINE run the exact-weight (FP32) contract on the
+ * multi-kernel plan at every T (precision AUTO or FP32 only). */
+typedef enum { MOE_CODEC_IQ4_NL = 0, MOE_CODEC_IQ4_XS = 1, MOE_CODEC_Q3_AFFINE = 2 } moe_codec;
+
 /* Layer shape.  Supported: hidden % 256 == 0, ffn % 128 == 0,
  * 1 <= n_experts <= 256, 1 <= top_k <= min(n_experts, 8), n_shared in {0, 1},
  * routed_scale finite.  Tokens per call: 0 <= T <= 65536.
@@ -109,6 +126,7 @@ typedef struct {
   float routed_scale;  /* multiplies the normalised routed weights (2.0) */
   int32_t precision;   /* moe_precision */
   int32_t shared_gate; /* 1: the shared expert is scaled by sigmoid(x . gate_w[E]); 0: weight 1 */
+  int32_t codec;       /* moe_codec of the expert weights */
 } moe_config;
 
 /* ---- queries (host only, no GPU work) ----------------------------------- */
@@ -121,10 +139,17 @@ const char* moe_status_string(int status);
 /* MOE_OK if the shape is supported, else MOE_EINVAL / MOE_EUNSUPPORTED. */
 moe_status moe_check_config(const moe_config* cfg);
 
-/* Bytes of one expert in either layout: 3 matrices of F*H/32 IQ4_NL blocks of
- * 18 bytes (the model card's 6,193,152 B for H=3584, F=1024).  0 if the
- * configuration is invalid. */
+/* Bytes of one expert in its codec's input layout: for IQ4_NL 3 matrices of
+ * F*H/32 blocks of 18 bytes (the model card's 6,193,152 B for H=3584,
+ * F=1024).  0 if the configuration is invalid. */
 size_t moe_expert_bytes(const moe_config* cfg);
+
+/* Bytes of one expert in the packed layout (what moe_pack_experts writes and
+ * the compute entry points read, expert e at e * this): moe_expert_bytes for
+ * IQ4_NL and Q3_AFFINE; for IQ4_XS 1120 bytes per 16 x 128 tile, 32 more than
+ * the format (each of a super-block's two tiles repeats its d).  0 if the
+ * configuration is invalid. */
+size_t moe_packed_expert_bytes(const moe_config* cfg);
 
 /* Precision the expert FFN will use for T tokens (resolves AUTO). */
 int32_t moe_resolved_precision(const moe_config* cfg, int32_t T);

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 MOE_OK, MOE_EINVAL, MOE_EALIGN, MOE_EWORKSPACE, MOE_EUNSUPPORTED, MOE_ELAUNCH = 0, -1, -2, -3, -4, -5
 PREC_AUTO, PREC_FP32, PREC_BF16, PREC_W4A8 = 0, 1, 2, 3
 MATRIX_GATE, MATRIX_UP, MATRIX_DOWN = 0, 1, 2
+CODEC_IQ4_NL, CODEC_IQ4_XS, CODEC_Q3_AFFINE = 0, 1, 2
 
 
 class MoeError(RuntimeError):
@@ -29,12 +30,13 @@ class MoeError(RuntimeError):
 class moe_config(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("routed_scale", ctypes.c_float),
-                ("precision", ctypes.c_int32), ("shared_gate", ctypes.c_int32)]
+                ("precision", ctypes.c_int32), ("shared_gate", ctypes.c_int32), ("codec", ctypes.c_int32)]
 
 
 def make_config(hidden: int, ffn: int, n_experts: int, top_k: int, n_shared: int = 1,
-                routed_scale: float = 2.0, precision: int = PREC_AUTO, shared_gate: int = 0) -> moe_config:
-    return moe_config(hidden, ffn, n_experts, top_k, n_shared, routed_scale, precision, shared_gate)
+                routed_scale: float = 2.0, precision: int = PREC_AUTO, shared_gate: int = 0,
+                codec: int = 0) -> moe_config:
+    return moe_config(hidden, ffn, n_experts, top_k, n_shared, routed_scale, precision, shared_gate, codec)
 
 
 def weight_cols(cfg: moe_config) -> int:
@@ -59,6 +61,7 @@ _SIGS = {
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "moe_check_config": ([_cfgp], _i32),
     "moe_expert_bytes": ([_cfgp], _sz),
+    "moe_packed_expert_bytes": ([_cfgp], _sz),
     "moe_resolved_precision": ([_cfgp, _i32], _i32),
     "moe_workspace_bytes": ([_cfgp, _i32], _sz),
     "moe_workspace_init": ([_cfgp, _i32, _vp, _sz, _vp], _i32),
@@ -119,6 +122,10 @@ def moe_check_config(cfg: moe_config) -> int:
 
 def moe_expert_bytes(cfg: moe_config) -> int:
     return _lib.moe_expert_bytes(ctypes.byref(cfg))
+
+
+def moe_packed_expert_bytes(cfg: moe_config) -> int:
+    return _lib.moe_packed_expert_bytes(ctypes.byref(cfg))
 
 
 def moe_resolved_precision(cfg: moe_config, T: int) -> int:
@@ -238,18 +245,18 @@ class DeviceLayer:
         if self.gate_w is not None:
             assert self.gate_w.shape[0] == cfg.n_experts + cfg.shared_gate
         self.bias = None if bias is None else dev(bias, torch.float32)
-        eb = moe_expert_bytes(cfg)
+        eb, pb = moe_expert_bytes(cfg), moe_packed_expert_bytes(cfg)
         self.arena = None
         if cfg.n_experts:
             src = dev(arena, torch.uint8)
             assert src.numel() == eb * cfg.n_experts
-            self.arena = torch.empty_like(src)
+            self.arena = torch.empty(pb * cfg.n_experts, dtype=torch.uint8, device=device)
             moe_pack_experts(cfg, cfg.n_experts, src, self.arena)
         self.shared = None
         if cfg.n_shared:
             ssrc = dev(shared, torch.uint8)
             assert ssrc.numel() == eb
-            self.shared = torch.empty_like(ssrc)
+            self.shared = torch.empty(pb, dtype=torch.uint8, device=device)
             moe_pack_experts(cfg, 1, ssrc, self.shared)
         self._ws = None
 

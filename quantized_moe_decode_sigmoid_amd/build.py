@@ -13,7 +13,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 SOURCES = ["api.cpp", "router.hip", "bucket.hip", "ffn_exact.hip", "ffn_bf16.hip", "layer_decode.hip", "stream.hip",
-           "chain.hip", "noalloc.hip", "ffn_w4a8.hip"]
+           "chain.hip", "noalloc.hip", "ffn_w4a8.hip", "ffn_codec.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are kept out of every kernel: hipcc otherwise forms

@@ -28,6 +28,12 @@ moe_status check_cfg(const moe_config* c) {
   if (c->shared_gate != 0 && c->shared_gate != 1) return MOE_EINVAL;
   if (c->hidden % 256 != 0 || c->hidden > kMaxHidden) return MOE_EUNSUPPORTED;
   if (c->ffn % 128 != 0 || c->ffn > 65536) return MOE_EUNSUPPORTED;
+  if (c->codec < MOE_CODEC_IQ4_NL || c->codec > MOE_CODEC_Q3_AFFINE) return MOE_EINVAL;
+  if (c->codec != MOE_CODEC_IQ4_NL) {
+    // the other codecs run the exact-weight (FP32) kernels only
+    if (c->precision != MOE_PREC_AUTO && c->precision != MOE_PREC_FP32) return MOE_EUNSUPPORTED;
+    if (c->codec == MOE_CODEC_IQ4_XS && c->ffn % 256 != 0) return MOE_EUNSUPPORTED;  // down rows: 256-weight blocks
+  }
   if (c->n_experts > 256) return MOE_EUNSUPPORTED;
   if (c->n_experts == 0) {
     // a dense FFN block: the always-on expert alone, nothing to route or gate
@@ -45,6 +51,7 @@ moe_status check_cfg(const moe_config* c) {
 // AUTO: the exact-weight contract while an expert serves at most 16 routes on
 // average (a dense block: its one expert at most 16 tokens), else bf16 tiles.
 int resolve_precision(const moe_config* c, int T) {
+  if (c->codec != MOE_CODEC_IQ4_NL) return MOE_PREC_FP32;
   if (c->precision != MOE_PREC_AUTO) return c->precision;
   if (c->n_experts == 0) return T <= 16 ? MOE_PREC_FP32 : MOE_PREC_BF16;
   return (int64_t)T * c->top_k <= 16 * (int64_t)c->n_experts ? MOE_PREC_FP32 : MOE_PREC_BF16;
@@ -53,7 +60,20 @@ int resolve_precision(const moe_config* c, int T) {
 // Values per row of the routing weights: K, plus the shared expert's gate.
 int weight_cols(const moe_config* c) { return c->top_k + c->shared_gate; }
 
-int64_t expert_bytes(const moe_config* c) { return 3 * (int64_t)c->ffn * (c->hidden / 32) * 18; }
+// Bytes of one expert in the codec's own (input) layout.
+int64_t expert_bytes(const moe_config* c) {
+  const int64_t w = 3 * (int64_t)c->ffn * c->hidden;
+  if (c->codec == MOE_CODEC_IQ4_XS) return w / 256 * 136;
+  if (c->codec == MOE_CODEC_Q3_AFFINE) return w / 64 * 28;
+  return w / 32 * 18;
+}
+
+// Bytes of one expert in the packed layout the kernels read (IQ4_XS repeats a
+// super-block's d in both of its tiles).
+int64_t packed_expert_bytes(const moe_config* c) {
+  if (c->codec == MOE_CODEC_IQ4_NL) return expert_bytes(c);
+  return 3 * (int64_t)(c->ffn / 16) * (c->hidden / 128) * qmoe::codec_tile_bytes(c->codec);
+}
 
 // Routes per work chunk of the FFN kernels of each contract (W4A8 uses the
 // exact-weight kernels' chunks).
@@ -73,7 +93,7 @@ int max_chunks(const moe_config* c, int T) { return max_chunks(c, T, chunk_rows(
 // Its second kernel hands data between workgroups, so it is taken only when
 // the device holds that kernel's whole grid at once.
 bool decode_path(const moe_config* c, int T) {
-  return T == 1 && c->n_experts > 0 && c->top_k <= qmoe::kMaxDecodeK && c->ffn <= qmoe::kMaxDecodeFfn &&
+  return T == 1 && c->n_experts > 0 && c->codec == MOE_CODEC_IQ4_NL && c->top_k <= qmoe::kMaxDecodeK && c->ffn <= qmoe::kMaxDecodeFfn &&
          c->hidden <= qmoe::kMaxDecodeHidden && resolve_precision(c, T) == MOE_PREC_FP32 &&
          qmoe::decode_grid_coresident(c->ffn, c->top_k, c->hidden, c->n_shared);
 }
@@ -197,22 +217,29 @@ moe_status run_expert_forward(const moe_config* cfg, int32_t T, const void* x, c
   TRY(launched(qmoe::launch_bucket(ids, T, K, E, cfg->n_shared, chunk_rows(prec), at<int32_t>(ws, p.counts),
                                    at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos),
                                    at<qmoe::Chunk>(ws, p.chunks), at<int32_t>(ws, p.n_chunks), stream)));
+  if (cfg->codec != MOE_CODEC_IQ4_NL)
+    return launched(qmoe::launch_ffn_codec(
+        cfg->codec, static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, cfg->shared_gate, max_chunks(cfg, T),
+        static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), packed_expert_bytes(cfg),
+        at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks),
+        at<int32_t>(ws, p.n_chunks), at<uint16_t>(ws, p.h_hi), at<uint16_t>(ws, p.h_lo), at<float>(ws, p.y), out,
+        stream));
   if (prec == MOE_PREC_W4A8)
     return launched(qmoe::launch_ffn_w4a8(
         static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, cfg->shared_gate, max_chunks(cfg, T),
-        static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
+        static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), packed_expert_bytes(cfg),
         at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks),
         at<int32_t>(ws, p.n_chunks), at<int8_t>(ws, p.xq), at<uint16_t>(ws, p.xd), at<float>(ws, p.h32),
         at<int8_t>(ws, p.hq), at<uint16_t>(ws, p.hd), at<float>(ws, p.y), out, stream));
   if (prec == MOE_PREC_BF16)
     return launched(qmoe::launch_ffn_bf16(
         static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, cfg->shared_gate, max_chunks(cfg, T),
-        static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
+        static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), packed_expert_bytes(cfg),
         at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks),
         at<int32_t>(ws, p.n_chunks), at<uint16_t>(ws, p.h_hi), at<float>(ws, p.y), out, stream));
   return launched(qmoe::launch_ffn_exact(
       static_cast<const uint16_t*>(x), T, H, F, K, cfg->n_shared, cfg->shared_gate, max_chunks(cfg, T),
-      static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), expert_bytes(cfg),
+      static_cast<const uint8_t*>(arena), static_cast<const uint8_t*>(shared), packed_expert_bytes(cfg),
       at<int32_t>(ws, p.perm), at<int32_t>(ws, p.pos), w, at<qmoe::Chunk>(ws, p.chunks), at<int32_t>(ws, p.n_chunks),
       at<uint16_t>(ws, p.h_hi), at<uint16_t>(ws, p.h_lo), at<float>(ws, p.y), out, stream));
 }
@@ -237,6 +264,10 @@ MOE_API moe_status moe_check_config(const moe_config* cfg) { return check_cfg(cf
 
 MOE_API size_t moe_expert_bytes(const moe_config* cfg) {
   return check_cfg(cfg) == MOE_OK ? (size_t)expert_bytes(cfg) : 0;
+}
+
+MOE_API size_t moe_packed_expert_bytes(const moe_config* cfg) {
+  return check_cfg(cfg) == MOE_OK ? (size_t)packed_expert_bytes(cfg) : 0;
 }
 
 MOE_API int32_t moe_resolved_precision(const moe_config* cfg, int32_t T) {
@@ -277,8 +308,12 @@ MOE_API moe_status moe_pack_experts(const moe_config* cfg, int32_t n_experts, co
   TRY(need(dst_dev));
   const char* s = static_cast<const char*>(src_dev);
   const char* d = static_cast<const char*>(dst_dev);
-  const int64_t bytes = (int64_t)n_experts * expert_bytes(cfg);
-  if (s < d + bytes && d < s + bytes) return MOE_EINVAL;  // overlap
+  const int64_t sbytes = (int64_t)n_experts * expert_bytes(cfg), dbytes = (int64_t)n_experts * packed_expert_bytes(cfg);
+  if (s < d + dbytes && d < s + sbytes) return MOE_EINVAL;  // overlap
+  if (cfg->codec != MOE_CODEC_IQ4_NL)
+    return launched(qmoe::launch_pack_codec(cfg->codec, static_cast<const uint8_t*>(src_dev),
+                                            static_cast<uint8_t*>(dst_dev), n_experts, cfg->hidden, cfg->ffn,
+                                            expert_bytes(cfg), packed_expert_bytes(cfg), stream));
   return launched(qmoe::launch_pack(static_cast<const uint8_t*>(src_dev), static_cast<uint8_t*>(dst_dev), n_experts,
                                     cfg->hidden, cfg->ffn, stream));
 }
@@ -290,9 +325,15 @@ MOE_API moe_status moe_dequant(const moe_config* cfg, const void* packed_expert_
   if (precision != MOE_PREC_FP32 && precision != MOE_PREC_BF16) return MOE_EINVAL;
   TRY(need(packed_expert_dev));
   TRY(need(out_dev));
-  const int64_t mat_bytes = expert_bytes(cfg) / 3;
+  const int64_t mat_bytes = packed_expert_bytes(cfg) / 3;
   const int rows = matrix < 2 ? cfg->ffn : cfg->hidden;
   const int cols = matrix < 2 ? cfg->hidden : cfg->ffn;
+  if (cfg->codec != MOE_CODEC_IQ4_NL) {
+    if (precision != MOE_PREC_FP32) return MOE_EUNSUPPORTED;
+    return launched(qmoe::launch_dequant_codec(cfg->codec, static_cast<const uint8_t*>(packed_expert_dev) +
+                                                               matrix * mat_bytes,
+                                               rows, cols, out_dev, stream));
+  }
   return launched(qmoe::launch_dequant(static_cast<const uint8_t*>(packed_expert_dev) + matrix * mat_bytes, rows,
                                        cols, precision == MOE_PREC_BF16 ? 1 : 0, out_dev, stream));
 }

@@ -57,6 +57,21 @@ hipError_t launch_ffn_w4a8(const uint16_t* x, int T, int H, int F, int K, int n_
                            int8_t* xq, uint16_t* xd, float* h, int8_t* hq, uint16_t* hd, float* y, float* out,
                            hipStream_t stream);
 
+// ---- other expert codecs (ffn_codec.hip): 1 = IQ4_XS, 2 = packed 3-bit affine
+
+int codec_tile_bytes(int codec);
+
+hipError_t launch_pack_codec(int codec, const uint8_t* src, uint8_t* dst, int n_experts, int H, int F,
+                             int64_t src_expert_bytes, int64_t dst_expert_bytes, hipStream_t stream);
+
+hipError_t launch_dequant_codec(int codec, const uint8_t* mat, int rows, int cols, float* out, hipStream_t stream);
+
+hipError_t launch_ffn_codec(int codec, const uint16_t* x, int T, int H, int F, int K, int n_shared, int gated,
+                            int max_chunks, const uint8_t* arena, const uint8_t* shared, int64_t expert_bytes,
+                            const int32_t* perm, const int32_t* pos, const float* w, const Chunk* chunks,
+                            const int32_t* n_chunks, uint16_t* h_hi, uint16_t* h_lo, float* y, float* out,
+                            hipStream_t stream);
+
 // ---- one decode token in two launches (layer_decode.hip)
 
 constexpr int kMaxDecodeK = 4;          // experts per token

@@ -30,6 +30,8 @@ _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lib = None
 
 KIND_X, KIND_GATE, KIND_EXPERT, KIND_BIAS = 1, 2, 3, 4
+IQ4_NL, IQ4_XS, Q3_AFFINE = 0, 1, 2  # expert codecs
+_UNIT = {IQ4_XS: (256, 136), Q3_AFFINE: (64, 28)}  # weights and bytes per super-block / group
 WEIGHT_STD = 0.02
 BLOCK_BYTES = 18
 
@@ -57,6 +59,7 @@ def _load():
     lib.synth_iq4nl.argtypes = [u64, u64, i64, dbl, vp]
     lib.synth_encode_iq4nl.argtypes = [vp, i64, vp]
     lib.synth_threads.restype = ctypes.c_int
+    lib.synth_codec.argtypes = [ctypes.c_int, u64, u64, i64, dbl, vp]
     _lib = lib
     return lib
 
@@ -104,6 +107,18 @@ def encode_iq4nl(w: np.ndarray) -> np.ndarray:
     return out
 
 
+def codec_blocks(codec: int, seed: int, stream: int, n_weights: int, std: float = WEIGHT_STD,
+                 out: np.ndarray | None = None) -> np.ndarray:
+    """N(0, std) weights (row-major, rows a multiple of the unit) encoded in an expert codec."""
+    if codec == IQ4_NL:
+        return iq4nl_blocks(seed, stream, n_weights // 32, std, out)
+    unit, nb = _UNIT[codec]
+    out = np.empty(n_weights // unit * nb, np.uint8) if out is None else out
+    assert out.dtype == np.uint8 and out.size == n_weights // unit * nb and out.flags.c_contiguous
+    _load().synth_codec(codec, seed, stream, n_weights // unit, std, out.ctypes.data)
+    return out
+
+
 @dataclass(frozen=True)
 class Shape:
     name: str
@@ -117,6 +132,7 @@ class Shape:
     seed: int = 0
     layers: int = 1      # distinct layers generated for the workload
     zipf_s: float = 0.0  # expert-popularity skew (0 = none)
+    codec: int = IQ4_NL  # expert weight codec
 
     @property
     def blocks_per_matrix(self) -> int:
@@ -124,7 +140,10 @@ class Shape:
 
     @property
     def expert_bytes(self) -> int:
-        return 3 * self.blocks_per_matrix * BLOCK_BYTES
+        if self.codec == IQ4_NL:
+            return 3 * self.blocks_per_matrix * BLOCK_BYTES
+        unit, nb = _UNIT[self.codec]
+        return 3 * self.ffn * self.hidden // unit * nb
 
 
 WORKLOADS = {
@@ -135,6 +154,11 @@ WORKLOADS = {
     "prefill": Shape("prefill", 2048, 2048, 256, 8, 512, seed=4, zipf_s=1.0),
     # a dense FFN block of the same model (no routing: one always-on expert of width 9216)
     "dense": Shape("dense", 1, 3584, 0, 0, 9216, seed=5),
+    # the Xing4 layer with experts in the other codecs
+    "xing4_xs": Shape("xing4_xs", 1, 3584, 64, 4, 1024, seed=6, codec=IQ4_XS),
+    "xing4_q3": Shape("xing4_q3", 1, 3584, 64, 4, 1024, seed=7, codec=Q3_AFFINE),
+    "tiny_xs": Shape("tiny_xs", 4, 256, 8, 2, 256, seed=8, codec=IQ4_XS),
+    "tiny_q3": Shape("tiny_q3", 4, 256, 8, 2, 128, seed=9, codec=Q3_AFFINE),
 }
 
 
@@ -167,14 +191,14 @@ def expert_arena(shape: Shape, layer: int = 0, seed: int | None = None,
     eb = shape.expert_bytes
     out = np.empty(shape.n_experts * eb, np.uint8) if out is None else out
     for e in range(shape.n_experts):
-        iq4nl_blocks(seed, stream_id(KIND_EXPERT, layer, e), eb // BLOCK_BYTES, out=out[e * eb:(e + 1) * eb])
+        codec_blocks(shape.codec, seed, stream_id(KIND_EXPERT, layer, e), 3 * shape.ffn * shape.hidden,
+                     out=out[e * eb:(e + 1) * eb])
     return out
 
 
 def shared_arena(shape: Shape, layer: int = 0, seed: int | None = None) -> np.ndarray:
     seed = shape.seed if seed is None else seed
-    eb = shape.expert_bytes
-    return iq4nl_blocks(seed, stream_id(KIND_EXPERT, layer, shape.n_experts), eb // BLOCK_BYTES)
+    return codec_blocks(shape.codec, seed, stream_id(KIND_EXPERT, layer, shape.n_experts), 3 * shape.ffn * shape.hidden)
 
 
 def zipf_bias(shape: Shape, lam: float, layer: int = 0, seed: int | None = None) -> np.ndarray:

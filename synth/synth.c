@@ -196,3 +196,91 @@ void synth_encode_iq4nl(const float* w, int64_t n_blocks, uint8_t* out) {
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < n_blocks; b++) encode_block(w + 32 * b, out + 18 * b);
 }
+
+/* ---- other expert codecs (input generation only) ----------------------- */
+
+/* IQ4_XS super-block of 256 weights: fp16 d, the high 2 bits of eight 6-bit
+ * sub-block scales (uint16, sub-block i at bits 2i), their low 4 bits (nibble
+ * i % 2 of byte 4 + i / 2), then 8 x 16 index bytes in IQ4_NL order; weight =
+ * d * (ls - 32) * table[index].  The plain encoder: each sub-block's ideal
+ * scale s_i maps its largest-magnitude weight onto -127 (as for IQ4_NL),
+ * d = fp16(max_i |s_i| / 31), ls_i = clamp(round(s_i / d) + 32, 0, 63), and
+ * each weight takes the nearest table value for the sub-block's scale. */
+static void encode_iq4xs(const float* w, uint8_t* out) {
+  double s[8];
+  double smax = 0.0;
+  for (int ib = 0; ib < 8; ib++) {
+    int imax = 0;
+    float amax = fabsf(w[32 * ib]);
+    for (int j = 1; j < 32; j++)
+      if (fabsf(w[32 * ib + j]) > amax) { amax = fabsf(w[32 * ib + j]); imax = j; }
+    s[ib] = (double)w[32 * ib + imax] / -127.0;
+    if (fabs(s[ib]) > smax) smax = fabs(s[ib]);
+  }
+  uint16_t dh = to_f16((float)(smax / 31.0));
+  double d = f16_value(dh);
+  memset(out, 0, 136);
+  out[0] = (uint8_t)(dh & 0xff);
+  out[1] = (uint8_t)(dh >> 8);
+  unsigned sh = 0;
+  for (int ib = 0; ib < 8; ib++) {
+    int ls = d == 0.0 ? 32 : (int)lround(s[ib] / d) + 32;
+    ls = ls < 0 ? 0 : (ls > 63 ? 63 : ls);
+    sh |= (unsigned)((ls >> 4) & 3) << (2 * ib);
+    out[4 + ib / 2] |= (uint8_t)((ls & 15) << (4 * (ib % 2)));
+    double dl = d * (double)(ls - 32);
+    uint8_t idx[32];
+    for (int j = 0; j < 32; j++) idx[j] = dl == 0.0 ? 8 : (uint8_t)nearest_index((double)w[32 * ib + j], dl);
+    for (int j = 0; j < 16; j++) out[8 + 16 * ib + j] = (uint8_t)(idx[j] | (idx[j + 16] << 4));
+  }
+  out[2] = (uint8_t)(sh & 0xff);
+  out[3] = (uint8_t)(sh >> 8);
+}
+
+/* Packed 3-bit affine group of 64 weights: fp16 scale, fp16 bias, then 24
+ * bytes with code j (0..7) at bits 3j..3j+2 of the little-endian bit string;
+ * weight = scale * code + bias.  The plain min/max encoder: bias = fp16(min),
+ * scale = fp16((max - min) / 7), code = clamp(round((w - bias) / scale), 0, 7). */
+static void encode_q3(const float* w, uint8_t* out) {
+  float lo = w[0], hi = w[0];
+  for (int j = 1; j < 64; j++) {
+    if (w[j] < lo) lo = w[j];
+    if (w[j] > hi) hi = w[j];
+  }
+  uint16_t sh = to_f16((hi - lo) / 7.0f), bh = to_f16(lo);
+  double scale = f16_value(sh), bias = f16_value(bh);
+  memset(out, 0, 28);
+  out[0] = (uint8_t)(sh & 0xff);
+  out[1] = (uint8_t)(sh >> 8);
+  out[2] = (uint8_t)(bh & 0xff);
+  out[3] = (uint8_t)(bh >> 8);
+  for (int j = 0; j < 64; j++) {
+    int q = scale == 0.0 ? 0 : (int)lround(((double)w[j] - bias) / scale);
+    q = q < 0 ? 0 : (q > 7 ? 7 : q);
+    for (int k = 0; k < 3; k++)
+      if ((q >> k) & 1) out[4 + (3 * j + k) / 8] |= (uint8_t)(1u << ((3 * j + k) % 8));
+  }
+}
+
+/* n_units consecutive super-blocks (IQ4_XS, 256 weights) or groups (3-bit, 64
+ * weights) encoding N(0, std) weights, weight k of unit u being normal element
+ * (unit size) * u + k of the stream. */
+void synth_codec(int codec, uint64_t seed, uint64_t stream, int64_t n_units, double std, uint8_t* out) {
+  uint64_t key = stream_key(seed, stream);
+  const int unit = codec == 1 ? 256 : 64;
+  const int bytes = codec == 1 ? 136 : 28;
+#pragma omp parallel for schedule(static)
+  for (int64_t u = 0; u < n_units; u++) {
+    float w[256];
+    for (int k = 0; k < unit; k += 2) {
+      float z0, z1;
+      normal_pair(key, (uint64_t)(unit / 2 * u + k / 2), &z0, &z1);
+      w[k] = (float)(std * (double)z0);
+      w[k + 1] = (float)(std * (double)z1);
+    }
+    if (codec == 1)
+      encode_iq4xs(w, out + bytes * u);
+    else
+      encode_q3(w, out + bytes * u);
+  }
+}

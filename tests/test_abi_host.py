@@ -36,7 +36,7 @@ def test_exports_nothing_else():
 
 
 def test_version_and_status_strings():
-    assert qm.moe_abi_version() == 2
+    assert qm.moe_abi_version() == 3
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(qm.status_string(s), str) and qm.status_string(s)
 
@@ -74,6 +74,27 @@ def test_chained_layer_argument_errors():
     assert call(eps=-1.0) == qm.MOE_EINVAL
     assert call(eps=float("inf")) == qm.MOE_EINVAL
     assert call(wsb=ws - 1) == qm.MOE_EWORKSPACE
+
+
+def test_codec_configs_and_sizes():
+    """Expert bytes of the three codecs at the Xing4 shape (4.5, 4.25 and 3.5 bits per weight: the packed 3-bit
+    expert is 7/9 of the IQ4_NL one), the packed sizes (IQ4_XS tiles repeat a super-block's scale), and the
+    rules: the other codecs run the FP32 contract only, IQ4_XS needs ffn % 256."""
+    nl = qm.make_config(**XING4)
+    xs = qm.make_config(**XING4, codec=qm.CODEC_IQ4_XS)
+    q3 = qm.make_config(**XING4, codec=qm.CODEC_Q3_AFFINE)
+    assert qm.moe_expert_bytes(nl) == 6193152 == qm.moe_packed_expert_bytes(nl)
+    assert qm.moe_expert_bytes(xs) == 3 * 1024 * 3584 // 256 * 136 == 5849088
+    assert qm.moe_packed_expert_bytes(xs) == 3 * (1024 // 16) * (3584 // 128) * 1120
+    assert qm.moe_expert_bytes(q3) == qm.moe_packed_expert_bytes(q3) == 6193152 * 7 // 9
+    for c in (xs, q3):
+        assert qm.moe_resolved_precision(c, 1) == qm.PREC_FP32
+        assert qm.moe_resolved_precision(c, 5000) == qm.PREC_FP32
+    bad = [(dict(codec=3), qm.MOE_EINVAL), (dict(codec=1, ffn=128), qm.MOE_EUNSUPPORTED),
+           (dict(codec=2, precision=qm.PREC_BF16), qm.MOE_EUNSUPPORTED),
+           (dict(codec=1, precision=qm.PREC_W4A8), qm.MOE_EUNSUPPORTED)]
+    for b, code in bad:
+        assert qm.moe_check_config(qm.make_config(**{**XING4, **b})) == code, b
 
 
 def test_dense_and_gated_configs():

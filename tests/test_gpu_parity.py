@@ -718,6 +718,53 @@ def test_layer_w4a8_gated_and_dense():
     assert_close(out, ref, "w4a8 dense T=3")
 
 
+# ---------------------------------------------------------------- other expert codecs
+
+@pytest.mark.parametrize("name", ["tiny_xs", "tiny_q3", "xing4_xs", "xing4_q3"])
+def test_codec_dequant_bit_exact(name):
+    """The packed IQ4_XS / 3-bit tiles decoded on the GPU (moe_dequant) against the oracle's reading of the input
+    layout, every weight of the first and last expert, bit for bit (both are exact in fp32)."""
+    s, inp = workload(name)
+    cfg = cfg_of(s)
+    cfg.codec = s.codec
+    dl = qm.DeviceLayer(cfg, inp["gate_w"], None, inp["arena"], inp["shared"])
+    eb, pb = s.expert_bytes, qm.moe_packed_expert_bytes(cfg)
+    for e in (0, s.n_experts - 1):
+        src = inp["arena"][e * eb:(e + 1) * eb]
+        at = 0
+        for m, (rows, cols) in enumerate([(s.ffn, s.hidden), (s.ffn, s.hidden), (s.hidden, s.ffn)]):
+            log(f"dequant {name} expert={e} matrix={m}")
+            out = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+            qm.moe_dequant(cfg, dl.arena[e * pb:(e + 1) * pb], m, qm.PREC_FP32, out)
+            rb = oracle.codec_row_bytes(s.codec, cols)
+            want = np.stack([oracle.dequant_codec(s.codec, src[at + r * rb: at + (r + 1) * rb], cols)
+                             for r in range(rows)]).astype(np.float32)
+            at += rows * rb
+            assert np.array_equal(out.cpu().numpy().view(np.uint32), want.view(np.uint32)), (name, e, m)
+
+
+@pytest.mark.parametrize("name,T", [("tiny_xs", 1), ("tiny_xs", 4), ("tiny_xs", 37), ("tiny_q3", 1), ("tiny_q3", 4),
+                                    ("tiny_q3", 37), ("xing4_xs", 1), ("xing4_xs", 5), ("xing4_q3", 1),
+                                    ("xing4_q3", 5), ("xing4_xs", 128), ("xing4_q3", 128)])
+def test_layer_codec(name, T):
+    """The layer with IQ4_XS and packed 3-bit experts (exact weights, multi-kernel plan) against the oracle:
+    routing bit-exact, outputs within tolerance."""
+    s, inp = workload(name)
+    cfg = cfg_of(s)
+    cfg.codec = s.codec
+    dl = qm.DeviceLayer(cfg, inp["gate_w"], None, inp["arena"], inp["shared"])
+    x = synth.tokens(s, T, first=60)
+    log(f"codec layer {name} T={T}")
+    ids = torch.empty((T, s.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s.top_k), dtype=torch.float32, device="cuda")
+    out = dl.forward(to_dev_bf16(x), topk_ids=ids, topk_w=w).cpu().numpy()
+    ref, rid, rw = oracle.layer(x, inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn, s.routed_scale,
+                                codec=s.codec)
+    assert np.array_equal(ids.cpu().numpy(), rid)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), rw.view(np.uint32))
+    assert_close(out, ref, f"codec {name} T={T}")
+
+
 # ---------------------------------------------------------------- the 38-layer stack workload
 
 def test_stack_layers_chained_with_zipf_bias():
