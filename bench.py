@@ -14,8 +14,9 @@ Default run (no flags): the four measured workloads in one process, one JSON lin
   * stack (nested): 38 Xing4 layers resident in HBM, T=1 per step through all of them, each
     layer's input chained from the previous one; Zipf(1.1) popularity.
   * variants (nested): the sigmoid-gated shared expert (decode), the W4A8 contract (Q8_0
-    activations: T=1, T=128, the T=2048 prefill call) and a dense FFN block (hidden 3584,
-    FFN 9216, T=1), each timed and checked against the oracle.
+    activations: T=1, T=128, the T=2048 prefill call), a dense FFN block (hidden 3584,
+    FFN 9216, T=1) and the IQ4_XS and packed 3-bit codecs (T=1, T=128), each timed and
+    checked against the oracle.
 Every leg times its steps with HIP events on the stream it launches on (median and spread
 over the steps), runs the CPU oracle on a bounded sample of its own inputs (the cpu_baseline),
 compares the GPU rows of those tokens with the oracle's (routing bit-exact, outputs within
@@ -786,7 +787,8 @@ MFMA_I8_PEAK_TOPS = 5000.0  # MI355X dense int8 MFMA, vendor figure
 def run_variants(args, check):
     """The layer's variants on the Xing4 and prefill shapes, each timed and checked against the oracle:
     the sigmoid-gated shared expert (decode, T=1), the W4A8 contract (Q8_0 activations; T=1, T=128 and the
-    T=2048 prefill call) and a dense FFN block of the same model (hidden 3584, FFN 9216; T=1)."""
+    T=2048 prefill call), a dense FFN block of the same model (hidden 3584, FFN 9216; T=1) and the Xing4
+    layer with IQ4_XS and packed 3-bit experts (T=1, T=128)."""
     import torch
 
     import quantized_moe_decode_sigmoid_amd as qm
@@ -978,7 +980,70 @@ def run_variants(args, check):
                                   dshape.ffn, 1.0)
         dense["parity"] = check.compare("variants.dense", dout[:8].cpu().numpy(), want)
     res["dense_ffn"] = dense
+    del ddl, dplaces
+    torch.cuda.empty_cache()
     log("variants: dense done")
+
+    # 4. the other expert codecs on the Xing4 layer: T = 1 and T = 128 (exact weights, multi-kernel plan)
+    codecs = {}
+    for name in ("xing4_xs", "xing4_q3"):
+        cs = synth.WORKLOADS[name]
+        cinp = synth.layer_inputs(cs)
+        ccfg = qm.make_config(H, F, E, K, codec=cs.codec)
+        cdl = qm.DeviceLayer(ccfg, cinp["gate_w"], None, cinp["arena"], cinp["shared"])
+        cplaces = [(cdl.gate_w.clone(), cdl.arena.clone(), cdl.shared.clone()) for _ in range(n_place)]
+        cx_bits = synth.tokens(cs, n_tok, first=40000)
+        cx = torch.from_numpy(cx_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        cws = torch.empty(qm.moe_workspace_bytes(ccfg, 128), dtype=torch.uint8, device=dev)
+        ceb = qm.moe_expert_bytes(ccfg)
+
+        def csweep():
+            for i in range(n_tok):
+                g, a, sh = cplaces[i % n_place]
+                qm.moe_layer_forward(ccfg, 1, cx[i:i + 1], g, None, a, sh, out[i:i + 1], ids[i:i + 1], wts[i:i + 1],
+                                     cws)
+
+        ms, per = timed_graph(csweep, args.steps)
+        call_us = ms * 1e3 / n_tok
+        nbytes = (K + 1) * ceb + E * H * 4 + H * 6
+        entry = {"expert_bytes": ceb, "packed_expert_bytes": qm.moe_packed_expert_bytes(ccfg),
+                 "decode_t1": {"tok_s": round(n_tok / (ms * 1e-3), 1), "avg_us": round(call_us, 3),
+                               "step_spread": spread(per),
+                               "roofline": {"bound": "hbm", "achieved": round(nbytes / call_us / 1e3, 1),
+                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                            "frac": round(nbytes / call_us / 1e3 / HBM_PEAK_GBS, 4),
+                                            "bytes_per_launch": nbytes}}}
+        if oracle is not None:
+            want, rid, rw = oracle.layer(cx_bits[:n_chk], cinp["gate_w"], cinp["arena"], cinp["shared"], K, F, 2.0,
+                                         codec=cs.codec)
+            entry["decode_t1"]["parity"] = check.compare(f"variants.{name}_t1", out[:n_chk].cpu().numpy(), want,
+                                                         ids[:n_chk].cpu().numpy(), rid, wts[:n_chk, :K].cpu().numpy(),
+                                                         rw)
+        itc = [0]
+
+        def cbatch():
+            g, a, sh = cplaces[itc[0] % n_place]
+            itc[0] += 1
+            qm.moe_layer_forward(ccfg, 128, cx[:128], g, None, a, sh, out[:128], ids[:128], wts[:128, :K], cws)
+
+        with torch.cuda.stream(stream):
+            for _ in range(4):
+                cbatch()
+            torch.cuda.synchronize()
+            total, per = timed_steps(torch, stream, cbatch, max(args.steps, 8))
+        call_us = total * 1e3 / max(args.steps, 8)
+        touched = int((np.bincount(ids[:128].cpu().numpy().reshape(-1), minlength=E) > 0).sum())
+        nbytes = (touched + 1) * ceb + E * H * 4 + 128 * H * 6
+        entry["batch_t128"] = {"tok_s": round(128 / (call_us * 1e-6), 1), "avg_us": round(call_us, 3),
+                               "step_spread": spread(per),
+                               "roofline": {"bound": "hbm", "achieved": round(nbytes / call_us / 1e3, 1),
+                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                            "frac": round(nbytes / call_us / 1e3 / HBM_PEAK_GBS, 4)}}
+        codecs[name] = entry
+        del cdl, cplaces
+        torch.cuda.empty_cache()
+        log(f"variants: {name} done")
+    res["codecs"] = codecs
     return res
 
 
