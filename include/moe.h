@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Status codes. */
 typedef enum {
@@ -292,6 +292,58 @@ moe_status moe_layer_forward_chained(const moe_config* cfg, int32_t T, const voi
                                      const float* sel_bias_dev, const void* arena_dev, const void* shared_dev,
                                      float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
                                      size_t ws_bytes, hipStream_t stream);
+
+/* ---- a stack of layers ----------------------------------------------------
+ * One decode token (T = 1) through L layers chained as in
+ * moe_layer_forward_chained (design record, section 6: the decode step
+ * captured as a whole rather than call by call):
+ *   x_0 = x0;  out_l = moe_layer_forward on x_l with layer l's weights;
+ *   x_{l+1} = bf16(rmsnorm(x_l + out_l)) with eps (moe_residual_rmsnorm).
+ * L + 1 launches on `stream`: one that resets the hand-off words of every
+ * layer, then one per layer in which the router is folded into the expert
+ * kernel of the decode plan (the shared expert's workgroups form the layer's
+ * input and make one router row each while the shared expert's tiles land;
+ * the other workgroups wait for the scores through device-scope words), so a
+ * layer costs one launch instead of the decode plan's two.  Results are
+ * bit-identical to L calls of moe_layer_forward_chained (layer 0:
+ * moe_layer_forward on x0) with the same weights: the same routing, x and
+ * outputs.
+ *   layers_host  host array of L layer descriptions (device pointers inside;
+ *                gate_w fp32 [E + shared_gate][H], sel_bias fp32 [E] or
+ *                NULL, arena and shared packed by moe_pack_experts), read
+ *                during the call only
+ *   x0_dev       bf16 [H]        layer 0's input
+ *   x_all_dev    bf16 [L][H]     out: every layer's input (row 0 = x0); must
+ *                                not overlap x0_dev
+ *   out_all_dev  fp32 [L][H]     out: every layer's output
+ *   ids_all_dev  int32 [L][K]    out, or NULL
+ *   w_all_dev    fp32 [L][K + shared_gate]  out, or NULL
+ *   ws           >= moe_stack_workspace_bytes(cfg, L)
+ * Supported (else MOE_EUNSUPPORTED): the decode plan's shapes (precision AUTO
+ * or FP32, IQ4_NL, top_k <= 4, ffn <= 1024, hidden <= 4096), n_shared = 1,
+ * n_experts + shared_gate <= ffn / 16 (router row r is made by the shared
+ * expert's workgroup r), 1 <= L <= 64, and a layer's grid (the decode plan's)
+ * resident on the device at once.  Every wait is bounded; if one gives up,
+ * the outputs are wrong and the status word is 1 (moe_stack_status).
+ * eps >= 0 and finite. */
+typedef struct {
+  const float* gate_w;
+  const float* sel_bias;
+  const void* arena;
+  const void* shared;
+} moe_stack_layer;
+
+moe_status moe_stack_workspace_bytes(const moe_config* cfg, int32_t L, size_t* bytes);
+
+moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_stack_layer* layers_host, const void* x0_dev,
+                            float eps, void* x_all_dev, float* out_all_dev, int32_t* ids_all_dev, float* w_all_dev,
+                            void* ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* Copy the last moe_stack_decode's status word (0: every wait ended in time,
+ * 1: one gave up) to status_dev (int32, device), on `stream` (one small
+ * kernel, no synchronization). */
+moe_status moe_stack_status(const moe_config* cfg, int32_t L, const void* ws_dev, size_t ws_bytes,
+                            int32_t* status_dev, hipStream_t stream);
 
 /* moe_layer_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under graph capture, tight serving loops,

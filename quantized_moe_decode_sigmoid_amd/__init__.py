@@ -56,6 +56,15 @@ import torch  # noqa: E402,F401
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _cfgp = ctypes.POINTER(moe_config)
+
+
+class moe_stack_layer(ctypes.Structure):
+    """One layer of moe_stack_decode: device pointers of its weights (include/moe.h)."""
+    _fields_ = [("gate_w", ctypes.c_void_p), ("sel_bias", ctypes.c_void_p), ("arena", ctypes.c_void_p),
+                ("shared", ctypes.c_void_p)]
+
+
+_stackp = ctypes.POINTER(moe_stack_layer)
 _SIGS = {
     "moe_abi_version": ([], _i32),
     "moe_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -79,6 +88,9 @@ _SIGS = {
     "moe_quantize_q8_0": ([_vp, _i32, ctypes.c_int64, _vp, _vp, _vp], _i32),
     "moe_stream_read": ([_vp, _sz, _vp, _vp], _i32),
     "moe_residual_rmsnorm": ([_vp, _vp, _i32, _i32, ctypes.c_float, _vp, _vp], _i32),
+    "moe_stack_workspace_bytes": ([_cfgp, _i32, ctypes.POINTER(_sz)], _i32),
+    "moe_stack_decode": ([_cfgp, _i32, _stackp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "moe_stack_status": ([_cfgp, _i32, _vp, _sz, _vp, _vp], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -221,6 +233,34 @@ def moe_layer_forward_noalloc(cfg, T, x, gate_w, sel_bias, arena, shared, out, t
     _check(_lib.moe_layer_forward_noalloc(ctypes.byref(cfg), T, _p(x), _p(gate_w), _p(sel_bias), _p(arena),
                                           _p(shared), _p(out), _p(topk_ids), _p(topk_w), _stream(stream)),
            "moe_layer_forward_noalloc")
+
+
+def moe_stack_workspace_bytes(cfg, L):
+    n = _sz(0)
+    _check(_lib.moe_stack_workspace_bytes(ctypes.byref(cfg), L, ctypes.byref(n)), "moe_stack_workspace_bytes")
+    return n.value
+
+
+def stack_layers(layers):
+    """A moe_stack_layer array from (gate_w, sel_bias, arena, shared) tuples of device tensors (or None)."""
+    arr = (moe_stack_layer * len(layers))()
+    for i, (g, b, a, sh) in enumerate(layers):
+        arr[i] = moe_stack_layer(_p(g), _p(b), _p(a), _p(sh))
+    return arr
+
+
+def moe_stack_decode(cfg, L, layers, x0, x_all, out_all, ids_all=None, w_all=None, ws=None, ws_bytes=None, eps=1e-6,
+                     stream=None):
+    """One decode token through L chained layers, one launch per layer with the router folded in (layers: stack_layers(...) array)."""
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
+    _check(_lib.moe_stack_decode(ctypes.byref(cfg), L, layers, _p(x0), eps, _p(x_all), _p(out_all), _p(ids_all),
+                                 _p(w_all), _p(ws), ws_bytes, _stream(stream)), "moe_stack_decode")
+
+
+def moe_stack_status(cfg, L, ws, status, ws_bytes=None, stream=None):
+    ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None else ws_bytes
+    _check(_lib.moe_stack_status(ctypes.byref(cfg), L, _p(ws), ws_bytes, _p(status), _stream(stream)),
+           "moe_stack_status")
 
 
 class DeviceLayer:

@@ -441,6 +441,139 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
+// ---- the stack kernel
+
+namespace {
+
+// Workspace of moe_stack_decode: the hand-off words of every layer, the
+// status word, the device copy of the layers' pointers, routing outputs when
+// the caller passes none.
+struct StackPlan {
+  size_t scores, hw, status, ids, w, total;
+};
+
+StackPlan make_stack_plan(const moe_config* c, int L) {
+  StackPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  const size_t E = (size_t)c->n_experts + c->shared_gate, K = (size_t)c->top_k;
+  (void)E;
+  p.scores = take((size_t)L * qmoe::kScoreReplicas * qmoe::kScoreRepStride * 4);
+  p.hw = take((size_t)L * (K + 1) * c->ffn * 4);
+  p.status = take(16);
+  p.ids = take((size_t)L * K * 4);
+  p.w = take((size_t)L * (K + c->shared_gate) * 4);
+  p.total = off;
+  return p;
+}
+
+// The shapes the stack kernel covers (with L checked by the caller).
+moe_status check_stack(const moe_config* cfg, int32_t L) {
+  TRY(check_common(cfg, 1));
+  if (L < 1 || L > qmoe::kMaxStackLayers) return MOE_EUNSUPPORTED;
+  if (cfg->n_experts < 1 || cfg->n_shared != 1 || cfg->n_experts + cfg->shared_gate > cfg->ffn / 16)
+    return MOE_EUNSUPPORTED;
+  if (cfg->codec != MOE_CODEC_IQ4_NL || cfg->top_k > qmoe::kMaxDecodeK || cfg->ffn > qmoe::kMaxDecodeFfn ||
+      cfg->hidden > qmoe::kMaxDecodeHidden || resolve_precision(cfg, 1) != MOE_PREC_FP32)
+    return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_stack_workspace_bytes(const moe_config* cfg, int32_t L, size_t* bytes) {
+  if (!bytes) return MOE_EINVAL;
+  TRY(check_stack(cfg, L));
+  *bytes = make_stack_plan(cfg, L).total;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_stack_layer* layers_host,
+                                    const void* x0_dev, float eps, void* x_all_dev, float* out_all_dev,
+                                    int32_t* ids_all_dev, float* w_all_dev, void* ws_dev, size_t ws_bytes,
+                                    hipStream_t stream) {
+  TRY(check_stack(cfg, L));
+  if (!(eps >= 0.0f) || !isfinite(eps)) return MOE_EINVAL;
+  if (!layers_host) return MOE_EINVAL;
+  for (int l = 0; l < L; l++) {
+    TRY(need(layers_host[l].gate_w));
+    TRY(optional_ptr(layers_host[l].sel_bias));
+    TRY(need(layers_host[l].arena));
+    TRY(need(layers_host[l].shared));
+  }
+  TRY(need(x0_dev));
+  TRY(need(x_all_dev));
+  TRY(need(out_all_dev));
+  TRY(optional_ptr(ids_all_dev));
+  TRY(optional_ptr(w_all_dev));
+  TRY(need(ws_dev));
+  const size_t H = cfg->hidden;
+  if (overlaps(x_all_dev, (size_t)L * H * 2, x0_dev, H * 2) ||
+      overlaps(out_all_dev, (size_t)L * H * 4, x0_dev, H * 2) ||
+      overlaps(out_all_dev, (size_t)L * H * 4, x_all_dev, (size_t)L * H * 2))
+    return MOE_EINVAL;
+  const StackPlan sp = make_stack_plan(cfg, L);
+  if (ws_bytes < sp.total) return MOE_EWORKSPACE;
+  if (overlaps(ws_dev, sp.total, out_all_dev, (size_t)L * H * 4) || overlaps(ws_dev, sp.total, x_all_dev, (size_t)L * H * 2))
+    return MOE_EINVAL;
+  if (!qmoe::stack_grid_coresident(cfg->ffn, cfg->top_k, cfg->hidden, cfg->n_shared)) return MOE_EUNSUPPORTED;
+
+  qmoe::StackArgs s;
+  s.a.x = static_cast<const uint16_t*>(x0_dev);
+  s.a.wg = nullptr;
+  s.a.bias = nullptr;
+  s.a.arena = nullptr;
+  s.a.shared = nullptr;
+  s.a.expert_bytes = expert_bytes(cfg);
+  s.a.H = cfg->hidden;
+  s.a.F = cfg->ffn;
+  s.a.E = cfg->n_experts;
+  s.a.K = cfg->top_k;
+  s.a.n_shared = cfg->n_shared;
+  s.a.gated = cfg->shared_gate;
+  s.a.scale = cfg->routed_scale;
+  s.a.scores = nullptr;
+  s.a.ids = nullptr;
+  s.a.w = nullptr;
+  s.a.hw = nullptr;
+  s.a.out = nullptr;
+  s.a.err = at<uint32_t>(ws_dev, sp.status);
+  s.a.x_prev = nullptr;
+  s.a.out_prev = nullptr;
+  s.a.eps = eps;
+  s.L = L;
+  s.x0 = static_cast<const uint16_t*>(x0_dev);
+  s.x_all = static_cast<uint16_t*>(x_all_dev);
+  s.out_all = out_all_dev;
+  s.ids_all = ids_all_dev ? ids_all_dev : at<int32_t>(ws_dev, sp.ids);
+  s.w_all = w_all_dev ? w_all_dev : at<float>(ws_dev, sp.w);
+  s.scores_all = at<float>(ws_dev, sp.scores);
+  s.hw_all = at<uint32_t>(ws_dev, sp.hw);
+  qmoe::StackLayer layers[qmoe::kMaxStackLayers];
+  for (int l = 0; l < L; l++) {
+    layers[l].wg = layers_host[l].gate_w;
+    layers[l].bias = layers_host[l].sel_bias;
+    layers[l].arena = static_cast<const uint8_t*>(layers_host[l].arena);
+    layers[l].shared = static_cast<const uint8_t*>(layers_host[l].shared);
+  }
+  return launched(qmoe::launch_stack_decode(s, layers, stream));
+}
+
+MOE_API moe_status moe_stack_status(const moe_config* cfg, int32_t L, const void* ws_dev, size_t ws_bytes,
+                                    int32_t* status_dev, hipStream_t stream) {
+  TRY(check_stack(cfg, L));
+  TRY(need(ws_dev));
+  TRY(need(status_dev));
+  const StackPlan sp = make_stack_plan(cfg, L);
+  if (ws_bytes < sp.total) return MOE_EWORKSPACE;
+  return launched(qmoe::launch_copy_words(at<const uint32_t>(const_cast<void*>(ws_dev), sp.status),
+                                          reinterpret_cast<uint32_t*>(status_dev), 1, stream));
+}
+
 MOE_API moe_status moe_layer_forward_chained(const moe_config* cfg, int32_t T, const void* x_prev_dev,
                                              const float* out_prev_dev, float eps, void* x_dev,
                                              const float* gate_w_dev, const float* sel_bias_dev,

@@ -55,17 +55,25 @@ constexpr uint32_t kPollLimit = 1u << 20;
 
 // ---------------------------------------------------------------- device-scope access
 
+constexpr int kDeviceScope = 16;  // cache-policy bit: device coherence
+
 // 16 bytes at byte offset off of a buffer, read through to device scope.
 __device__ __forceinline__ uint4 ld_dev_x4(__amdgpu_buffer_rsrc_t r, int off) {
-  constexpr int kDeviceScope = 16;  // cache-policy bit: device coherence
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceScope));
+}
+
+__device__ __forceinline__ uint32_t ld_dev(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kDeviceScope);
 }
 
 typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
 
 __device__ __forceinline__ void st_dev_x4(__amdgpu_buffer_rsrc_t r, int off, uint4 v) {
-  constexpr int kDeviceScope = 16;
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, kDeviceScope);
+}
+
+__device__ __forceinline__ void st_dev(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kDeviceScope);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base) {
@@ -74,6 +82,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base) {
 
 __device__ __forceinline__ bool ready(uint4 v) {
   return v.x != kNotReady && v.y != kNotReady && v.z != kNotReady && v.w != kNotReady;
+}
+
+// A bounded wait gives up when it has re-read kPollLimit times, or, checked
+// every 64 re-reads, when another wait of the launch has already given up
+// (so that one failure does not make every later wait run to its bound).
+__device__ __forceinline__ bool give_up(const uint32_t* err, uint32_t it) {
+  return it > kPollLimit || ((it & 63u) == 0u && ld_dev(buffer_of(err), 0) != 0u);
 }
 
 // ---------------------------------------------------------------- LDS
@@ -94,6 +109,8 @@ struct GateUpLds {
   uint16_t x[kMaxDecodeHidden];                                                // the token's activations
   uint32_t scales[kGuMaxRowTiles][2][kMaxDecodeHidden / 128][kScaleWords];  // [row tile][gate/up][kg]
   f32x4 red[kGuMaxRowTiles][kDecWaves][4];                                  // column 0 of each wave's acc
+  float rrow[kMaxDecodeHidden];  // the stack kernel: a router row of this layer
+  float nred[4];                 // the stack kernel: the norm's wavefront sums
 };
 
 struct DownLds {
@@ -104,14 +121,17 @@ struct DownLds {
   float y[kDnSlots][32];
 };
 
+// The table comes last: every LDS DMA destination (x, scales, a router row)
+// then lies in the first 64 KB.
 struct ExpertsLds {
-  __attribute__((aligned(16))) uint32_t tbl[kPairTableWords];
   RouteLds route;
   union {
     GateUpLds g;
     DownLds d;
   } u;
+  __attribute__((aligned(256))) uint32_t tbl[kPairTableWords];
 };
+static_assert(offsetof(ExpertsLds, tbl) <= 65536, "LDS DMA destinations in the first 64 KB");
 
 // ---------------------------------------------------------------- kernel 1: scores
 
@@ -224,7 +244,47 @@ __device__ __forceinline__ RouteIn route_fetch(const DecodeArgs& a) {
   return v;
 }
 
-__device__ void route_rank(const DecodeArgs& a, RouteLds& r, RouteIn v) {
+// The stack kernel's version: the scores are written by other workgroups of
+// the same launch (device-scope stores, one per copy), so each is re-read
+// from this workgroup's copy until it no longer shows the "not ready" pattern
+// (a score is never NaN).
+__device__ __forceinline__ uint32_t poll_score(const DecodeArgs& a, int e) {
+  const __amdgpu_buffer_rsrc_t rs = buffer_of(a.scores + (blockIdx.x % kScoreReplicas) * kScoreRepStride);
+  uint32_t v = ld_dev(rs, 4 * e);
+  uint32_t it = 0;
+  while (v == kNotReady) {
+    if (give_up(a.err, ++it)) {
+      st_dev(buffer_of(a.err), 0, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_dev(rs, 4 * e);
+  }
+  return v;
+}
+
+__device__ __forceinline__ RouteIn route_poll(const DecodeArgs& a) {
+  RouteIn v = {0.0f, 0.0f};
+  const int e = threadIdx.x;
+  if (e < a.E) {
+    v.b = a.bias ? a.bias[e] : 0.0f;
+    v.s = __uint_as_float(poll_score(a, e));
+  }
+  return v;
+}
+
+// The token's routing (every thread of the workgroup calls it; thread e < E
+// brings expert e's score and bias), in two forms with the same result: the
+// K largest selection scores s + bias (ties: the lower expert index), their
+// scores, and the weights scale * s_k / (((s_0 + s_1) + ...)) in slot order.
+//
+// route_rank_lds: every expert's rank among all E counted by its own thread
+// from LDS, three barriers (≈2.3 µs at E = 64).  The two-launch decode keeps
+// this form: measured against route_rank_wave there, the later start of the
+// routed experts' tiles lets the shared expert's tiles (no routing needed)
+// land first, so the down workgroups do the shared slot while the routed h is
+// still being made (18.6 against 19.9 µs per call).
+__device__ void route_rank_lds(const DecodeArgs& a, RouteLds& r, RouteIn v) {
   const int e = threadIdx.x;
   if (e < a.E) {
     r.score[e] = v.s;
@@ -251,31 +311,83 @@ __device__ void route_rank(const DecodeArgs& a, RouteLds& r, RouteIn v) {
   __syncthreads();
 }
 
-__device__ __forceinline__ void route_local(const DecodeArgs& a, RouteLds& r) { route_rank(a, r, route_fetch(a)); }
+// route_rank_wave: wavefront 0 takes the K in K rounds of topk_take, from
+// registers when E <= 64, else through LDS, one barrier (≈0.9 µs at E = 64);
+// the stack kernel's form, where the ranking follows the wait for the scores.
+__device__ void route_rank_wave(const DecodeArgs& a, RouteLds& r, RouteIn v) {
+#pragma clang fp contract(off)
+  const int e = threadIdx.x;
+  if (a.E > 64) {  // experts past wavefront 0 meet in LDS
+    if (e < a.E) {
+      r.score[e] = v.s;
+      r.sel[e] = a.bias ? v.s + v.b : v.s;
+    }
+    __syncthreads();
+  }
+  if (e < 64) {
+    float S = 0.0f;
+    if (a.E <= 64) {
+      const bool avail = e < a.E;
+      const float s[1] = {avail ? v.s : 0.0f};
+      uint32_t key[1] = {avail ? sel_order_bits(a.bias ? v.s + v.b : v.s) : 0u};
+      for (int k = 0; k < a.K; k++) {
+        float sk;
+        const int id = topk_take<1>(key, s, e, sk);
+        if (e == 0) {
+          r.ids[k] = id;
+          r.sval[k] = sk;
+        }
+        S = S + sk;
+      }
+    } else {
+      float s[4];
+      uint32_t key[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int x = e + 64 * q;
+        const bool avail = x < a.E;
+        s[q] = avail ? r.score[x] : 0.0f;
+        key[q] = avail ? sel_order_bits(r.sel[x]) : 0u;
+      }
+      for (int k = 0; k < a.K; k++) {
+        float sk;
+        const int id = topk_take<4>(key, s, e, sk);
+        if (e == 0) {
+          r.ids[k] = id;
+          r.sval[k] = sk;
+        }
+        S = S + sk;
+      }
+    }
+    if (e == 0)
+      for (int k = 0; k < a.K; k++) r.w[k] = (r.sval[k] / S) * a.scale;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void route_local(const DecodeArgs& a, RouteLds& r) { route_rank_lds(a, r, route_fetch(a)); }
 
 // ---------------------------------------------------------------- gate / up role
 
 // waves 0-3: W_gate over quarters of the blocks of H; waves 4-7: W_up.
 // h of (row 16rt + 4G + i) is written to hw[slot][...] as bf16 hi | lo << 16.
+//
+// 1. the row tiles' scales (16-byte piece p = 64 j + lane of [matrix][kg][8]
+//    of row tile t, for j = 0..7) and, with dma_x, x (piece p of the row) by
+//    LDS DMA, one wave load each, pieces past the matrix repeating a valid
+//    one (never read); then this wave's nibble words.
 template <int NRT>
-__device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, int rt0, ExpertsLds& sh) {
+__device__ __forceinline__ void gate_up_dma(const DecodeArgs& a, const uint8_t* ex, int rt0, ExpertsLds& sh,
+                                            bool dma_x) {
   static_assert(NRT >= 1 && NRT <= kGuMaxRowTiles, "row tiles per workgroup");
   GateUpLds& g = sh.u.g;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c = lane & 15, G = lane >> 4;
   const int64_t mat_bytes = a.expert_bytes / 3;
   const int nkg = a.H >> 7;
-  const int q = wave % kGuSplit, mat = wave / kGuSplit;
-  const int kg0 = q * nkg / kGuSplit, nk = (q + 1) * nkg / kGuSplit - kg0;
   const int64_t rt_bytes = (int64_t)nkg * kTileBytes;
   const uint8_t* rowtiles = ex + rt0 * rt_bytes;  // gate of row tile rt0; up is mat_bytes further
-
-  // 1. the row tiles' scales (16-byte piece p = 64 j + lane of [matrix][kg][8]
-  //    of row tile t, for j = 0..7) and x (piece p of the row) by LDS DMA,
-  //    one wave load each, pieces past the matrix repeating a valid one (never
-  //    read); then this wave's nibble words.  Only the DMA is waited for
-  //    before the MFMAs: each tile's MFMAs start when its words have landed.
-  for (int j = wave; j < 8 * NRT + 8; j += kDecWaves) {
+  const int n_dma = 8 * NRT + (dma_x ? 8 : 0);
+  for (int j = wave; j < n_dma; j += kDecWaves) {
     if (j < 8 * NRT) {
       const int t = j >> 3, p = 64 * (j & 7) + lane, m = p >> 8, kg = min((p >> 3) & 31, nkg - 1);
       dma16_stream(rowtiles + t * rt_bytes + m * mat_bytes + (int64_t)kg * kTileBytes + kTileNibbleBytes + 16 * (p & 7),
@@ -285,8 +397,19 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
       dma16(a.x + 8 * min(p, (a.H >> 3) - 1), &g.x[512 * (j - 8 * NRT)]);
     }
   }
-  asm volatile("" ::: "memory");  // keep the nibble loads after the DMA
-  u32x4 nib[NRT][kGuMaxKg];
+  asm volatile("" ::: "memory");  // keep later loads after the DMA
+}
+
+template <int NRT>
+__device__ __forceinline__ void gate_up_words(const DecodeArgs& a, const uint8_t* ex, int rt0,
+                                              u32x4 (&nib)[NRT][kGuMaxKg]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t mat_bytes = a.expert_bytes / 3;
+  const int nkg = a.H >> 7;
+  const int q = wave % kGuSplit, mat = wave / kGuSplit;
+  const int kg0 = q * nkg / kGuSplit;
+  const int64_t rt_bytes = (int64_t)nkg * kTileBytes;
+  const uint8_t* rowtiles = ex + rt0 * rt_bytes;
 #pragma unroll
   for (int t = 0; t < NRT; t++)
 #pragma unroll
@@ -294,14 +417,34 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
       const int kg = min(kg0 + i, nkg - 1);
       nib[t][i] = ld16(rowtiles + t * rt_bytes + mat * mat_bytes + (int64_t)kg * kTileBytes + 16 * lane);
     }
-  build_pair_table(sh.tbl);
-  wait_dma_before<NRT * kGuMaxKg>();
-  __syncthreads();
+}
 
-  // 2. MFMAs: every column carries the token (a broadcast operand), column 0
-  //    is kept; acc[t][i] (row 4G+i of row tile t) += d * (levels . x).
-  //    Tiles past this wave's range are skipped (a branch uniform over the
-  //    wavefront).
+// 1. the row tiles' scales (16-byte piece p = 64 j + lane of [matrix][kg][8]
+//    of row tile t, for j = 0..7) and, with dma_x, x (piece p of the row) by
+//    LDS DMA, one wave load each, pieces past the matrix repeating a valid
+//    one (never read); then this wave's nibble words.
+template <int NRT>
+__device__ __forceinline__ void gate_up_issue(const DecodeArgs& a, const uint8_t* ex, int rt0, ExpertsLds& sh,
+                                              bool dma_x, u32x4 (&nib)[NRT][kGuMaxKg]) {
+  gate_up_dma<NRT>(a, ex, rt0, sh, dma_x);
+  gate_up_words<NRT>(a, ex, rt0, nib);
+}
+
+// 2. MFMAs: every column carries the token (a broadcast operand), column 0
+//    is kept; acc[t][i] (row 4G+i of row tile t) += d * (levels . x).
+//    Tiles past this wave's range are skipped (a branch uniform over the
+//    wavefront).  3. wave t, column 0: g and u of row tile t summed in wave
+//    order, h = silu(g) * u, stored with one device-scope store per 4 rows.
+//    Needs the table, the scales and x in LDS.
+template <int NRT>
+__device__ __forceinline__ void gate_up_compute(const DecodeArgs& a, int slot, int rt0, ExpertsLds& sh,
+                                                const u32x4 (&nib)[NRT][kGuMaxKg]) {
+  GateUpLds& g = sh.u.g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, G = lane >> 4;
+  const int nkg = a.H >> 7;
+  const int q = wave % kGuSplit, mat = wave / kGuSplit;
+  const int kg0 = q * nkg / kGuSplit, nk = (q + 1) * nkg / kGuSplit - kg0;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[NRT];
 #pragma unroll
@@ -330,8 +473,6 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
 #pragma unroll
     for (int t = 0; t < NRT; t++) g.red[t][wave][G] = acc[t];
   __syncthreads();
-  // 3. wave t, column 0: g and u of row tile t summed in wave order,
-  //    h = silu(g) * u
   if (wave < NRT && c == 0) {
     const int t = wave;
     f32x4 gs = g.red[t][0][G], us = g.red[t][kGuSplit][G];
@@ -351,6 +492,18 @@ __device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, i
     const int off = (int)(((int64_t)slot * a.F + 16 * (rt0 + t) + 4 * G) * 4);
     st_dev_x4(buffer_of(a.hw), off, make_uint4(hw4[0], hw4[1], hw4[2], hw4[3]));
   }
+}
+
+// The whole role: only the DMA is waited for before the MFMAs (each tile's
+// MFMAs start when its words have landed).
+template <int NRT>
+__device__ void gate_up_role(const DecodeArgs& a, const uint8_t* ex, int slot, int rt0, ExpertsLds& sh) {
+  u32x4 nib[NRT][kGuMaxKg];
+  gate_up_issue<NRT>(a, ex, rt0, sh, true, nib);
+  build_pair_table(sh.tbl);
+  wait_dma_before<NRT * kGuMaxKg>();
+  __syncthreads();
+  gate_up_compute<NRT>(a, slot, rt0, sh, nib);
 }
 
 // ---------------------------------------------------------------- down role
@@ -432,8 +585,8 @@ __device__ __forceinline__ void poll_h_rows(const DecodeArgs& a, DownLds& d, int
   uint4 v = ld_dev_x4(rh, off);
   uint32_t it = 0;
   while (!ready(v)) {
-    if (++it > kPollLimit) {
-      a.err[0] = 1u;
+    if (give_up(a.err, ++it)) {
+      st_dev(buffer_of(a.err), 0, 1u);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
@@ -446,6 +599,9 @@ __device__ __forceinline__ void poll_h_rows(const DecodeArgs& a, DownLds& d, int
       make_uint2((v.x >> 16) | (v.y & 0xffff0000u), (v.z >> 16) | (v.w & 0xffff0000u));
 }
 
+// PERSIST (the stack kernel): the scores come from other workgroups of the
+// same launch (waited for, bounded).
+template <bool PERSIST>
 __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   DownLds& d = sh.u.d;
   RouteLds& r = sh.route;
@@ -463,14 +619,23 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   u32x4 nib[kDnSlots];
   // 1. the router scores (and the shared expert's gate), then the shared
   //    expert's tiles (they need no routing)
-  const RouteIn rin = route_fetch(a);
-  const float gate = a.gated ? a.scores[a.E] : 1.0f;
+  RouteIn rin;
+  float gate = 1.0f;
+  if constexpr (!PERSIST) {
+    rin = route_fetch(a);
+    gate = a.gated ? a.scores[a.E] : 1.0f;
+  }
   const uint8_t* shx = a.n_shared ? a.shared : a.arena;
   nib[kMaxDecodeK] = ld16(down_tiles(shx, rt) + (int64_t)kgc * kTileBytes + 16 * lane);
   if (wave < 2) dma_slot_scales(d, down_tiles(shx, 2 * blk), nkg, kMaxDecodeK, wave);
   build_pair_table(sh.tbl);
+  if constexpr (PERSIST) {
+    rin = route_poll(a);
+    if (a.gated) gate = __uint_as_float(poll_score(a, a.E));
+  }
   // 2. routing, then the routed experts' tiles
-  route_rank(a, r, rin);
+  if constexpr (PERSIST) route_rank_wave(a, r, rin);
+  else route_rank_lds(a, r, rin);
   load_routed_slots<0>(a, r, nib, rt, kgc, nkg);
   if (wave >= 2 && wave < 2 + 2 * a.K) {
     const int slot = (wave - 2) >> 1;
@@ -536,8 +701,181 @@ __global__ __launch_bounds__(kDecThreads, 8) void k_decode_experts(DecodeArgs a)
   } else if ((blk -= a.n_routed_wg) < a.n_shared_wg) {
     gate_up_role<1>(a, a.shared, a.K, blk, sh);
   } else {
-    down_role(a, blk - a.n_shared_wg, sh);
+    down_role<false>(a, blk - a.n_shared_wg, sh);
   }
+}
+
+// ---------------------------------------------------------------- the stack step
+
+// One decode token through L layers in L + 1 launches: k_stack_reset, then
+// one k_stack_layer per layer, each the grid of k_decode_experts with the
+// router folded in (no separate router launch per layer):
+//   [routed]  the layer's input formed from the previous layer's input and
+//             output, then the scores (waited for), ranking (route_rank_wave),
+//             the gate/up tiles of its slot and row tile, gate/up;
+//   [shared]  router row blk (row E: the shared expert's gate) and the
+//             previous layer's input and output requested first, the layer's
+//             input, the logit and score (device-scope stores, one per score
+//             copy), then the shared expert's gate/up;
+//   [down]    as in k_decode_experts, with the scores waited for.
+// Every hand-off word of every layer (scores, h) is "not ready" when the step
+// starts (k_stack_reset) and written once.  The down workgroups wait for the
+// scores and for h, the routed ones for the scores: the launcher checks that
+// the grid is resident at once (as for k_decode_experts).  Every wait is
+// bounded; after one gives up the others give up within 64 re-reads.
+
+// The layer's input from the previous layer's input xs (bf16, in LDS,
+// replaced in place) and output (written by the previous launch, so plain
+// loads see it): the operations and order of k_residual_rmsnorm -- threads
+// v < 256 play its threads (elements v, v + 256, ...), each wavefront's sums
+// meet in an xor butterfly, the 4 wavefront sums are added in order.  The
+// loads are issued first (stack_input_load) so that they overlap the
+// workgroup's LDS DMA.
+constexpr int kInPer = kMaxDecodeHidden / 256;
+static_assert(kMaxDecodeFfn / 16 <= kScoreRepStride, "a layer's router rows fit in one score copy");
+
+__device__ __forceinline__ void stack_input_load(const DecodeArgs& a, const float* out_prev, float (&o)[kInPer]) {
+  const int v = threadIdx.x, n = a.H >> 8;
+#pragma unroll
+  for (int i = 0; i < kInPer; i++) o[i] = (v < 256 && i < n) ? out_prev[v + 256 * i] : 0.0f;
+}
+
+__device__ void stack_input(const DecodeArgs& a, const float (&o)[kInPer], uint16_t* xs, float* nred) {
+  const int v = threadIdx.x, n = a.H >> 8;
+  if (v < 256) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kInPer; i++) {
+      if (i < n) {
+        const float h = bf16_bits_to_f32(xs[v + 256 * i]) + o[i];
+        ss = __builtin_fmaf(h, h, ss);
+      }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) ss += __shfl_xor(ss, s, 64);
+    if ((v & 63) == 0) nred[v >> 6] = ss;
+  }
+  __syncthreads();
+  if (v < 256) {
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) tot += nred[w];
+    const float r = 1.0f / __builtin_sqrtf(tot / (float)a.H + a.eps);
+#pragma unroll
+    for (int i = 0; i < kInPer; i++) {
+      if (i < n) {
+        const float h = bf16_bits_to_f32(xs[v + 256 * i]) + o[i];
+        xs[v + 256 * i] = (uint16_t)f32_to_bf16_rne(h * r);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// router_logit_vals' fixed order with the activations and the router row
+// read from LDS one 256-element step at a time.
+__device__ __forceinline__ float router_logit_lds(const uint16_t* xs, const float* wrow, int H, int lane) {
+#pragma clang fp contract(off)
+  const int M = H >> 8;
+  float p = 0.0f;
+  for (int m = 0; m < M; m++) {
+    const uint2 xv = *reinterpret_cast<const uint2*>(xs + 256 * m + 4 * lane);
+    const float4 w = *reinterpret_cast<const float4*>(wrow + 256 * m + 4 * lane);
+    p = __builtin_fmaf(bf16_bits_to_f32(xv.x & 0xffffu), w.x, p);
+    p = __builtin_fmaf(bf16_bits_to_f32(xv.x >> 16), w.y, p);
+    p = __builtin_fmaf(bf16_bits_to_f32(xv.y & 0xffffu), w.z, p);
+    p = __builtin_fmaf(bf16_bits_to_f32(xv.y >> 16), w.w, p);
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_xor(p, s, 64);
+  return p;
+}
+
+// The previous layer's input (layer 0: the step's input) into LDS by DMA,
+// 16 bytes per lane, pieces past the row repeating a valid one.
+__device__ __forceinline__ void dma_x(const uint16_t* x, int H, uint16_t* xs) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave < 8) {
+    const int p = 64 * wave + lane;
+    dma16(x + 8 * min(p, (H >> 3) - 1), xs + 512 * wave);
+  }
+}
+
+__device__ void stack_shared_layer(const DecodeArgs& a, int l, int blk, ExpertsLds& sh, const float* out_prev,
+                                   uint16_t* x_out) {
+  GateUpLds& g = sh.u.g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const bool has_row = blk < a.E + a.gated;
+  // 1. the score first (the routed workgroups wait for it): the router row
+  //    and the previous layer's input by LDS DMA, the layer's input, the
+  //    logit and score
+  if (has_row && wave < (a.H >> 8))
+    dma16_stream(a.wg + (size_t)blk * a.H + 256 * wave + 4 * lane, &g.rrow[256 * wave]);
+  dma_x(a.x, a.H, g.x);
+  float o[kInPer];
+  if (l > 0) stack_input_load(a, out_prev, o);
+  build_pair_table(sh.tbl);
+  wait_loads();
+  __syncthreads();
+  if (l > 0) stack_input(a, o, g.x, g.nred);
+  if (has_row && wave == 0) {
+    const float p = router_logit_lds(g.x, g.rrow, a.H, lane);
+    if (lane < kScoreReplicas)
+      st_dev(buffer_of(a.scores), 4 * (kScoreRepStride * lane + blk), __float_as_uint(sigmoid_fixed(p)));
+  }
+  if (blk == 0 && (int)threadIdx.x < (a.H >> 3))
+    *reinterpret_cast<uint4*>(x_out + 8 * threadIdx.x) = *reinterpret_cast<const uint4*>(&g.x[8 * threadIdx.x]);
+  // 2. gate/up of the shared expert
+  gate_up_dma<1>(a, a.shared, blk, sh, false);
+  u32x4 nib[1][kGuMaxKg];
+  gate_up_words<1>(a, a.shared, blk, nib);
+  wait_dma_before<kGuMaxKg>();
+  __syncthreads();
+  gate_up_compute<1>(a, a.K, blk, sh, nib);
+}
+
+__device__ void stack_routed_layer(const DecodeArgs& a, int l, int blk, ExpertsLds& sh, const float* out_prev) {
+  GateUpLds& g = sh.u.g;
+  const int n_rt_f = a.F >> 4;
+  const int slot = blk / n_rt_f, rt = blk % n_rt_f;
+  // the layer's input first: it is ready before the scores can be
+  dma_x(a.x, a.H, g.x);
+  float o[kInPer];
+  if (l > 0) stack_input_load(a, out_prev, o);
+  build_pair_table(sh.tbl);
+  wait_loads();
+  __syncthreads();
+  if (l > 0) stack_input(a, o, g.x, g.nred);
+  route_rank_wave(a, sh.route, route_poll(a));
+  const uint8_t* ex = a.arena + (int64_t)sh.route.ids[slot] * a.expert_bytes;
+  gate_up_dma<1>(a, ex, rt, sh, false);
+  u32x4 nib[1][kGuMaxKg];
+  gate_up_words<1>(a, ex, rt, nib);
+  wait_dma_before<kGuMaxKg>();
+  __syncthreads();
+  gate_up_compute<1>(a, slot, rt, sh, nib);
+}
+
+// One layer of the step.  x: the previous layer's input (layer 0: the
+// step's input); out_prev: the previous layer's output (layer 0: null).
+__global__ __launch_bounds__(kDecThreads, 8) void k_stack_layer(DecodeArgs a, int l, const float* out_prev,
+                                                                  uint16_t* x_out) {
+  __shared__ ExpertsLds sh;
+  const int blk = blockIdx.x;
+  if (blk < a.n_routed_wg) stack_routed_layer(a, l, blk, sh, out_prev);
+  else if (blk < a.n_routed_wg + a.n_shared_wg) stack_shared_layer(a, l, blk - a.n_routed_wg, sh, out_prev, x_out);
+  else down_role<true>(a, blk - a.n_routed_wg - a.n_shared_wg, sh);
+}
+
+// Every hand-off word of the step (scores and h of every layer) to "not
+// ready", the give-up word to 0.
+__global__ void k_stack_reset(float* scores_all, int64_t n_scores, uint32_t* hw_all, int64_t n_hw, uint32_t* err) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_scores + n_hw; i += stride) {
+    if (i < n_scores) reinterpret_cast<uint32_t*>(scores_all)[i] = kNotReady;
+    else hw_all[i - n_scores] = kNotReady;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) err[0] = 0u;
 }
 
 namespace {
@@ -584,6 +922,62 @@ hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream) {
   hipLaunchKernelGGL(k_decode_experts, dim3(a.n_shared_wg + a.n_routed_wg + a.n_down_wg), dim3(kDecThreads), 0,
                      stream, a);
   return hipGetLastError();
+}
+
+static std::atomic<int> g_stack_capacity[64];
+
+bool stack_grid_coresident(int F, int K, int H, int n_shared) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    clear_last_error();
+    return false;
+  }
+  int cap = g_stack_capacity[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_stack_layer),
+                                                     kDecThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+      clear_last_error();
+      return false;
+    }
+    cap = per_cu * cus > 0 ? per_cu * cus : -1;
+    g_stack_capacity[dev].store(cap, std::memory_order_relaxed);
+  }
+  return cap > 0 && decode_grid_size(F, K, H, n_shared) <= cap;
+}
+
+hipError_t launch_stack_decode(StackArgs s, const StackLayer* layers, hipStream_t stream) {
+  DecodeArgs b = s.a;
+  b.n_router = b.E + b.gated;
+  b.n_shared_wg = b.F / 16;
+  b.n_routed_wg = b.K * (b.F / 16);
+  b.n_down_wg = b.H / 32;
+  const int64_t n_scores = (int64_t)s.L * kScoreReplicas * kScoreRepStride, n_hw = (int64_t)s.L * (b.K + 1) * b.F;
+  clear_last_error();
+  hipLaunchKernelGGL(k_stack_reset, dim3(256), dim3(256), 0, stream, s.scores_all, n_scores, s.hw_all, n_hw, b.err);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t H = b.H;
+  for (int l = 0; l < s.L; l++) {
+    DecodeArgs a = b;
+    a.x = l == 0 ? s.x0 : s.x_all + (l - 1) * H;
+    a.wg = layers[l].wg;
+    a.bias = layers[l].bias;
+    a.arena = layers[l].arena;
+    a.shared = layers[l].shared;
+    a.scores = s.scores_all + (size_t)l * kScoreReplicas * kScoreRepStride;
+    a.hw = s.hw_all + (size_t)l * (b.K + 1) * b.F;
+    a.out = s.out_all + l * H;
+    a.ids = s.ids_all + (size_t)l * b.K;
+    a.w = s.w_all + (size_t)l * (b.K + b.gated);
+    clear_last_error();
+    hipLaunchKernelGGL(k_stack_layer, dim3(b.n_shared_wg + b.n_routed_wg + b.n_down_wg), dim3(kDecThreads), 0, stream,
+                       a, l, l > 0 ? s.out_all + (l - 1) * H : nullptr, s.x_all + l * H);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 __global__ void k_fill_u32(uint32_t* p, int64_t n) {

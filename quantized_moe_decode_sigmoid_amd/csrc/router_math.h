@@ -124,15 +124,45 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t k) {
   return max(max(r0, r1), max(r2, r3));
 }
 
+// One round of a wavefront's selection over NQ keys per lane (lane l holds
+// experts l, l + 64, ...; key 0: no candidate): the largest key left, as a
+// wave-wide maximum, and among equal keys the smallest expert index (first
+// set bit of the first non-empty ballot, in expert order).  The owner lane
+// retires it; every lane gets the expert index (returned) and its unbiased
+// score s_win.
+template <int NQ>
+__device__ __forceinline__ int topk_take(uint32_t (&key)[NQ], const float (&s)[NQ], int lane, float& s_win) {
+  uint32_t mk = key[0];
+#pragma unroll
+  for (int q = 1; q < NQ; q++) mk = max(mk, key[q]);
+  const uint32_t m = wave_max_u32(mk);
+  int e = 64 * NQ;
+#pragma unroll
+  for (int q = NQ - 1; q >= 0; q--) {
+    const uint64_t b = __builtin_amdgcn_ballot_w64(key[q] == m);
+    if (b) e = 64 * q + (int)__builtin_ctzll(b);
+  }
+  const int qe = e >> 6, le = e & 63;
+  float sw = 0.0f;
+#pragma unroll
+  for (int q = 0; q < NQ; q++) {
+    if (q == qe) {
+      if (lane == le) key[q] = 0u;
+      sw = s[q];
+    }
+  }
+  s_win = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw), le));
+  return e;
+}
+
 // One wavefront selects the K experts of one token from its E sigmoid scores
-// (E <= 256; lane l holds experts l, l + 64, l + 128, l + 192): K rounds, each
-// taking the largest selection score (s + bias) left, as a wave-wide maximum
-// of its order-preserving bits, and among equal scores the smallest expert
-// index (first set bit of the first non-empty ballot, in expert order), then
-// retiring it.  Lane 0 writes the slots to ids[0..K) and the weights
-// scale * s_k / (((s_0 + s_1) + s_2) + ...) to w (either may point to global
-// or LDS memory); with a sigmoid-gated shared expert (gated != 0) also
-// w[K] = scores[E], the gate's own sigmoid score (not normalised or scaled).
+// (E <= 256; lane l holds experts l, l + 64, l + 128, l + 192): K rounds of
+// topk_take on the selection scores (s + bias), each taking the largest left
+// (ties: the smallest expert index).  Lane 0 writes the slots to ids[0..K)
+// and the weights scale * s_k / (((s_0 + s_1) + s_2) + ...) to w (either may
+// point to global or LDS memory); with a sigmoid-gated shared expert
+// (gated != 0) also w[K] = scores[E], the gate's own sigmoid score (not
+// normalised or scaled).
 __device__ __forceinline__ void topk_wave(const float* scores, const float* bias, int E, int K, float scale,
                                           int lane, int32_t* ids, float* wout, int gated = 0) {
 #pragma clang fp contract(off)
@@ -148,27 +178,7 @@ __device__ __forceinline__ void topk_wave(const float* scores, const float* bias
   }
   int chosen[8];
   float chosen_s[8];
-  for (int k = 0; k < K; k++) {
-    const uint32_t m = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
-    int e = 256;
-#pragma unroll
-    for (int q = 3; q >= 0; q--) {
-      const uint64_t b = __builtin_amdgcn_ballot_w64(key[q] == m);
-      if (b) e = 64 * q + (int)__builtin_ctzll(b);
-    }
-    // the owner lane retires the winner; its unbiased score to every lane
-    const int qe = e >> 6, le = e & 63;
-    float sw = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-      if (q == qe) {
-        if (lane == le) key[q] = 0u;
-        sw = s[q];
-      }
-    }
-    chosen[k] = e;
-    chosen_s[k] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sw), le));
-  }
+  for (int k = 0; k < K; k++) chosen[k] = topk_take<4>(key, s, lane, chosen_s[k]);
   if (lane == 0) {
     float S = 0.0f;
     for (int k = 0; k < K; k++) S = S + chosen_s[k];

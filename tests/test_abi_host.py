@@ -36,7 +36,7 @@ def test_exports_nothing_else():
 
 
 def test_version_and_status_strings():
-    assert qm.moe_abi_version() == 3
+    assert qm.moe_abi_version() == 4
     for s in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(qm.status_string(s), str) and qm.status_string(s)
 
@@ -74,6 +74,49 @@ def test_chained_layer_argument_errors():
     assert call(eps=-1.0) == qm.MOE_EINVAL
     assert call(eps=float("inf")) == qm.MOE_EINVAL
     assert call(wsb=ws - 1) == qm.MOE_EWORKSPACE
+
+
+def test_stack_decode_argument_errors():
+    """moe_stack_decode: the shapes it covers, its workspace size, and argument errors (all refused before
+    any launch)."""
+    cfg = qm.make_config(**XING4)
+    n1, n38 = qm.moe_stack_workspace_bytes(cfg, 1), qm.moe_stack_workspace_bytes(cfg, 38)
+    assert 0 < n1 < n38
+    # scores + h words per layer are the bulk: 38 layers x (64 + 5 x 1024) words
+    assert n38 >= 38 * (64 + 5 * 1024) * 4
+    for bad, code in [(dict(), None), (dict(n_shared=0), qm.MOE_EUNSUPPORTED), (dict(ffn=512), qm.MOE_EUNSUPPORTED),
+                      (dict(top_k=5), qm.MOE_EUNSUPPORTED), (dict(hidden=4352), qm.MOE_EUNSUPPORTED),
+                      (dict(shared_gate=1), qm.MOE_EUNSUPPORTED)]:
+        c = qm.make_config(**{**XING4, **bad})
+        if code is None:
+            continue
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_stack_workspace_bytes(c, 4)
+        assert ei.value.status == code, bad
+    for L in (0, 65):
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_stack_workspace_bytes(cfg, L)
+        assert ei.value.status == qm.MOE_EUNSUPPORTED
+    H = XING4["hidden"]
+    L = 3
+    good = qm.stack_layers([(A, None, A, A)] * L)
+
+    def call(layers=good, x0=A, x_all=A + 0x100000, out_all=A + 0x200000, eps=1e-6, wsb=None):
+        wsb = qm.moe_stack_workspace_bytes(cfg, L) if wsb is None else wsb
+        with pytest.raises(qm.MoeError) as ei:
+            qm.moe_stack_decode(cfg, L, layers, x0, x_all, out_all, ws=A + 0x400000, ws_bytes=wsb, eps=eps,
+                                stream=0)
+        return ei.value.status
+
+    assert call(layers=None) == qm.MOE_EINVAL
+    assert call(layers=qm.stack_layers([(A, None, A, A), (A, None, None, A), (A, None, A, A)])) == qm.MOE_EINVAL
+    assert call(layers=qm.stack_layers([(A, A + 4, A, A)] * L)) == qm.MOE_EALIGN
+    assert call(x0=None) == qm.MOE_EINVAL
+    assert call(x_all=A + 0x100008) == qm.MOE_EALIGN
+    assert call(x_all=A) == qm.MOE_EINVAL                           # overlaps x0
+    assert call(out_all=A + 0x100000 + 2 * H) == qm.MOE_EINVAL     # overlaps x_all
+    assert call(eps=float("nan")) == qm.MOE_EINVAL
+    assert call(wsb=qm.moe_stack_workspace_bytes(cfg, L) - 1) == qm.MOE_EWORKSPACE
 
 
 def test_codec_configs_and_sizes():
