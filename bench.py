@@ -12,7 +12,9 @@ Default run (no flags): the four measured workloads in one process, one JSON lin
     the fraction of bf16 MFMA peak, and the HBM fraction.
   * batch (nested): one T=128 call of the Xing4 layer per step.
   * stack (nested): 38 Xing4 layers resident in HBM, T=1 per step through all of them, each
-    layer's input chained from the previous one; Zipf(1.1) popularity.
+    layer's input chained from the previous one, by moe_stack_decode (one launch per layer,
+    the router folded in); the same step as chained per-layer calls timed beside it;
+    Zipf(1.1) popularity.
   * variants (nested): the sigmoid-gated shared expert (decode), the W4A8 contract (Q8_0
     activations: T=1, T=128, the T=2048 prefill call), a dense FFN block (hidden 3584,
     FFN 9216, T=1) and the IQ4_XS and packed 3-bit codecs (T=1, T=128), each timed and
@@ -20,7 +22,7 @@ Default run (no flags): the four measured workloads in one process, one JSON lin
 Every leg times its steps with HIP events on the stream it launches on (median and spread
 over the steps), runs the CPU oracle on a bounded sample of its own inputs (the cpu_baseline),
 compares the GPU rows of those tokens with the oracle's (routing bit-exact, outputs within
-max-abs 2e-2 / rel-L2 1e-3) and, on the decode path, reads the status word.  Any miss makes
+max-abs 2e-2 / rel-L2 1e-3) and, on the decode and stack paths, reads the status word.  Any miss makes
 the exit status non-zero after the line is printed.
 
 `--workload X` runs one leg alone and prints its line at top level (profiling runs).
@@ -600,8 +602,10 @@ def run_batch(args, check):
 
 def run_stack(args, check):
     """38 MoE layers of the Xing4 shape resident in HBM, one token per step (T=1) through all of them,
-    each layer's input chained from the previous layer's input and output by bf16(rmsnorm(x + out)),
-    formed inside the next layer's router kernel (moe_layer_forward_chained); Zipf(1.1) expert popularity."""
+    each layer's input chained from the previous layer's input and output by bf16(rmsnorm(x + out)):
+    moe_stack_decode (one reset launch, then one launch per layer with the router folded in), timed
+    through a HIP graph; the same step as chained moe_layer_forward_chained calls timed beside it;
+    Zipf(1.1) expert popularity."""
     import torch
 
     import quantized_moe_decode_sigmoid_amd as qm
@@ -640,35 +644,39 @@ def run_stack(args, check):
     S = args.stack_tokens
     x_bits = synth.tokens(shape, S, first=7000)
     x0 = torch.from_numpy(x_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
-    ws = torch.empty(qm.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device=dev)
-    qm.moe_workspace_init(cfg, 1, ws)
-    outs = torch.empty((nl, H), dtype=torch.float32, device=dev)
-    xl = torch.empty((nl, H), dtype=torch.bfloat16, device=dev)  # each layer's input
+    arr = qm.stack_layers([(dl.gate_w, dl.bias, dl.arena, dl.shared) for dl in layers])
+    sws = torch.empty(qm.moe_stack_workspace_bytes(cfg, nl), dtype=torch.uint8, device=dev)
+    xall = torch.empty((S, nl, H), dtype=torch.bfloat16, device=dev)  # every token's input to every layer
+    oall = torch.empty((S, nl, H), dtype=torch.float32, device=dev)
     ids = torch.empty((S, nl, K), dtype=torch.int32, device=dev)
     wts = torch.empty((S, nl, K), dtype=torch.float32, device=dev)
 
-    def layer_call(i, l):
-        """Layer l of token i: layer 0 on the token itself, every later layer chained (its input
-        bf16(rmsnorm(previous input + previous output)) formed inside the call)."""
-        dl = layers[l]
-        if l == 0:
-            qm.moe_layer_forward(cfg, 1, xl[0:1], dl.gate_w, dl.bias, dl.arena, dl.shared, outs[0:1], ids[i, 0],
-                                 wts[i, 0], ws)
-        else:
-            qm.moe_layer_forward_chained(cfg, 1, xl[l - 1:l], outs[l - 1:l], xl[l:l + 1], dl.gate_w, dl.bias, dl.arena,
-                                         dl.shared, outs[l:l + 1], ids[i, l], wts[i, l], ws)
-
-    def token(i, x_in=None, o_out=None):
-        xl[0].copy_(x0[i])
-        for l in range(nl):
-            layer_call(i, l)
-        if x_in is not None:
-            x_in.copy_(xl)
-            o_out.copy_(outs)
+    def stack_step(i):
+        qm.moe_stack_decode(cfg, nl, arr, x0[i:i + 1], xall[i], oall[i], ids[i], wts[i], sws)
 
     def steps():
         for i in range(S):
-            token(i)
+            stack_step(i)
+
+    # the same step as chained layer calls (layer 0 on the token, layers 1.. by moe_layer_forward_chained,
+    # the norm inside the router kernel): the path moe_stack_decode replaces, timed for comparison
+    ws = torch.empty(qm.moe_workspace_bytes(cfg, 1), dtype=torch.uint8, device=dev)
+    qm.moe_workspace_init(cfg, 1, ws)
+    outs = torch.empty((nl, H), dtype=torch.float32, device=dev)
+    xl = torch.empty((nl, H), dtype=torch.bfloat16, device=dev)
+    cids = torch.empty((nl, K), dtype=torch.int32, device=dev)
+    cw = torch.empty((nl, K), dtype=torch.float32, device=dev)
+
+    def chained_steps():
+        for i in range(S):
+            xl[0].copy_(x0[i])
+            for l, dl in enumerate(layers):
+                if l == 0:
+                    qm.moe_layer_forward(cfg, 1, xl[0:1], dl.gate_w, dl.bias, dl.arena, dl.shared, outs[0:1],
+                                         cids[0], cw[0], ws)
+                else:
+                    qm.moe_layer_forward_chained(cfg, 1, xl[l - 1:l], outs[l - 1:l], xl[l:l + 1], dl.gate_w,
+                                                 dl.bias, dl.arena, dl.shared, outs[l:l + 1], cids[l], cw[l], ws)
 
     stream = torch.cuda.Stream()
     with torch.cuda.stream(stream):
@@ -681,27 +689,34 @@ def run_stack(args, check):
             graph.replay()
         torch.cuda.synchronize()
         total_ms, per_replay = timed_steps(torch, stream, graph.replay, args.steps)
-        # the layer calls alone: events around each call of one eager pass over the S tokens, the queue kept
-        # busy by a spin kernel so that host launch gaps do not enter
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(S * nl)]
+        st = torch.full((4,), -1, dtype=torch.int32, device=dev)
+        qm.moe_stack_status(cfg, nl, sws, st)
+        word = int(st[0].item())
+        # the calls alone: events around each call of one eager pass over the S tokens, the queue kept busy
+        # by a spin kernel so that host launch gaps do not enter
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(S)]
         torch.cuda._sleep(200_000_000)
         for i in range(S):
-            xl[0].copy_(x0[i])
-            for l in range(nl):
-                starts[i * nl + l].record(stream)
-                layer_call(i, l)
-                ends[i * nl + l].record(stream)
+            starts[i].record(stream)
+            stack_step(i)
+            ends[i].record(stream)
         torch.cuda.synchronize()
-        # every layer's input and output of the first tokens, for the oracle (eager, same kernels)
-        n_chk = min(S, 8)
-        x_in = torch.empty((n_chk, nl, H), dtype=torch.bfloat16, device=dev)
-        o_out = torch.empty((n_chk, nl, H), dtype=torch.float32, device=dev)
-        for i in range(n_chk):
-            token(i, x_in[i], o_out[i])
+        # the chained calls, captured and timed the same way
+        chained_steps()
         torch.cuda.synchronize()
-        word = status_word(torch, qm, cfg, 1, ws)
+        cgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cgraph, stream=stream):
+            chained_steps()
+        for _ in range(args.warmup):
+            cgraph.replay()
+        torch.cuda.synchronize()
+        chained_ms, _ = timed_steps(torch, stream, cgraph.replay, args.steps)
+        del cgraph
+    n_chk = min(S, 8)
+    x_in, o_out = xall[:n_chk], oall[:n_chk]
     ms_per_token = total_ms / (args.steps * S)
+    chained_ms_per_token = chained_ms / (args.steps * S)
     moe_ms_per_token = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / S
     eb = qm.moe_expert_bytes(cfg)
     expert_bytes = nl * (K + shape.n_shared) * eb
@@ -760,18 +775,23 @@ def run_stack(args, check):
                                "shared, ffn 1024, IQ4_NL, sigmoid router, scale 2.0; layer input = bf16(rmsnorm("
                                "previous input + previous output)) by one fused kernel; Zipf(1.1) expert popularity",
                    "layers": nl, "distinct_tokens": S, "zipf_lambda": lam, "graph": True,
-                   "chaining": "layers 1..37 by moe_layer_forward_chained (the norm inside the router kernel)",
+                   "call": "moe_stack_decode: one reset launch, then one launch per layer (router, norm of the "
+                           "previous layer's input and output, experts)",
                    "expert_sets": f"router weights and biases drawn per layer; expert weights drawn for {nd} "
                                   f"layers, each layer's placed at its own address"},
         "step_spread": spread(np.asarray(per_replay) / S),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("stack_traffic.json"),
-                     "kernel": "whole step: per layer k_decode_scores (with the chaining norm) + k_decode_experts",
+                     "kernel": "whole step: k_stack_reset + one k_stack_layer per layer",
                      "bytes_per_token": expert_bytes + router_bytes},
         "cpu_baseline": cpu,
         "parity": parity,
         "expert_bytes_per_token": expert_bytes,
         "moe_calls_ms_per_token": round(moe_ms_per_token, 4),
+        "chained_calls": {"ms_per_token": round(chained_ms_per_token, 4),
+                          "value": round(1e3 / chained_ms_per_token, 2), "unit": "tok/s",
+                          "path": "per layer moe_layer_forward_chained (k_decode_scores with the norm + "
+                                  "k_decode_experts), graph of the same tokens"},
         "moe_calls_gbs": round((expert_bytes + router_bytes) / (moe_ms_per_token * 1e-3) / 1e9, 1),
         "popularity": {"rank_frequency_slope": slope, "routes_by_rank": [int(v) for v in by_rank[:16]],
                        "routes": int(by_rank.sum())},
