@@ -867,13 +867,19 @@ __global__ __launch_bounds__(kDecThreads, 8) void k_stack_layer(DecodeArgs a, in
   else down_role<true>(a, blk - a.n_routed_wg - a.n_shared_wg, sh);
 }
 
-// Every hand-off word of the step (scores and h of every layer) to "not
-// ready", the give-up word to 0.
-__global__ void k_stack_reset(float* scores_all, int64_t n_scores, uint32_t* hw_all, int64_t n_hw, uint32_t* err) {
+// Every hand-off word of the step to "not ready" -- the n_router scores of
+// each of the kScoreReplicas copies of each of the L layers, and the h
+// words of every layer -- and the give-up word to 0.
+__global__ void k_stack_reset(float* scores_all, int L, int n_router, uint32_t* hw_all, int64_t n_hw, uint32_t* err) {
+  const int64_t n_scores = (int64_t)L * kScoreReplicas * n_router;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_scores + n_hw; i += stride) {
-    if (i < n_scores) reinterpret_cast<uint32_t*>(scores_all)[i] = kNotReady;
-    else hw_all[i - n_scores] = kNotReady;
+    if (i < n_scores) {
+      const int64_t copy = i / n_router, e = i % n_router;  // copy = layer * kScoreReplicas + c
+      reinterpret_cast<uint32_t*>(scores_all)[copy * kScoreRepStride + e] = kNotReady;
+    } else {
+      hw_all[i - n_scores] = kNotReady;
+    }
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) err[0] = 0u;
 }
@@ -953,9 +959,10 @@ hipError_t launch_stack_decode(StackArgs s, const StackLayer* layers, hipStream_
   b.n_shared_wg = b.F / 16;
   b.n_routed_wg = b.K * (b.F / 16);
   b.n_down_wg = b.H / 32;
-  const int64_t n_scores = (int64_t)s.L * kScoreReplicas * kScoreRepStride, n_hw = (int64_t)s.L * (b.K + 1) * b.F;
+  const int64_t n_hw = (int64_t)s.L * (b.K + 1) * b.F;
   clear_last_error();
-  hipLaunchKernelGGL(k_stack_reset, dim3(256), dim3(256), 0, stream, s.scores_all, n_scores, s.hw_all, n_hw, b.err);
+  hipLaunchKernelGGL(k_stack_reset, dim3(256), dim3(256), 0, stream, s.scores_all, s.L, b.n_router, s.hw_all, n_hw,
+                     b.err);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const size_t H = b.H;
