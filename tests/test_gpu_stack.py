@@ -59,8 +59,8 @@ def stack_layers(nl, with_bias=True):
     return _STACK[key]
 
 
-def run_stack(cfg, layers, x0, nl, ws):
-    s = synth.WORKLOADS["stack"]
+def run_stack(cfg, layers, x0, nl, ws, s=None):
+    s = s or synth.WORKLOADS["stack"]
     xs = torch.full((nl, s.hidden), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
     outs = torch.full((nl, s.hidden), float("nan"), dtype=torch.float32, device="cuda")
     ids = torch.full((nl, s.top_k), -1, dtype=torch.int32, device="cuda")
@@ -70,12 +70,13 @@ def run_stack(cfg, layers, x0, nl, ws):
     return xs, outs, ids, w
 
 
-def run_chained(cfg, layers, x0, nl):
-    s = synth.WORKLOADS["stack"]
+def run_chained(cfg, layers, x0, nl, s=None):
+    s = s or synth.WORKLOADS["stack"]
     xs = torch.empty((nl, s.hidden), dtype=torch.bfloat16, device="cuda")
     outs = torch.empty((nl, s.hidden), dtype=torch.float32, device="cuda")
-    ids = torch.empty((nl, s.top_k), dtype=torch.int32, device="cuda")
-    w = torch.empty((nl, s.top_k), dtype=torch.float32, device="cuda")
+    kp = (s.top_k + 3) // 4 * 4  # rows 16-byte aligned, as the layer call's routing outputs must be
+    ids = torch.empty((nl, kp), dtype=torch.int32, device="cuda")
+    w = torch.empty((nl, kp), dtype=torch.float32, device="cuda")
     ws = layers[0].workspace(1)
     xs[0].copy_(x0[0])
     for l, dl in enumerate(layers):
@@ -84,7 +85,7 @@ def run_chained(cfg, layers, x0, nl):
         else:
             qm.moe_layer_forward_chained(cfg, 1, xs[l - 1:l], outs[l - 1:l], xs[l:l + 1], dl.gate_w, dl.bias,
                                          dl.arena, dl.shared, outs[l:l + 1], ids[l], w[l], ws)
-    return xs, outs, ids, w
+    return xs, outs, ids[:, :s.top_k], w[:, :s.top_k]
 
 
 def stack_ws(cfg, nl):
@@ -186,3 +187,35 @@ def test_stack_decode_graph_replay():
             _ = layers[rep].forward(x0[0:1])  # eager work between replays
             torch.cuda.synchronize()
     assert_stack_status_ok(cfg, nl, ws)
+
+
+@pytest.mark.parametrize("nl", [1, 4])
+def test_stack_decode_tiny_shape(nl):
+    """The tiny shape (hidden 256, ffn 128, 8 experts top-2 + 1 shared: one 256-element router step, one
+    packed down tile per row, 8 router rows in 8 shared workgroups), router weights, experts and Zipf
+    selection biases drawn per layer: moe_stack_decode equals the chained calls bit for bit, and every
+    layer's routing equals the oracle's on the GPU's input to that layer."""
+    s = synth.WORKLOADS["tiny"]
+    cfg = cfg_of(s)
+    layers, host = [], []
+    for l in range(nl):
+        inp = synth.layer_inputs(s, layer=l)
+        b = synth.zipf_bias(s, 0.05, layer=l)
+        layers.append(qm.DeviceLayer(cfg, inp["gate_w"], torch.from_numpy(b).cuda(), inp["arena"], inp["shared"]))
+        host.append((inp, b))
+    for tok in (0, 1, 2):
+        x0 = to_dev_bf16(synth.tokens(s, 1, first=300 + tok))
+        ws = stack_ws(cfg, nl)
+        log(f"stack decode tiny L={nl} token={tok}")
+        got = run_stack(cfg, layers, x0, nl, ws, s)
+        want = run_chained(cfg, layers, x0, nl, s)
+        torch.cuda.synchronize()
+        assert_stack_status_ok(cfg, nl, ws)
+        assert_same(got, want, f"tiny L={nl} token {tok}")
+        xin = got[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        gid = got[2].cpu().numpy()
+        for l in range(nl):
+            inp, b = host[l]
+            _, rid, _ = oracle.layer(xin[l:l + 1], inp["gate_w"], inp["arena"], inp["shared"], s.top_k, s.ffn,
+                                     s.routed_scale, b)
+            assert np.array_equal(gid[l:l + 1], rid), (tok, l)
