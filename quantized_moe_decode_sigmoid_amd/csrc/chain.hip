@@ -28,8 +28,7 @@ __global__ __launch_bounds__(kChainThreads) void k_residual_rmsnorm(const float*
     const float h = bf16_bits_to_f32(xr[i]) + o[i];
     ss = __builtin_fmaf(h, h, ss);
   }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) ss += __shfl_xor(ss, s, 64);
+  ss = wave_xor_sum(ss);
   if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
   __syncthreads();
   float tot = 0.0f;

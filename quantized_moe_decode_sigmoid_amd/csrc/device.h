@@ -114,6 +114,52 @@ __device__ __forceinline__ void dma16_stream(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, lds, 16, 0, kNonTemporal);
 }
 
+// Cross-lane partners without a trip through LDS memory: lane i gets the
+// value of lane i ^ M -- M = 1, 2 (DPP quad permutes), 8 (DPP rotation by 8
+// inside a row of 16), 4 and 16 (ds_swizzle with an xor mask, which stays in
+// the LDS unit's crossbar), 32 (v_permlane32_swap: lanes below 32 take the
+// swapped-in upper half, the others the lower half).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  const int u = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (M == 1) {
+    r = __builtin_amdgcn_update_dpp(0, u, 0xB1, 0xf, 0xf, false);
+  } else if constexpr (M == 2) {
+    r = __builtin_amdgcn_update_dpp(0, u, 0x4E, 0xf, 0xf, false);
+  } else if constexpr (M == 4) {
+    r = __builtin_amdgcn_ds_swizzle(u, 0x101f);
+  } else if constexpr (M == 8) {
+    r = __builtin_amdgcn_update_dpp(0, u, 0x128, 0xf, 0xf, false);
+  } else if constexpr (M == 16) {
+    r = __builtin_amdgcn_ds_swizzle(u, 0x401f);
+  } else {
+    static_assert(M == 32, "xor partners 1 .. 32");
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    r = (threadIdx.x & 32) ? (int)p[0] : (int)p[1];
+  }
+  return __builtin_bit_cast(float, r);
+}
+
+// The wavefront's xor butterfly: v + v(lane ^ 32), then partners 16, 8, 4, 2
+// and 1 -- the same additions in the same order as a loop of xor shuffles;
+// every lane ends with the same value.
+__device__ __forceinline__ float wave_xor_sum(float v) {
+  v = v + lane_xor<32>(v);
+  v = v + lane_xor<16>(v);
+  v = v + lane_xor<8>(v);
+  v = v + lane_xor<4>(v);
+  v = v + lane_xor<2>(v);
+  v = v + lane_xor<1>(v);
+  return v;
+}
+
+// Lane i gets the value of lane i + 1 of its row of 16 (DPP row shift; lane
+// 15 of a row gets 0).
+__device__ __forceinline__ float lane_next_in_row(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x101, 0xf, 0xf, false));
+}
+
 // Every load of this wavefront (LDS DMA included) has landed.
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

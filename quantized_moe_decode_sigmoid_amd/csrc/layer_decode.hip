@@ -176,8 +176,7 @@ __device__ __forceinline__ void chained_input(const DecodeArgs& a, int lane, flo
         ss = __builtin_fmaf(hv, hv, ss);
       }
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) ss += __shfl_xor(ss, s, 64);
+    ss = wave_xor_sum(ss);
     part[q] = ss;
   }
   float tot = 0.0f;
@@ -557,7 +556,7 @@ __device__ __forceinline__ void down_slot(ExpertsLds& sh, const u32x4 (&nib)[kDn
     acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), cc[3], acc[3]);
   }
 #pragma unroll
-  for (int j = 0; j < 4; j++) acc[j] += __shfl_down(acc[j], 1, 64);
+  for (int j = 0; j < 4; j++) acc[j] += lane_next_in_row(acc[j]);
   if (c == 0) *reinterpret_cast<f32x4*>(&d.part[wave][S][4 * G]) = acc;
 }
 
@@ -751,8 +750,7 @@ __device__ void stack_input(const DecodeArgs& a, const float (&o)[kInPer], uint1
         ss = __builtin_fmaf(h, h, ss);
       }
     }
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) ss += __shfl_xor(ss, s, 64);
+    ss = wave_xor_sum(ss);
     if ((v & 63) == 0) nred[v >> 6] = ss;
   }
   __syncthreads();
@@ -786,9 +784,7 @@ __device__ __forceinline__ float router_logit_lds(const uint16_t* xs, const floa
     p = __builtin_fmaf(bf16_bits_to_f32(xv.y & 0xffffu), w.z, p);
     p = __builtin_fmaf(bf16_bits_to_f32(xv.y >> 16), w.w, p);
   }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_xor(p, s, 64);
-  return p;
+  return wave_xor_sum(p);
 }
 
 // The previous layer's input (layer 0: the step's input) into LDS by DMA,

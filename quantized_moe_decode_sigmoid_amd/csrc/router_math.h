@@ -75,9 +75,7 @@ __device__ __forceinline__ float router_logit_vals(const uint2 (&xv)[MMAX], int 
       p = __builtin_fmaf(bf16_bits_to_f32(xv[m].y >> 16), w[m].w, p);
     }
   }
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) p = p + __shfl_xor(p, s, 64);
-  return p;
+  return wave_xor_sum(p);
 }
 
 // The same with the lane's activations read from the row xrow.
