@@ -159,7 +159,8 @@ int32_t moe_resolved_precision(const moe_config* cfg, int32_t T);
 size_t moe_workspace_bytes(const moe_config* cfg, int32_t T);
 
 /* Zero the status word of a workspace (its first 4 bytes).  The decode path
- * of moe_layer_forward (T = 1, K <= 4, H <= 4096, F <= 1024, FP32 contract)
+ * of moe_layer_forward (T = 1, K <= 4, H <= 4096, F <= 1024, H <= 4 F with a shared
+ * expert, FP32 contract)
  * hands data between workgroups of one kernel and bounds every wait; a wait
  * that gives up (which a correct launch never does) sets this word to 1.
  * Workspaces need no other preparation. */

@@ -91,9 +91,12 @@ int max_chunks(const moe_config* c, int T) { return max_chunks(c, T, chunk_rows(
 
 // The two-launch decode path covers one token with the exact-weight contract.
 // Its second kernel hands data between workgroups, so it is taken only when
-// the device holds that kernel's whole grid at once.
+// the device holds that kernel's whole grid at once.  The shared expert's
+// down rows are split over its F/16 gate/up workgroups, at most 4 row tiles
+// of 16 each: hidden <= 4 ffn.
 bool decode_path(const moe_config* c, int T) {
-  return T == 1 && c->n_experts > 0 && c->codec == MOE_CODEC_IQ4_NL && c->top_k <= qmoe::kMaxDecodeK && c->ffn <= qmoe::kMaxDecodeFfn &&
+  return T == 1 && c->n_experts > 0 && c->codec == MOE_CODEC_IQ4_NL && c->top_k <= qmoe::kMaxDecodeK &&
+         c->ffn <= qmoe::kMaxDecodeFfn && (c->n_shared == 0 || c->hidden <= 4 * c->ffn) &&
          c->hidden <= qmoe::kMaxDecodeHidden && resolve_precision(c, T) == MOE_PREC_FP32 &&
          qmoe::decode_grid_coresident(c->ffn, c->top_k, c->hidden, c->n_shared);
 }
@@ -120,7 +123,7 @@ Plan make_plan(const moe_config* c, int T) {
     return here;
   };
   p.status = take(4);
-  p.hw = take((size_t)(c->top_k + 1) * F * 4);
+  p.hw = take((size_t)qmoe::hw_words(c->top_k, (int)F, (int)H) * 4);
   p.scores = take((size_t)T * (E + c->shared_gate) * 4);
   p.ids = take(R * 4);
   p.w = take((size_t)T * weight_cols(c) * 4);

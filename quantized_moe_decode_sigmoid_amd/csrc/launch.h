@@ -91,7 +91,8 @@ struct DecodeArgs {
   float* scores;       // [E + gated] sigmoid scores (first kernel -> second)
   int32_t* ids;        // [K] routing outputs
   float* w;            // [K + gated]
-  uint32_t* hw;        // [(K + 1) * F] h words: bf16(h) | bf16(h - bf16(h)) << 16
+  uint32_t* hw;        // [hw_words(K, F, H)]: h words bf16(h) | bf16(h - bf16(h)) << 16 of the K + 1 slots
+                       // ([K + 1][F]), then the shared expert's down rows y_s[H] (fp32 bits)
   float* out;          // [H]
   uint32_t* err;       // set to 1 if a wait gave up
   // chained input (x_prev non-null): the first kernel forms x = bf16(rmsnorm(x_prev + out_prev)) itself (the
@@ -101,6 +102,9 @@ struct DecodeArgs {
   float eps;
   int n_router, n_shared_wg, n_routed_wg, n_down_wg;  // grid partition (set by the launcher)
 };
+
+// Words of the decode hand-off buffer: h of K + 1 slots, the shared expert's down rows.
+__host__ __device__ inline int hw_words(int K, int F, int H) { return (K + 1) * F + H; }
 
 hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream);
 
@@ -130,7 +134,7 @@ struct StackArgs {
   int32_t* ids_all;     // [L][K]
   float* w_all;         // [L][K + gated]
   float* scores_all;    // [L][E + gated]
-  uint32_t* hw_all;     // [L][(K + 1) F]
+  uint32_t* hw_all;     // [L][(K + 1) F] (the stack keeps the shared expert in its down workgroups)
 };
 
 hipError_t launch_stack_decode(StackArgs s, const StackLayer* layers, hipStream_t stream);

@@ -198,7 +198,7 @@ __global__ __launch_bounds__(64) void k_decode_scores(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int e = blockIdx.x;
   // reset the h hand-off words of k_decode_experts
-  const int n_words = (a.K + 1) * a.F;
+  const int n_words = hw_words(a.K, a.F, a.H);
   for (int i = blockIdx.x * 64 + threadIdx.x; i < n_words; i += gridDim.x * 64) a.hw[i] = kNotReady;
   if (e < a.E + a.gated) {  // row E: the shared expert's gate
     float4 w[MMAX];
@@ -278,11 +278,12 @@ __device__ __forceinline__ RouteIn route_poll(const DecodeArgs& a) {
 // scores, and the weights scale * s_k / (((s_0 + s_1) + ...)) in slot order.
 //
 // route_rank_lds: every expert's rank among all E counted by its own thread
-// from LDS, three barriers (≈2.3 µs at E = 64).  The two-launch decode keeps
-// this form: measured against route_rank_wave there, the later start of the
-// routed experts' tiles lets the shared expert's tiles (no routing needed)
-// land first, so the down workgroups do the shared slot while the routed h is
-// still being made (18.6 against 19.9 µs per call).
+// from LDS, three barriers (≈2.3 µs at E = 64).  The decode kernel's down
+// workgroups use it: they only need the routing to request their routed
+// tiles, and requesting those later leaves the routed gate/up tiles more of
+// the memory system (measured: 17.57 against 17.64 µs per call with
+// route_rank_wave there, and 18.6 against 19.9 µs before the shared expert's
+// down rows moved to its own workgroups).
 __device__ void route_rank_lds(const DecodeArgs& a, RouteLds& r, RouteIn v) {
   const int e = threadIdx.x;
   if (e < a.E) {
@@ -311,8 +312,9 @@ __device__ void route_rank_lds(const DecodeArgs& a, RouteLds& r, RouteIn v) {
 }
 
 // route_rank_wave: wavefront 0 takes the K in K rounds of topk_take, from
-// registers when E <= 64, else through LDS, one barrier (≈0.9 µs at E = 64);
-// the stack kernel's form, where the ranking follows the wait for the scores.
+// registers when E <= 64, else through LDS, one barrier (≈0.9 µs at E = 64):
+// the routed gate/up workgroups' form, and every workgroup's in the stack
+// kernel, where the ranking follows the wait for the scores.
 __device__ void route_rank_wave(const DecodeArgs& a, RouteLds& r, RouteIn v) {
 #pragma clang fp contract(off)
   const int e = threadIdx.x;
@@ -364,7 +366,7 @@ __device__ void route_rank_wave(const DecodeArgs& a, RouteLds& r, RouteIn v) {
   __syncthreads();
 }
 
-__device__ __forceinline__ void route_local(const DecodeArgs& a, RouteLds& r) { route_rank_lds(a, r, route_fetch(a)); }
+__device__ __forceinline__ void route_local(const DecodeArgs& a, RouteLds& r) { route_rank_wave(a, r, route_fetch(a)); }
 
 // ---------------------------------------------------------------- gate / up role
 
@@ -598,8 +600,103 @@ __device__ __forceinline__ void poll_h_rows(const DecodeArgs& a, DownLds& d, int
       make_uint2((v.x >> 16) | (v.y & 0xffff0000u), (v.z >> 16) | (v.w & 0xffff0000u));
 }
 
+// The shared expert's down rows y_s[H] (fp32 bits) follow the h words of the
+// K + 1 slots in the same hand-off buffer.
+__device__ __forceinline__ uint32_t* shared_y(const DecodeArgs& a) { return a.hw + (a.K + 1) * a.F; }
+
+// Word i of a hand-off array, re-read until it no longer shows the "not
+// ready" pattern (bounded, like every wait).
+__device__ __forceinline__ uint32_t poll_word(const DecodeArgs& a, const uint32_t* base, int i) {
+  const __amdgpu_buffer_rsrc_t rb = buffer_of(base);
+  uint32_t v = ld_dev(rb, 4 * i);
+  uint32_t it = 0;
+  while (v == kNotReady) {
+    if (give_up(a.err, ++it)) {
+      st_dev(buffer_of(a.err), 0, 1u);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_dev(rb, 4 * i);
+  }
+  return v;
+}
+
+// The shared expert's down projection, spread over the shared workgroups
+// after their gate/up row tile (so that the down workgroups only wait for the
+// routed slots): workgroup blk takes q = ceil((H/16) / (F/16)) <= 4 row tiles
+// of H from tile q * blk.  Item i = wave + 16 j is (row tile i / nkg, packed
+// tile kg = i % nkg).  It waits for the shared expert's whole h, then
+// publishes its rows of y_s with device-scope stores, in the arithmetic of the
+// down role's slots: each item's 4 blocks in order (scale times MFMA result,
+// fused), the two B columns added, the items of a row added in kg order.
+constexpr int kShDnMaxTiles = 4;
+constexpr int kShDnItems = kShDnMaxTiles * (kMaxDecodeFfn / 128) / kDecWaves;
+static_assert(kShDnMaxTiles <= 2 * kDnSlots, "row tile t's scale pieces in d.scales[t / 2][t % 2]");
+static_assert(kShDnMaxTiles * (kMaxDecodeFfn / 128) * 16 <= kDecWaves * kDnSlots * 16, "the parts fit in d.part");
+static_assert(kShDnMaxTiles * (kMaxDecodeFfn / 128) <= kShDnItems * kDecWaves, "the items fit the waves");
+
+__device__ void shared_down_part(const DecodeArgs& a, int blk, ExpertsLds& sh) {
+  DownLds& d = sh.u.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, G = lane >> 4;
+  const int nkg = a.F >> 7;
+  const int n_rt = a.H >> 4;
+  const int q = (n_rt + a.n_shared_wg - 1) / a.n_shared_wg;
+  const int t0 = blk * q, nt = max(0, min(q, n_rt - t0));
+  const int n_items = nt * nkg;
+  const uint8_t* down = a.shared + 2 * (a.expert_bytes / 3);
+  // row tile t's scale pieces in d.scales[t / 2][t % 2], its items' parts in
+  // part[t][kg][16] (a view of d.part)
+  float(*part)[kMaxDecodeFfn / 128][16] = reinterpret_cast<float(*)[kMaxDecodeFfn / 128][16]>(&d.part[0][0][0]);
+  u32x4 nib[kShDnItems];
+#pragma unroll
+  for (int j = 0; j < kShDnItems; j++) {
+    const int i = wave + kDecWaves * j;
+    if (i < n_items) nib[j] = ld16(down + ((int64_t)(t0 + i / nkg) * nkg + i % nkg) * kTileBytes + 16 * lane);
+  }
+  if (wave < nt) dma_slot_scales(d, down + (int64_t)(t0 + (wave & ~1)) * nkg * kTileBytes, nkg, wave >> 1, wave & 1);
+  poll_h_rows(a, d, a.K, 1);
+  wait_loads();
+  __syncthreads();
+  const uint16_t* hp = c == 1 ? d.hl[kMaxDecodeK] : d.hh[kMaxDecodeK];
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kShDnItems; j++) {
+    const int i = wave + kDecWaves * j;
+    if (i < n_items) {
+      const int t = i / nkg, kg = i % nkg;
+      f32x4 acc = zero;
+#pragma unroll
+      for (int b = 0; b < 4; b++) {
+        const bf16x8 bop = *reinterpret_cast<const bf16x8*>(hp + 32 * (4 * kg + b) + 8 * G);
+        const bf16x8 wa = decode_word(sh.tbl, uword(nib[j], b), lane & 31);
+        const uint32_t s01 = d.scales[t >> 1][t & 1][kg][8 * G + 2 * b];
+        const uint32_t s23 = d.scales[t >> 1][t & 1][kg][8 * G + 2 * b + 1];
+        const f32x4 cc = mfma16x16x32(wa, bop, zero);
+        acc[0] = __builtin_fmaf(half_bits_to_float(s01), cc[0], acc[0]);
+        acc[1] = __builtin_fmaf(half_bits_to_float(s01 >> 16), cc[1], acc[1]);
+        acc[2] = __builtin_fmaf(half_bits_to_float(s23), cc[2], acc[2]);
+        acc[3] = __builtin_fmaf(half_bits_to_float(s23 >> 16), cc[3], acc[3]);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; k++) acc[k] += lane_next_in_row(acc[k]);
+      if (c == 0) *reinterpret_cast<f32x4*>(&part[t][kg][4 * G]) = acc;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nt * 16) {
+    const int t = threadIdx.x >> 4, r16 = threadIdx.x & 15;
+    float y = 0.0f;
+    for (int kg = 0; kg < nkg; kg++) y += part[t][kg][r16];
+    st_dev(buffer_of(shared_y(a)), 4 * (16 * (t0 + t) + r16), __float_as_uint(y));
+  }
+}
+
 // PERSIST (the stack kernel): the scores come from other workgroups of the
-// same launch (waited for, bounded).
+// same launch (waited for, bounded), and the shared expert is one more slot
+// of these workgroups.  Otherwise (the decode kernel) the shared expert's down
+// rows come finished from the shared workgroups (shared_down_part) and are
+// waited for in the combine.
 template <bool PERSIST>
 __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   DownLds& d = sh.u.d;
@@ -611,22 +708,25 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   const bool has_tile = kg < nkg;
   const int kgc = has_tile ? kg : nkg - 1;
   const int64_t mat_bytes = a.expert_bytes / 3;
+  constexpr bool kSharedSlot = PERSIST;
 
   auto down_tiles = [&](const uint8_t* ex, int rtile) {
     return ex + 2 * mat_bytes + (int64_t)rtile * nkg * kTileBytes;
   };
   u32x4 nib[kDnSlots];
-  // 1. the router scores (and the shared expert's gate), then the shared
-  //    expert's tiles (they need no routing)
+  // 1. the router scores (and the shared expert's gate); in the stack, the
+  //    shared expert's tiles (they need no routing)
   RouteIn rin;
   float gate = 1.0f;
   if constexpr (!PERSIST) {
     rin = route_fetch(a);
     gate = a.gated ? a.scores[a.E] : 1.0f;
   }
-  const uint8_t* shx = a.n_shared ? a.shared : a.arena;
-  nib[kMaxDecodeK] = ld16(down_tiles(shx, rt) + (int64_t)kgc * kTileBytes + 16 * lane);
-  if (wave < 2) dma_slot_scales(d, down_tiles(shx, 2 * blk), nkg, kMaxDecodeK, wave);
+  if constexpr (kSharedSlot) {
+    const uint8_t* shx = a.n_shared ? a.shared : a.arena;
+    nib[kMaxDecodeK] = ld16(down_tiles(shx, rt) + (int64_t)kgc * kTileBytes + 16 * lane);
+    if (wave < 2) dma_slot_scales(d, down_tiles(shx, 2 * blk), nkg, kMaxDecodeK, wave);
+  }
   build_pair_table(sh.tbl);
   if constexpr (PERSIST) {
     rin = route_poll(a);
@@ -640,14 +740,16 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
     const int slot = (wave - 2) >> 1;
     dma_slot_scales(d, down_tiles(a.arena + (int64_t)r.ids[slot] * a.expert_bytes, 2 * blk), nkg, slot, wave & 1);
   }
-  // 3. h of the shared expert (made first) and its MFMAs, while the routed
-  //    experts' h is still being made
+  // 3. in the stack, h of the shared expert (made first) and its MFMAs, while
+  //    the routed experts' h is still being made
   static_assert(kMaxDecodeK * (kMaxDecodeFfn / 4) <= kDecThreads, "one h piece per thread");
-  if (a.n_shared) {
-    poll_h_rows(a, d, a.K, 1);
-    wait_loads();  // this wave's tiles and scale pieces (LDS DMA)
-    __syncthreads();
-    if (has_tile) down_slot<kMaxDecodeK>(sh, nib, rtl, kg);
+  if constexpr (kSharedSlot) {
+    if (a.n_shared) {
+      poll_h_rows(a, d, a.K, 1);
+      wait_loads();  // this wave's tiles and scale pieces (LDS DMA)
+      __syncthreads();
+      if (has_tile) down_slot<kMaxDecodeK>(sh, nib, rtl, kg);
+    }
   }
   // 4. h of the routed slots and their MFMAs
   poll_h_rows(a, d, 0, a.K);
@@ -658,19 +760,23 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   // 5. the wave parts of each (row tile, slot) added in order
   for (int i = threadIdx.x; i < kDnSlots * 32; i += kDecThreads) {
     const int s2 = i >> 5, row = i & 31, rt2 = row >> 4, r16 = row & 15;
-    if (s2 < a.K || (s2 == kMaxDecodeK && a.n_shared)) {
+    if (s2 < a.K || (kSharedSlot && s2 == kMaxDecodeK && a.n_shared)) {
       float t = 0.0f;
       for (int q = 0; q < nkg; q++) t += d.part[rt2 + 2 * q][s2][r16];
       d.y[s2][row] = t;
     }
   }
   __syncthreads();
-  // 6. slot-order combine of these 32 rows
+  // 6. slot-order combine of these 32 rows, the shared expert's row last
   if (threadIdx.x < 32) {
     const int row = threadIdx.x;
     float acc = 0.0f;
     for (int k = 0; k < a.K; k++) acc = __builtin_fmaf(r.w[k], d.y[k][row], acc);
-    if (a.n_shared) acc = a.gated ? __builtin_fmaf(gate, d.y[kMaxDecodeK][row], acc) : acc + d.y[kMaxDecodeK][row];
+    if (a.n_shared) {
+      const float ys = kSharedSlot ? d.y[kMaxDecodeK][row]
+                                   : __uint_as_float(poll_word(a, shared_y(a), 32 * blk + row));
+      acc = a.gated ? __builtin_fmaf(gate, ys, acc) : acc + ys;
+    }
     a.out[32 * blk + row] = acc;
   }
   // the routing outputs, written once (w[K]: the shared expert's gate)
@@ -687,9 +793,10 @@ __global__ __launch_bounds__(kDecThreads, 8) void k_decode_experts(DecodeArgs a)
   __shared__ ExpertsLds sh;
   int blk = blockIdx.x;
   const int n_rt_f = a.F >> 4;
-  // Block order: routed gate/up, shared gate/up, down.  Every producer of an
-  // h word has a lower block index than every workgroup that waits for it,
-  // so the kernel completes whatever number of workgroups is resident.
+  // Block order: routed gate/up, shared gate/up (then the shared expert's
+  // down rows, which wait for the h of every shared workgroup), down.  The
+  // waits cross workgroups both ways, so the whole grid must be resident at
+  // once (the plan checks it).
   // Workgroups are placed in block order, one per CU first: the routed ones,
   // whose first request is the router scores, get a CU of their own, so that
   // request does not queue behind another workgroup's weight tiles.
@@ -699,6 +806,8 @@ __global__ __launch_bounds__(kDecThreads, 8) void k_decode_experts(DecodeArgs a)
     gate_up_role<1>(a, a.arena + (int64_t)sh.route.ids[slot] * a.expert_bytes, slot, rt, sh);
   } else if ((blk -= a.n_routed_wg) < a.n_shared_wg) {
     gate_up_role<1>(a, a.shared, a.K, blk, sh);
+    __syncthreads();  // the gate/up LDS is reused
+    shared_down_part(a, blk, sh);
   } else {
     down_role<false>(a, blk - a.n_shared_wg, sh);
   }
