@@ -12,8 +12,8 @@ Default run (no flags): the four measured workloads in one process, one JSON lin
     the fraction of bf16 MFMA peak, and the HBM fraction.
   * batch (nested): one T=128 call of the Xing4 layer per step.
   * stack (nested): 38 Xing4 layers resident in HBM, T=1 per step through all of them, each
-    layer's input chained from the previous one, by moe_stack_decode (one launch per layer,
-    the router folded in); the same step as chained per-layer calls timed beside it;
+    layer's input chained from the previous one, by moe_stack_decode (one call: two decode
+    launches per layer); the same step as chained per-layer calls timed beside it;
     Zipf(1.1) popularity.
   * variants (nested): the sigmoid-gated shared expert (decode), the W4A8 contract (Q8_0
     activations: T=1, T=128, the T=2048 prefill call), a dense FFN block (hidden 3584,
@@ -603,9 +603,9 @@ def run_batch(args, check):
 def run_stack(args, check):
     """38 MoE layers of the Xing4 shape resident in HBM, one token per step (T=1) through all of them,
     each layer's input chained from the previous layer's input and output by bf16(rmsnorm(x + out)):
-    moe_stack_decode (one reset launch, then one launch per layer with the router folded in), timed
-    through a HIP graph; the same step as chained moe_layer_forward_chained calls timed beside it;
-    Zipf(1.1) expert popularity."""
+    moe_stack_decode (one call: per layer the decode plan's two launches, the layer's input formed in the
+    first), timed through a HIP graph; the same step as chained moe_layer_forward_chained calls timed beside
+    it; Zipf(1.1) expert popularity."""
     import torch
 
     import quantized_moe_decode_sigmoid_amd as qm
@@ -775,14 +775,14 @@ def run_stack(args, check):
                                "shared, ffn 1024, IQ4_NL, sigmoid router, scale 2.0; layer input = bf16(rmsnorm("
                                "previous input + previous output)) by one fused kernel; Zipf(1.1) expert popularity",
                    "layers": nl, "distinct_tokens": S, "zipf_lambda": lam, "graph": True,
-                   "call": "moe_stack_decode: one reset launch, then one launch per layer (router, norm of the "
-                           "previous layer's input and output, experts)",
+                   "call": "moe_stack_decode: per layer the router kernel (norm of the previous layer's input "
+                           "and output, logits) and the experts kernel",
                    "expert_sets": f"router weights and biases drawn per layer; expert weights drawn for {nd} "
                                   f"layers, each layer's placed at its own address"},
         "step_spread": spread(np.asarray(per_replay) / S),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("stack_traffic.json"),
-                     "kernel": "whole step: k_stack_reset + one k_stack_layer per layer",
+                     "kernel": "whole step: per layer k_decode_scores_chained + k_decode_experts",
                      "bytes_per_token": expert_bytes + router_bytes},
         "cpu_baseline": cpu,
         "parity": parity,

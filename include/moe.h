@@ -300,19 +300,18 @@ moe_status moe_layer_forward_chained(const moe_config* cfg, int32_t T, const voi
  * captured as a whole rather than call by call):
  *   x_0 = x0;  out_l = moe_layer_forward on x_l with layer l's weights;
  *   x_{l+1} = bf16(rmsnorm(x_l + out_l)) with eps (moe_residual_rmsnorm).
- * L + 1 launches on `stream`: one that resets the hand-off words of every
- * layer, then one per layer in which the router is folded into the expert
- * kernel of the decode plan (the shared expert's workgroups form the layer's
- * input and make one router row each while the shared expert's tiles land;
- * the other workgroups wait for the scores through device-scope words), so a
- * layer costs one launch instead of the decode plan's two.  Results are
- * bit-identical to L calls of moe_layer_forward_chained (layer 0:
+ * 2 L launches on `stream`: per layer the decode plan's two kernels, the
+ * layer's input formed in the first (as in moe_layer_forward_chained: 256
+ * threads per router row form bf16(rmsnorm(x + out)) and the logit); layer 0
+ * reads x0, copies it to row 0 of x_all and clears the status word.  Results
+ * are bit-identical to L calls of moe_layer_forward_chained (layer 0:
  * moe_layer_forward on x0) with the same weights: the same routing, x and
- * outputs.
+ * outputs.  One token's decode workspace is reused by every layer.
  *   layers_host  host array of L layer descriptions (device pointers inside;
  *                gate_w fp32 [E + shared_gate][H], sel_bias fp32 [E] or
- *                NULL, arena and shared packed by moe_pack_experts), read
- *                during the call only
+ *                NULL, arena and shared packed by moe_pack_experts; shared
+ *                may be NULL without a shared expert), read during the
+ *                call only
  *   x0_dev       bf16 [H]        layer 0's input
  *   x_all_dev    bf16 [L][H]     out: every layer's input (row 0 = x0); must
  *                                not overlap x0_dev
@@ -321,12 +320,11 @@ moe_status moe_layer_forward_chained(const moe_config* cfg, int32_t T, const voi
  *   w_all_dev    fp32 [L][K + shared_gate]  out, or NULL
  *   ws           >= moe_stack_workspace_bytes(cfg, L)
  * Supported (else MOE_EUNSUPPORTED): the decode plan's shapes (precision AUTO
- * or FP32, IQ4_NL, top_k <= 4, ffn <= 1024, hidden <= 4096), n_shared = 1,
- * n_experts + shared_gate <= ffn / 16 (router row r is made by the shared
- * expert's workgroup r), 1 <= L <= 64, and a layer's grid (the decode plan's)
- * resident on the device at once.  Every wait is bounded; if one gives up,
- * the outputs are wrong and the status word is 1 (moe_stack_status).
- * eps >= 0 and finite. */
+ * or FP32, IQ4_NL, n_experts >= 1, top_k <= 4, ffn <= 1024, hidden <= 4096,
+ * hidden <= 4 ffn with a shared expert; gated or not), 1 <= L <= 64, and the
+ * decode kernel's grid resident on the device at once.  Every wait is
+ * bounded; if one gives up, the outputs are wrong and the status word is 1
+ * (moe_stack_status).  eps >= 0 and finite. */
 typedef struct {
   const float* gate_w;
   const float* sel_bias;

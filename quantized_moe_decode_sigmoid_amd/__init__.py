@@ -251,7 +251,7 @@ def stack_layers(layers):
 
 def moe_stack_decode(cfg, L, layers, x0, x_all, out_all, ids_all=None, w_all=None, ws=None, ws_bytes=None, eps=1e-6,
                      stream=None):
-    """One decode token through L chained layers, one launch per layer with the router folded in (layers: stack_layers(...) array)."""
+    """One decode token through L chained layers in one call, two decode launches per layer (layers: stack_layers(...))."""
     ws_bytes = ws.numel() * ws.element_size() if ws_bytes is None and ws is not None else (ws_bytes or 0)
     _check(_lib.moe_stack_decode(ctypes.byref(cfg), L, layers, _p(x0), eps, _p(x_all), _p(out_all), _p(ids_all),
                                  _p(w_all), _p(ws), ws_bytes, _stream(stream)), "moe_stack_decode")

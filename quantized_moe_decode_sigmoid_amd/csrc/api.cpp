@@ -94,11 +94,14 @@ int max_chunks(const moe_config* c, int T) { return max_chunks(c, T, chunk_rows(
 // the device holds that kernel's whole grid at once.  The shared expert's
 // down rows are split over its F/16 gate/up workgroups, at most 4 row tiles
 // of 16 each: hidden <= 4 ffn.
-bool decode_path(const moe_config* c, int T) {
-  return T == 1 && c->n_experts > 0 && c->codec == MOE_CODEC_IQ4_NL && c->top_k <= qmoe::kMaxDecodeK &&
+bool decode_shape(const moe_config* c) {
+  return c->n_experts > 0 && c->codec == MOE_CODEC_IQ4_NL && c->top_k <= qmoe::kMaxDecodeK &&
          c->ffn <= qmoe::kMaxDecodeFfn && (c->n_shared == 0 || c->hidden <= 4 * c->ffn) &&
-         c->hidden <= qmoe::kMaxDecodeHidden && resolve_precision(c, T) == MOE_PREC_FP32 &&
-         qmoe::decode_grid_coresident(c->ffn, c->top_k, c->hidden, c->n_shared);
+         c->hidden <= qmoe::kMaxDecodeHidden && resolve_precision(c, 1) == MOE_PREC_FP32;
+}
+
+bool decode_path(const moe_config* c, int T) {
+  return T == 1 && decode_shape(c) && qmoe::decode_grid_coresident(c->ffn, c->top_k, c->hidden, c->n_shared);
 }
 
 // Workspace plan: 256-byte aligned sub-buffers.
@@ -448,41 +451,31 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 namespace {
 
-// Workspace of moe_stack_decode: the hand-off words of every layer, the
-// status word, the device copy of the layers' pointers, routing outputs when
-// the caller passes none.
+// Workspace of moe_stack_decode: the decode plan's workspace of one token
+// (scores, hand-off words, status word), which every layer reuses, then the
+// routing outputs of every layer for a caller that passes none.
 struct StackPlan {
-  size_t scores, hw, status, ids, w, total;
+  Plan dec;
+  size_t ids, w, total;
 };
 
 StackPlan make_stack_plan(const moe_config* c, int L) {
   StackPlan p;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += (bytes + 255) & ~(size_t)255;
-    return o;
-  };
-  const size_t E = (size_t)c->n_experts + c->shared_gate, K = (size_t)c->top_k;
-  (void)E;
-  p.scores = take((size_t)L * qmoe::kScoreReplicas * qmoe::kScoreRepStride * 4);
-  p.hw = take((size_t)L * (K + 1) * c->ffn * 4);
-  p.status = take(16);
-  p.ids = take((size_t)L * K * 4);
-  p.w = take((size_t)L * (K + c->shared_gate) * 4);
+  p.dec = make_plan(c, 1);
+  size_t off = align_up(p.dec.total);
+  p.ids = off;
+  off += align_up((size_t)L * c->top_k * 4);
+  p.w = off;
+  off += align_up((size_t)L * weight_cols(c) * 4);
   p.total = off;
   return p;
 }
 
-// The shapes the stack kernel covers (with L checked by the caller).
+// The shapes of the decode plan (the device check comes in moe_stack_decode).
 moe_status check_stack(const moe_config* cfg, int32_t L) {
   TRY(check_common(cfg, 1));
   if (L < 1 || L > qmoe::kMaxStackLayers) return MOE_EUNSUPPORTED;
-  if (cfg->n_experts < 1 || cfg->n_shared != 1 || cfg->n_experts + cfg->shared_gate > cfg->ffn / 16)
-    return MOE_EUNSUPPORTED;
-  if (cfg->codec != MOE_CODEC_IQ4_NL || cfg->top_k > qmoe::kMaxDecodeK || cfg->ffn > qmoe::kMaxDecodeFfn ||
-      cfg->hidden > qmoe::kMaxDecodeHidden || resolve_precision(cfg, 1) != MOE_PREC_FP32)
-    return MOE_EUNSUPPORTED;
+  if (!decode_shape(cfg)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -506,7 +499,8 @@ MOE_API moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_
     TRY(need(layers_host[l].gate_w));
     TRY(optional_ptr(layers_host[l].sel_bias));
     TRY(need(layers_host[l].arena));
-    TRY(need(layers_host[l].shared));
+    if (cfg->n_shared) TRY(need(layers_host[l].shared));
+    else TRY(optional_ptr(layers_host[l].shared));
   }
   TRY(need(x0_dev));
   TRY(need(x_all_dev));
@@ -523,47 +517,31 @@ MOE_API moe_status moe_stack_decode(const moe_config* cfg, int32_t L, const moe_
   if (ws_bytes < sp.total) return MOE_EWORKSPACE;
   if (overlaps(ws_dev, sp.total, out_all_dev, (size_t)L * H * 4) || overlaps(ws_dev, sp.total, x_all_dev, (size_t)L * H * 2))
     return MOE_EINVAL;
-  if (!qmoe::stack_grid_coresident(cfg->ffn, cfg->top_k, cfg->hidden, cfg->n_shared)) return MOE_EUNSUPPORTED;
+  if (!qmoe::decode_grid_coresident(cfg->ffn, cfg->top_k, cfg->hidden, cfg->n_shared)) return MOE_EUNSUPPORTED;
 
-  qmoe::StackArgs s;
-  s.a.x = static_cast<const uint16_t*>(x0_dev);
-  s.a.wg = nullptr;
-  s.a.bias = nullptr;
-  s.a.arena = nullptr;
-  s.a.shared = nullptr;
-  s.a.expert_bytes = expert_bytes(cfg);
-  s.a.H = cfg->hidden;
-  s.a.F = cfg->ffn;
-  s.a.E = cfg->n_experts;
-  s.a.K = cfg->top_k;
-  s.a.n_shared = cfg->n_shared;
-  s.a.gated = cfg->shared_gate;
-  s.a.scale = cfg->routed_scale;
-  s.a.scores = nullptr;
-  s.a.ids = nullptr;
-  s.a.w = nullptr;
-  s.a.hw = nullptr;
-  s.a.out = nullptr;
-  s.a.err = at<uint32_t>(ws_dev, sp.status);
-  s.a.x_prev = nullptr;
-  s.a.out_prev = nullptr;
-  s.a.eps = eps;
-  s.L = L;
-  s.x0 = static_cast<const uint16_t*>(x0_dev);
-  s.x_all = static_cast<uint16_t*>(x_all_dev);
-  s.out_all = out_all_dev;
-  s.ids_all = ids_all_dev ? ids_all_dev : at<int32_t>(ws_dev, sp.ids);
-  s.w_all = w_all_dev ? w_all_dev : at<float>(ws_dev, sp.w);
-  s.scores_all = at<float>(ws_dev, sp.scores);
-  s.hw_all = at<uint32_t>(ws_dev, sp.hw);
-  qmoe::StackLayer layers[qmoe::kMaxStackLayers];
+  // Per layer the decode plan's two launches, the layer's input formed in the
+  // first (as moe_layer_forward_chained); layer 0 reads x0, copies it to row 0
+  // of x_all and clears the give-up word.
+  int32_t* ids_all = ids_all_dev ? ids_all_dev : at<int32_t>(ws_dev, sp.ids);
+  float* w_all = w_all_dev ? w_all_dev : at<float>(ws_dev, sp.w);
+  uint16_t* x_all = static_cast<uint16_t*>(x_all_dev);
+  const int WK = weight_cols(cfg);
   for (int l = 0; l < L; l++) {
-    layers[l].wg = layers_host[l].gate_w;
-    layers[l].bias = layers_host[l].sel_bias;
-    layers[l].arena = static_cast<const uint8_t*>(layers_host[l].arena);
-    layers[l].shared = static_cast<const uint8_t*>(layers_host[l].shared);
+    const moe_stack_layer& ly = layers_host[l];
+    qmoe::DecodeArgs a = decode_args(cfg, l == 0 ? x0_dev : x_all + (size_t)l * H, ly.gate_w, ly.sel_bias, ly.arena,
+                                     ly.shared, out_all_dev + (size_t)l * H, ids_all + (size_t)l * cfg->top_k,
+                                     w_all + (size_t)l * WK, ws_dev, sp.dec);
+    if (l == 0) {
+      a.x_copy = x_all;
+      a.zero_err = 1;
+    } else {
+      a.x_prev = x_all + (size_t)(l - 1) * H;
+      a.out_prev = out_all_dev + (size_t)(l - 1) * H;
+      a.eps = eps;
+    }
+    TRY(launched(qmoe::launch_layer_decode(a, stream)));
   }
-  return launched(qmoe::launch_stack_decode(s, layers, stream));
+  return MOE_OK;
 }
 
 MOE_API moe_status moe_stack_status(const moe_config* cfg, int32_t L, const void* ws_dev, size_t ws_bytes,
@@ -573,7 +551,7 @@ MOE_API moe_status moe_stack_status(const moe_config* cfg, int32_t L, const void
   TRY(need(status_dev));
   const StackPlan sp = make_stack_plan(cfg, L);
   if (ws_bytes < sp.total) return MOE_EWORKSPACE;
-  return launched(qmoe::launch_copy_words(at<const uint32_t>(const_cast<void*>(ws_dev), sp.status),
+  return launched(qmoe::launch_copy_words(at<const uint32_t>(const_cast<void*>(ws_dev), sp.dec.status),
                                           reinterpret_cast<uint32_t*>(status_dev), 1, stream));
 }
 

@@ -101,6 +101,10 @@ struct DecodeArgs {
   const float* out_prev;
   float eps;
   int n_router, n_shared_wg, n_routed_wg, n_down_wg;  // grid partition (set by the launcher)
+  // stack steps: the first layer's scores kernel also copies x to x_copy
+  // (when non-null) and clears the give-up word (when zero_err)
+  uint16_t* x_copy = nullptr;
+  int zero_err = 0;
 };
 
 // Words of the decode hand-off buffer: h of K + 1 slots, the shared expert's down rows.
@@ -108,40 +112,8 @@ __host__ __device__ inline int hw_words(int K, int F, int H) { return (K + 1) * 
 
 hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream);
 
-// The decode step of a stack of layers (layer_decode.hip): a reset of the
-// hand-off words, then one launch per layer with the router folded in.
-// Shapes: those of the decode plan with n_shared = 1 and E + gated <= F / 16
-// (router row r is made by shared workgroup r).
+// Layers one moe_stack_decode call takes (two decode launches per layer).
 constexpr int kMaxStackLayers = 64;
-// Each layer's scores are written in kScoreReplicas copies kScoreRepStride
-// floats apart (4 KiB + 256 B, so the copies fall in different memory
-// channels): the workgroups that wait for them read copy blockIdx % 16, which
-// spreads the re-reads of several hundred waiting wavefronts over 16 places.
-constexpr int kScoreReplicas = 16;
-constexpr int kScoreRepStride = 1088;
-struct StackLayer {
-  const float* wg;      // [E + gated][H]
-  const float* bias;    // [E] or null
-  const uint8_t* arena;
-  const uint8_t* shared;
-};
-struct StackArgs {
-  DecodeArgs a;         // shape and the give-up word; the per-layer fields are set per layer
-  int L;
-  const uint16_t* x0;   // [H] layer 0's input
-  uint16_t* x_all;      // [L][H] every layer's input
-  float* out_all;       // [L][H] every layer's output
-  int32_t* ids_all;     // [L][K]
-  float* w_all;         // [L][K + gated]
-  float* scores_all;    // [L][E + gated]
-  uint32_t* hw_all;     // [L][(K + 1) F] (the stack keeps the shared expert in its down workgroups)
-};
-
-hipError_t launch_stack_decode(StackArgs s, const StackLayer* layers, hipStream_t stream);
-
-// Whether the stack step's per-layer grid (that of k_decode_experts) fits on
-// the current device at once.
-bool stack_grid_coresident(int F, int K, int H, int n_shared);
 
 hipError_t launch_zero_words(uint32_t* p, int64_t n, hipStream_t stream);
 

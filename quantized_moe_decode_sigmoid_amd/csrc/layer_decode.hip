@@ -7,23 +7,27 @@
 //
 //   k_decode_scores   one wavefront (workgroup) per router row: fp32 logit and
 //                     sigmoid score (row E: the shared expert's gate, when
-//                     the shared expert is sigmoid-gated).
+//                     the shared expert is sigmoid-gated); the chained form
+//                     (k_decode_scores_chained, 256 threads per row) first
+//                     forms the layer's input from the previous layer's.
 //                     It also writes the "not ready" pattern into the words
-//                     through which the next kernel hands h from its gate/up
-//                     workgroups to its down workgroups; the previous token's
-//                     second kernel has finished, so nobody reads them now.
+//                     through which the next kernel hands data between its
+//                     workgroups; the previous token's second kernel has
+//                     finished, so nobody reads them now.
 //   k_decode_experts  roles by block index:
-//     [shared]  gate/up + SiLU*up of the shared expert, one 16-row tile of F;
 //     [routed]  gate/up + SiLU*up of routed slot k, one 16-row tile of F;
-//     [down]    32 rows of H: down projection of every slot and of the shared
-//               expert, then the slot-order combine of those rows.
-//   Every workgroup that needs the routing ranks the E scores itself (top-K
-//   in LDS), so there is no hand-off for it.  The down workgroups request
-//   their weight tiles as soon as they know the experts, then read the h
-//   words of the gate/up workgroups, repeating a read while it still shows
-//   the "not ready" pattern (a finite h never has it).  Each h word is written
-//   once with one device-scope store, so a word that is not "not ready" is
-//   complete: no counter, atomic or fence is involved.
+//     [shared]  gate/up + SiLU*up of the shared expert, one 16-row tile of F,
+//               then (the shared expert's h complete) its down rows of up to
+//               4 row tiles of H;
+//     [down]    32 rows of H: down projection of the routed slots, then the
+//               slot-order combine of those rows with the shared expert's.
+//   Every workgroup that needs the routing ranks the E scores itself, so
+//   there is no hand-off for it.  The down workgroups request their weight
+//   tiles as soon as they know the experts, then read the h words of the
+//   gate/up workgroups, repeating a read while it still shows the "not ready"
+//   pattern (a finite value never has it).  Each word is written once with
+//   one device-scope store, so a word that is not "not ready" is complete: no
+//   counter, atomic or fence is involved.
 //
 // Every global load of a role is issued before its result is first used and
 // none sits behind a runtime branch (indices are clamped, unused values
@@ -109,8 +113,6 @@ struct GateUpLds {
   uint16_t x[kMaxDecodeHidden];                                                // the token's activations
   uint32_t scales[kGuMaxRowTiles][2][kMaxDecodeHidden / 128][kScaleWords];  // [row tile][gate/up][kg]
   f32x4 red[kGuMaxRowTiles][kDecWaves][4];                                  // column 0 of each wave's acc
-  float rrow[kMaxDecodeHidden];  // the stack kernel: a router row of this layer
-  float nred[4];                 // the stack kernel: the norm's wavefront sums
 };
 
 struct DownLds {
@@ -135,64 +137,6 @@ static_assert(offsetof(ExpertsLds, tbl) <= 65536, "LDS DMA destinations in the f
 
 // ---------------------------------------------------------------- kernel 1: scores
 
-// The layer's input formed from the previous layer's input and output,
-// x = bf16(h * r), h = fp32(x_prev) + out_prev, r = 1 / sqrt(mean(h^2) + eps),
-// with exactly the operations and order of k_residual_rmsnorm (chain.hip):
-// there, thread v of 256 sums h_i^2 over i = v, v + 256, ... with fused
-// multiply-adds, each wavefront's 64 sums meet in an xor butterfly and the 4
-// wavefront sums are added in order; here lane j plays threads j, j + 64,
-// j + 128, j + 192.  The lane loads its router elements 256m + 4j + c (vector
-// loads, all issued at once), passes h through LDS to the lanes that sum it,
-// and gets its router elements of x back in xv.
-template <int MMAX>
-__device__ __forceinline__ void chained_input(const DecodeArgs& a, int lane, float* hbuf, uint2 (&xv)[MMAX]) {
-  const int H = a.H, M = H >> 8;
-  uint2 xp[MMAX];
-  float4 op[MMAX];
-#pragma unroll
-  for (int m = 0; m < MMAX; m++) {
-    const int i0 = 256 * (m < M ? m : M - 1) + 4 * lane;
-    xp[m] = *reinterpret_cast<const uint2*>(a.x_prev + i0);
-    op[m] = *reinterpret_cast<const float4*>(a.out_prev + i0);
-  }
-  float4 h[MMAX];
-#pragma unroll
-  for (int m = 0; m < MMAX; m++) {
-    h[m].x = bf16_bits_to_f32(xp[m].x & 0xffffu) + op[m].x;
-    h[m].y = bf16_bits_to_f32(xp[m].x >> 16) + op[m].y;
-    h[m].z = bf16_bits_to_f32(xp[m].y & 0xffffu) + op[m].z;
-    h[m].w = bf16_bits_to_f32(xp[m].y >> 16) + op[m].w;
-    if (m < M) *reinterpret_cast<float4*>(hbuf + 256 * m + 4 * lane) = h[m];
-  }
-  __syncthreads();
-  float part[4];
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    float ss = 0.0f;
-#pragma unroll
-    for (int n = 0; n < MMAX; n++) {
-      if (n < M) {
-        const float hv = hbuf[lane + 64 * q + 256 * n];
-        ss = __builtin_fmaf(hv, hv, ss);
-      }
-    }
-    ss = wave_xor_sum(ss);
-    part[q] = ss;
-  }
-  float tot = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; q++) tot += part[q];
-  const float r = 1.0f / __builtin_sqrtf(tot / (float)H + a.eps);
-#pragma unroll
-  for (int m = 0; m < MMAX; m++) {
-    const uint32_t y0 = f32_to_bf16_rne(h[m].x * r);
-    const uint32_t y1 = f32_to_bf16_rne(h[m].y * r);
-    const uint32_t y2 = f32_to_bf16_rne(h[m].z * r);
-    const uint32_t y3 = f32_to_bf16_rne(h[m].w * r);
-    xv[m] = make_uint2(y0 | (y1 << 16), y2 | (y3 << 16));
-  }
-}
-
 template <int MMAX>
 __global__ __launch_bounds__(64) void k_decode_scores(DecodeArgs a) {
   const int lane = threadIdx.x;
@@ -200,24 +144,70 @@ __global__ __launch_bounds__(64) void k_decode_scores(DecodeArgs a) {
   // reset the h hand-off words of k_decode_experts
   const int n_words = hw_words(a.K, a.F, a.H);
   for (int i = blockIdx.x * 64 + threadIdx.x; i < n_words; i += gridDim.x * 64) a.hw[i] = kNotReady;
+  if (e == 0) {
+    if (a.zero_err && lane == 0) a.err[0] = 0u;
+    if (a.x_copy)
+      for (int i = lane; i < (a.H >> 3); i += 64)
+        *reinterpret_cast<uint4*>(a.x_copy + 8 * i) = *reinterpret_cast<const uint4*>(a.x + 8 * i);
+  }
   if (e < a.E + a.gated) {  // row E: the shared expert's gate
     float4 w[MMAX];
     load_router_row<MMAX>(a.wg + (size_t)e * a.H, a.H, lane, w);
-    float p;
-    if (a.x_prev) {
-      __shared__ float hbuf[256 * MMAX];
-      uint2 xv[MMAX];
-      chained_input<MMAX>(a, lane, hbuf, xv);
-      if (e == 0) {  // the layer's input, for the second kernel and the caller
-        uint16_t* xo = const_cast<uint16_t*>(a.x);
+    const float p = router_logit<MMAX>(a.x, a.H, lane, w);
+    if (lane == 0) a.scores[e] = sigmoid_fixed(p);
+  }
+}
+
+// The chained form (x_prev non-null): 256 threads per router row.  The
+// layer's input x = bf16(h * r), h = fp32(x_prev) + out_prev,
+// r = 1 / sqrt(mean(h^2) + eps), with exactly the operations and order of
+// k_residual_rmsnorm (chain.hip): thread v sums h_i^2 over i = v, v + 256, ...
+// with fused multiply-adds, each wavefront's 64 sums meet in an xor butterfly,
+// the 4 wavefront sums are added in order; every thread forms x of its
+// elements into LDS (workgroup 0 also writes x for the experts kernel and the
+// caller), then wavefront 0 makes the logit from LDS and its router row in
+// registers, in router_logit's order.
+template <int MMAX>
+__global__ __launch_bounds__(256) void k_decode_scores_chained(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[256 * MMAX];
+  __shared__ float nred[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e = blockIdx.x;
+  const int H = a.H, M = H >> 8;
+  const int n_words = hw_words(a.K, a.F, a.H);
+  for (int i = blockIdx.x * 256 + tid; i < n_words; i += gridDim.x * 256) a.hw[i] = kNotReady;
+  if (e >= a.E + a.gated) return;  // (uniform over the workgroup)
+  float4 w[MMAX];
+  if (wave == 0) load_router_row<MMAX>(a.wg + (size_t)e * H, H, lane, w);
+  float h[MMAX];
 #pragma unroll
-        for (int m = 0; m < MMAX; m++)
-          if (m < (a.H >> 8)) *reinterpret_cast<uint2*>(xo + 256 * m + 4 * lane) = xv[m];
-      }
-      p = router_logit_vals<MMAX>(xv, a.H, w);
-    } else {
-      p = router_logit<MMAX>(a.x, a.H, lane, w);
+  for (int n = 0; n < MMAX; n++) {
+    const int i = tid + 256 * (n < M ? n : M - 1);
+    h[n] = bf16_bits_to_f32(a.x_prev[i]) + a.out_prev[i];
+  }
+  float ss = 0.0f;
+#pragma unroll
+  for (int n = 0; n < MMAX; n++)
+    if (n < M) ss = __builtin_fmaf(h[n], h[n], ss);
+  ss = wave_xor_sum(ss);
+  if (lane == 0) nred[wave] = ss;
+  __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; q++) tot += nred[q];
+  const float r = 1.0f / __builtin_sqrtf(tot / (float)H + a.eps);
+  uint16_t* xo = const_cast<uint16_t*>(a.x);
+#pragma unroll
+  for (int n = 0; n < MMAX; n++) {
+    if (n < M) {
+      const uint16_t y = (uint16_t)f32_to_bf16_rne(h[n] * r);
+      xs[tid + 256 * n] = y;
+      if (e == 0) xo[tid + 256 * n] = y;  // the layer's input, for the second kernel and the caller
     }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float p = router_logit<MMAX>(xs, H, lane, w);
     if (lane == 0) a.scores[e] = sigmoid_fixed(p);
   }
 }
@@ -240,35 +230,6 @@ __device__ __forceinline__ RouteIn route_fetch(const DecodeArgs& a) {
   RouteIn v;
   v.s = a.scores[e];
   v.b = a.bias ? a.bias[e] : 0.0f;
-  return v;
-}
-
-// The stack kernel's version: the scores are written by other workgroups of
-// the same launch (device-scope stores, one per copy), so each is re-read
-// from this workgroup's copy until it no longer shows the "not ready" pattern
-// (a score is never NaN).
-__device__ __forceinline__ uint32_t poll_score(const DecodeArgs& a, int e) {
-  const __amdgpu_buffer_rsrc_t rs = buffer_of(a.scores + (blockIdx.x % kScoreReplicas) * kScoreRepStride);
-  uint32_t v = ld_dev(rs, 4 * e);
-  uint32_t it = 0;
-  while (v == kNotReady) {
-    if (give_up(a.err, ++it)) {
-      st_dev(buffer_of(a.err), 0, 1u);
-      break;
-    }
-    __builtin_amdgcn_s_sleep(1);
-    v = ld_dev(rs, 4 * e);
-  }
-  return v;
-}
-
-__device__ __forceinline__ RouteIn route_poll(const DecodeArgs& a) {
-  RouteIn v = {0.0f, 0.0f};
-  const int e = threadIdx.x;
-  if (e < a.E) {
-    v.b = a.bias ? a.bias[e] : 0.0f;
-    v.s = __uint_as_float(poll_score(a, e));
-  }
   return v;
 }
 
@@ -313,8 +274,7 @@ __device__ void route_rank_lds(const DecodeArgs& a, RouteLds& r, RouteIn v) {
 
 // route_rank_wave: wavefront 0 takes the K in K rounds of topk_take, from
 // registers when E <= 64, else through LDS, one barrier (≈0.9 µs at E = 64):
-// the routed gate/up workgroups' form, and every workgroup's in the stack
-// kernel, where the ranking follows the wait for the scores.
+// the routed gate/up workgroups' form.
 __device__ void route_rank_wave(const DecodeArgs& a, RouteLds& r, RouteIn v) {
 #pragma clang fp contract(off)
   const int e = threadIdx.x;
@@ -692,12 +652,9 @@ __device__ void shared_down_part(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   }
 }
 
-// PERSIST (the stack kernel): the scores come from other workgroups of the
-// same launch (waited for, bounded), and the shared expert is one more slot
-// of these workgroups.  Otherwise (the decode kernel) the shared expert's down
-// rows come finished from the shared workgroups (shared_down_part) and are
-// waited for in the combine.
-template <bool PERSIST>
+// Down of 32 rows of H over the routed slots, then the slot-order combine
+// with the shared expert's rows, which come finished from the shared
+// workgroups (shared_down_part) and are waited for.
 __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   DownLds& d = sh.u.d;
   RouteLds& r = sh.route;
@@ -708,73 +665,46 @@ __device__ void down_role(const DecodeArgs& a, int blk, ExpertsLds& sh) {
   const bool has_tile = kg < nkg;
   const int kgc = has_tile ? kg : nkg - 1;
   const int64_t mat_bytes = a.expert_bytes / 3;
-  constexpr bool kSharedSlot = PERSIST;
 
   auto down_tiles = [&](const uint8_t* ex, int rtile) {
     return ex + 2 * mat_bytes + (int64_t)rtile * nkg * kTileBytes;
   };
   u32x4 nib[kDnSlots];
-  // 1. the router scores (and the shared expert's gate); in the stack, the
-  //    shared expert's tiles (they need no routing)
-  RouteIn rin;
-  float gate = 1.0f;
-  if constexpr (!PERSIST) {
-    rin = route_fetch(a);
-    gate = a.gated ? a.scores[a.E] : 1.0f;
-  }
-  if constexpr (kSharedSlot) {
-    const uint8_t* shx = a.n_shared ? a.shared : a.arena;
-    nib[kMaxDecodeK] = ld16(down_tiles(shx, rt) + (int64_t)kgc * kTileBytes + 16 * lane);
-    if (wave < 2) dma_slot_scales(d, down_tiles(shx, 2 * blk), nkg, kMaxDecodeK, wave);
-  }
+  // 1. the router scores (and the shared expert's gate), routing, then the
+  //    routed experts' tiles
+  const RouteIn rin = route_fetch(a);
+  const float gate = a.gated ? a.scores[a.E] : 1.0f;
   build_pair_table(sh.tbl);
-  if constexpr (PERSIST) {
-    rin = route_poll(a);
-    if (a.gated) gate = __uint_as_float(poll_score(a, a.E));
-  }
-  // 2. routing, then the routed experts' tiles
-  if constexpr (PERSIST) route_rank_wave(a, r, rin);
-  else route_rank_lds(a, r, rin);
+  route_rank_lds(a, r, rin);
   load_routed_slots<0>(a, r, nib, rt, kgc, nkg);
   if (wave >= 2 && wave < 2 + 2 * a.K) {
     const int slot = (wave - 2) >> 1;
     dma_slot_scales(d, down_tiles(a.arena + (int64_t)r.ids[slot] * a.expert_bytes, 2 * blk), nkg, slot, wave & 1);
   }
-  // 3. in the stack, h of the shared expert (made first) and its MFMAs, while
-  //    the routed experts' h is still being made
+  // 2. h of the routed slots and their MFMAs
   static_assert(kMaxDecodeK * (kMaxDecodeFfn / 4) <= kDecThreads, "one h piece per thread");
-  if constexpr (kSharedSlot) {
-    if (a.n_shared) {
-      poll_h_rows(a, d, a.K, 1);
-      wait_loads();  // this wave's tiles and scale pieces (LDS DMA)
-      __syncthreads();
-      if (has_tile) down_slot<kMaxDecodeK>(sh, nib, rtl, kg);
-    }
-  }
-  // 4. h of the routed slots and their MFMAs
   poll_h_rows(a, d, 0, a.K);
   wait_loads();
   __syncthreads();
   if (has_tile) down_routed_slots<0>(a, sh, nib, rtl, kg);
   __syncthreads();
-  // 5. the wave parts of each (row tile, slot) added in order
-  for (int i = threadIdx.x; i < kDnSlots * 32; i += kDecThreads) {
+  // 3. the wave parts of each (row tile, slot) added in order
+  for (int i = threadIdx.x; i < kMaxDecodeK * 32; i += kDecThreads) {
     const int s2 = i >> 5, row = i & 31, rt2 = row >> 4, r16 = row & 15;
-    if (s2 < a.K || (kSharedSlot && s2 == kMaxDecodeK && a.n_shared)) {
+    if (s2 < a.K) {
       float t = 0.0f;
       for (int q = 0; q < nkg; q++) t += d.part[rt2 + 2 * q][s2][r16];
       d.y[s2][row] = t;
     }
   }
   __syncthreads();
-  // 6. slot-order combine of these 32 rows, the shared expert's row last
+  // 4. slot-order combine of these 32 rows, the shared expert's row last
   if (threadIdx.x < 32) {
     const int row = threadIdx.x;
     float acc = 0.0f;
     for (int k = 0; k < a.K; k++) acc = __builtin_fmaf(r.w[k], d.y[k][row], acc);
     if (a.n_shared) {
-      const float ys = kSharedSlot ? d.y[kMaxDecodeK][row]
-                                   : __uint_as_float(poll_word(a, shared_y(a), 32 * blk + row));
+      const float ys = __uint_as_float(poll_word(a, shared_y(a), 32 * blk + row));
       acc = a.gated ? __builtin_fmaf(gate, ys, acc) : acc + ys;
     }
     a.out[32 * blk + row] = acc;
@@ -809,184 +739,8 @@ __global__ __launch_bounds__(kDecThreads, 8) void k_decode_experts(DecodeArgs a)
     __syncthreads();  // the gate/up LDS is reused
     shared_down_part(a, blk, sh);
   } else {
-    down_role<false>(a, blk - a.n_shared_wg, sh);
+    down_role(a, blk - a.n_shared_wg, sh);
   }
-}
-
-// ---------------------------------------------------------------- the stack step
-
-// One decode token through L layers in L + 1 launches: k_stack_reset, then
-// one k_stack_layer per layer, each the grid of k_decode_experts with the
-// router folded in (no separate router launch per layer):
-//   [routed]  the layer's input formed from the previous layer's input and
-//             output, then the scores (waited for), ranking (route_rank_wave),
-//             the gate/up tiles of its slot and row tile, gate/up;
-//   [shared]  router row blk (row E: the shared expert's gate) and the
-//             previous layer's input and output requested first, the layer's
-//             input, the logit and score (device-scope stores, one per score
-//             copy), then the shared expert's gate/up;
-//   [down]    as in k_decode_experts, with the scores waited for.
-// Every hand-off word of every layer (scores, h) is "not ready" when the step
-// starts (k_stack_reset) and written once.  The down workgroups wait for the
-// scores and for h, the routed ones for the scores: the launcher checks that
-// the grid is resident at once (as for k_decode_experts).  Every wait is
-// bounded; after one gives up the others give up within 64 re-reads.
-
-// The layer's input from the previous layer's input xs (bf16, in LDS,
-// replaced in place) and output (written by the previous launch, so plain
-// loads see it): the operations and order of k_residual_rmsnorm -- threads
-// v < 256 play its threads (elements v, v + 256, ...), each wavefront's sums
-// meet in an xor butterfly, the 4 wavefront sums are added in order.  The
-// loads are issued first (stack_input_load) so that they overlap the
-// workgroup's LDS DMA.
-constexpr int kInPer = kMaxDecodeHidden / 256;
-static_assert(kMaxDecodeFfn / 16 <= kScoreRepStride, "a layer's router rows fit in one score copy");
-
-__device__ __forceinline__ void stack_input_load(const DecodeArgs& a, const float* out_prev, float (&o)[kInPer]) {
-  const int v = threadIdx.x, n = a.H >> 8;
-#pragma unroll
-  for (int i = 0; i < kInPer; i++) o[i] = (v < 256 && i < n) ? out_prev[v + 256 * i] : 0.0f;
-}
-
-__device__ void stack_input(const DecodeArgs& a, const float (&o)[kInPer], uint16_t* xs, float* nred) {
-  const int v = threadIdx.x, n = a.H >> 8;
-  if (v < 256) {
-    float ss = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kInPer; i++) {
-      if (i < n) {
-        const float h = bf16_bits_to_f32(xs[v + 256 * i]) + o[i];
-        ss = __builtin_fmaf(h, h, ss);
-      }
-    }
-    ss = wave_xor_sum(ss);
-    if ((v & 63) == 0) nred[v >> 6] = ss;
-  }
-  __syncthreads();
-  if (v < 256) {
-    float tot = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; w++) tot += nred[w];
-    const float r = 1.0f / __builtin_sqrtf(tot / (float)a.H + a.eps);
-#pragma unroll
-    for (int i = 0; i < kInPer; i++) {
-      if (i < n) {
-        const float h = bf16_bits_to_f32(xs[v + 256 * i]) + o[i];
-        xs[v + 256 * i] = (uint16_t)f32_to_bf16_rne(h * r);
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// router_logit_vals' fixed order with the activations and the router row
-// read from LDS one 256-element step at a time.
-__device__ __forceinline__ float router_logit_lds(const uint16_t* xs, const float* wrow, int H, int lane) {
-#pragma clang fp contract(off)
-  const int M = H >> 8;
-  float p = 0.0f;
-  for (int m = 0; m < M; m++) {
-    const uint2 xv = *reinterpret_cast<const uint2*>(xs + 256 * m + 4 * lane);
-    const float4 w = *reinterpret_cast<const float4*>(wrow + 256 * m + 4 * lane);
-    p = __builtin_fmaf(bf16_bits_to_f32(xv.x & 0xffffu), w.x, p);
-    p = __builtin_fmaf(bf16_bits_to_f32(xv.x >> 16), w.y, p);
-    p = __builtin_fmaf(bf16_bits_to_f32(xv.y & 0xffffu), w.z, p);
-    p = __builtin_fmaf(bf16_bits_to_f32(xv.y >> 16), w.w, p);
-  }
-  return wave_xor_sum(p);
-}
-
-// The previous layer's input (layer 0: the step's input) into LDS by DMA,
-// 16 bytes per lane, pieces past the row repeating a valid one.
-__device__ __forceinline__ void dma_x(const uint16_t* x, int H, uint16_t* xs) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave < 8) {
-    const int p = 64 * wave + lane;
-    dma16(x + 8 * min(p, (H >> 3) - 1), xs + 512 * wave);
-  }
-}
-
-__device__ void stack_shared_layer(const DecodeArgs& a, int l, int blk, ExpertsLds& sh, const float* out_prev,
-                                   uint16_t* x_out) {
-  GateUpLds& g = sh.u.g;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const bool has_row = blk < a.E + a.gated;
-  // 1. the score first (the routed workgroups wait for it): the router row
-  //    and the previous layer's input by LDS DMA, the layer's input, the
-  //    logit and score
-  if (has_row && wave < (a.H >> 8))
-    dma16_stream(a.wg + (size_t)blk * a.H + 256 * wave + 4 * lane, &g.rrow[256 * wave]);
-  dma_x(a.x, a.H, g.x);
-  float o[kInPer];
-  if (l > 0) stack_input_load(a, out_prev, o);
-  build_pair_table(sh.tbl);
-  wait_loads();
-  __syncthreads();
-  if (l > 0) stack_input(a, o, g.x, g.nred);
-  if (has_row && wave == 0) {
-    const float p = router_logit_lds(g.x, g.rrow, a.H, lane);
-    if (lane < kScoreReplicas)
-      st_dev(buffer_of(a.scores), 4 * (kScoreRepStride * lane + blk), __float_as_uint(sigmoid_fixed(p)));
-  }
-  if (blk == 0 && (int)threadIdx.x < (a.H >> 3))
-    *reinterpret_cast<uint4*>(x_out + 8 * threadIdx.x) = *reinterpret_cast<const uint4*>(&g.x[8 * threadIdx.x]);
-  // 2. gate/up of the shared expert
-  gate_up_dma<1>(a, a.shared, blk, sh, false);
-  u32x4 nib[1][kGuMaxKg];
-  gate_up_words<1>(a, a.shared, blk, nib);
-  wait_dma_before<kGuMaxKg>();
-  __syncthreads();
-  gate_up_compute<1>(a, a.K, blk, sh, nib);
-}
-
-__device__ void stack_routed_layer(const DecodeArgs& a, int l, int blk, ExpertsLds& sh, const float* out_prev) {
-  GateUpLds& g = sh.u.g;
-  const int n_rt_f = a.F >> 4;
-  const int slot = blk / n_rt_f, rt = blk % n_rt_f;
-  // the layer's input first: it is ready before the scores can be
-  dma_x(a.x, a.H, g.x);
-  float o[kInPer];
-  if (l > 0) stack_input_load(a, out_prev, o);
-  build_pair_table(sh.tbl);
-  wait_loads();
-  __syncthreads();
-  if (l > 0) stack_input(a, o, g.x, g.nred);
-  route_rank_wave(a, sh.route, route_poll(a));
-  const uint8_t* ex = a.arena + (int64_t)sh.route.ids[slot] * a.expert_bytes;
-  gate_up_dma<1>(a, ex, rt, sh, false);
-  u32x4 nib[1][kGuMaxKg];
-  gate_up_words<1>(a, ex, rt, nib);
-  wait_dma_before<kGuMaxKg>();
-  __syncthreads();
-  gate_up_compute<1>(a, slot, rt, sh, nib);
-}
-
-// One layer of the step.  x: the previous layer's input (layer 0: the
-// step's input); out_prev: the previous layer's output (layer 0: null).
-__global__ __launch_bounds__(kDecThreads, 8) void k_stack_layer(DecodeArgs a, int l, const float* out_prev,
-                                                                  uint16_t* x_out) {
-  __shared__ ExpertsLds sh;
-  const int blk = blockIdx.x;
-  if (blk < a.n_routed_wg) stack_routed_layer(a, l, blk, sh, out_prev);
-  else if (blk < a.n_routed_wg + a.n_shared_wg) stack_shared_layer(a, l, blk - a.n_routed_wg, sh, out_prev, x_out);
-  else down_role<true>(a, blk - a.n_routed_wg - a.n_shared_wg, sh);
-}
-
-// Every hand-off word of the step to "not ready" -- the n_router scores of
-// each of the kScoreReplicas copies of each of the L layers, and the h
-// words of every layer -- and the give-up word to 0.
-__global__ void k_stack_reset(float* scores_all, int L, int n_router, uint32_t* hw_all, int64_t n_hw, uint32_t* err) {
-  const int64_t n_scores = (int64_t)L * kScoreReplicas * n_router;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_scores + n_hw; i += stride) {
-    if (i < n_scores) {
-      const int64_t copy = i / n_router, e = i % n_router;  // copy = layer * kScoreReplicas + c
-      reinterpret_cast<uint32_t*>(scores_all)[copy * kScoreRepStride + e] = kNotReady;
-    } else {
-      hw_all[i - n_scores] = kNotReady;
-    }
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) err[0] = 0u;
 }
 
 namespace {
@@ -1026,70 +780,16 @@ hipError_t launch_layer_decode(DecodeArgs a, hipStream_t stream) {
   a.n_routed_wg = a.K * (a.F / 16);
   a.n_down_wg = a.H / 32;
   clear_last_error();
-  hipLaunchKernelGGL(k_decode_scores<kMaxDecodeHidden / 256>, dim3(a.n_router), dim3(64), 0, stream, a);
+  if (a.x_prev)
+    hipLaunchKernelGGL(k_decode_scores_chained<kMaxDecodeHidden / 256>, dim3(a.n_router), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(k_decode_scores<kMaxDecodeHidden / 256>, dim3(a.n_router), dim3(64), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   clear_last_error();
   hipLaunchKernelGGL(k_decode_experts, dim3(a.n_shared_wg + a.n_routed_wg + a.n_down_wg), dim3(kDecThreads), 0,
                      stream, a);
   return hipGetLastError();
-}
-
-static std::atomic<int> g_stack_capacity[64];
-
-bool stack_grid_coresident(int F, int K, int H, int n_shared) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    clear_last_error();
-    return false;
-  }
-  int cap = g_stack_capacity[dev].load(std::memory_order_relaxed);
-  if (cap == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_stack_layer),
-                                                     kDecThreads, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
-      clear_last_error();
-      return false;
-    }
-    cap = per_cu * cus > 0 ? per_cu * cus : -1;
-    g_stack_capacity[dev].store(cap, std::memory_order_relaxed);
-  }
-  return cap > 0 && decode_grid_size(F, K, H, n_shared) <= cap;
-}
-
-hipError_t launch_stack_decode(StackArgs s, const StackLayer* layers, hipStream_t stream) {
-  DecodeArgs b = s.a;
-  b.n_router = b.E + b.gated;
-  b.n_shared_wg = b.F / 16;
-  b.n_routed_wg = b.K * (b.F / 16);
-  b.n_down_wg = b.H / 32;
-  const int64_t n_hw = (int64_t)s.L * (b.K + 1) * b.F;
-  clear_last_error();
-  hipLaunchKernelGGL(k_stack_reset, dim3(256), dim3(256), 0, stream, s.scores_all, s.L, b.n_router, s.hw_all, n_hw,
-                     b.err);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  const size_t H = b.H;
-  for (int l = 0; l < s.L; l++) {
-    DecodeArgs a = b;
-    a.x = l == 0 ? s.x0 : s.x_all + (l - 1) * H;
-    a.wg = layers[l].wg;
-    a.bias = layers[l].bias;
-    a.arena = layers[l].arena;
-    a.shared = layers[l].shared;
-    a.scores = s.scores_all + (size_t)l * kScoreReplicas * kScoreRepStride;
-    a.hw = s.hw_all + (size_t)l * (b.K + 1) * b.F;
-    a.out = s.out_all + l * H;
-    a.ids = s.ids_all + (size_t)l * b.K;
-    a.w = s.w_all + (size_t)l * (b.K + b.gated);
-    clear_last_error();
-    hipLaunchKernelGGL(k_stack_layer, dim3(b.n_shared_wg + b.n_routed_wg + b.n_down_wg), dim3(kDecThreads), 0, stream,
-                       a, l, l > 0 ? s.out_all + (l - 1) * H : nullptr, s.x_all + l * H);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
-  return hipSuccess;
 }
 
 __global__ void k_fill_u32(uint32_t* p, int64_t n) {

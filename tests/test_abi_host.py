@@ -81,14 +81,15 @@ def test_stack_decode_argument_errors():
     any launch)."""
     cfg = qm.make_config(**XING4)
     n1, n38 = qm.moe_stack_workspace_bytes(cfg, 1), qm.moe_stack_workspace_bytes(cfg, 38)
-    assert 0 < n1 < n38
-    # scores + h words per layer are the bulk: 38 layers x (64 + 5 x 1024) words
-    assert n38 >= 38 * (64 + 5 * 1024) * 4
-    for bad, code in [(dict(), None), (dict(n_shared=0), qm.MOE_EUNSUPPORTED), (dict(ffn=512), qm.MOE_EUNSUPPORTED),
+    # one token's decode workspace, reused by every layer, plus every layer's routing outputs
+    assert qm.moe_workspace_bytes(cfg, 1) <= n1 < n38 <= n1 + 2 * 38 * 8 * 4 + 512
+    for bad, code in [(dict(), None), (dict(n_shared=0), None), (dict(shared_gate=1), None),
+                      (dict(ffn=512), qm.MOE_EUNSUPPORTED),  # hidden > 4 ffn: not the decode plan's shape
                       (dict(top_k=5), qm.MOE_EUNSUPPORTED), (dict(hidden=4352), qm.MOE_EUNSUPPORTED),
-                      (dict(shared_gate=1), qm.MOE_EUNSUPPORTED)]:
+                      (dict(n_experts=0, top_k=0), qm.MOE_EUNSUPPORTED)]:
         c = qm.make_config(**{**XING4, **bad})
         if code is None:
+            assert qm.moe_stack_workspace_bytes(c, 4) > 0, bad
             continue
         with pytest.raises(qm.MoeError) as ei:
             qm.moe_stack_workspace_bytes(c, 4)

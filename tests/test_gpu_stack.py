@@ -1,5 +1,5 @@
-"""GPU tests of moe_stack_decode (the whole decode step of a stack of layers: one reset launch, then one
-launch per layer with the router folded in), through the C ABI: bit for bit against the chained per-layer
+"""GPU tests of moe_stack_decode (the whole decode step of a stack of layers in one call: per layer the decode
+plan's two launches, the layer's input formed in the first), through the C ABI: bit for bit against the chained per-layer
 calls it replaces, against the CPU oracle layer by layer, under graph capture, and with the selection bias
 absent or present."""
 import numpy as np
