@@ -253,7 +253,11 @@ moe_status moe_router_scores(const moe_config* cfg, int32_t T, const void* x_dev
 moe_status moe_bucket(const moe_config* cfg, int32_t T, const int32_t* topk_ids_dev, int32_t* counts_dev,
                       int32_t* offsets_dev, int32_t* perm_dev, int32_t* pos_dev, hipStream_t stream);
 
-/* Expert FFN and combine for given routing:
+/* Expert FFN and combine for given routing (FFN(x) = W_down (silu(W_gate x) *
+ * (W_up x)): zLLM "Algorithm Layer", FFN section; IQ4_NL weights: model card,
+ * pure-NumPy parity section; weighting after the down projection, fp32 sum:
+ * design record, section 2; slot-order sum over the bucketed routes, no
+ * atomics: design record, section 4):
  *   out[t] = sum_{k=0..K-1} topk_w[t][k] * FFN_{topk_ids[t][k]}(x[t])
  *            + FFN_shared(x[t])                     (if n_shared == 1)
  *   x_dev        bf16 [T][H]
@@ -266,7 +270,10 @@ moe_status moe_expert_forward(const moe_config* cfg, int32_t T, const void* x_de
                               const float* topk_w_dev, const void* arena_dev, const void* shared_dev,
                               float* out_dev, void* ws_dev, size_t ws_bytes, hipStream_t stream);
 
-/* The whole layer: moe_route then moe_expert_forward.  topk_ids_out_dev and
+/* The whole layer (model card "Model and routing": sigmoid router with
+ * selection bias, top-K of E routed experts plus the shared expert, weights
+ * times routed_scale; design record, section 1, for the Xing4 layer):
+ * moe_route then moe_expert_forward.  topk_ids_out_dev and
  * topk_w_out_dev receive the routing when non-NULL (else the workspace holds
  * it).  ws: >= moe_workspace_bytes(cfg, T). */
 moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
