@@ -79,7 +79,7 @@ def run_route(dl, x_bits, bias_dev=None):
 
 
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 1), ("tiny", 100), ("xing4", 64), ("batch", 128),
-                                     ("xing4", 300), ("prefill", 300), ("prefill", 2048)])
+                                     ("xing4", 300), ("xing4", 1000), ("prefill", 300), ("prefill", 2048)])
 def test_route_bit_exact(name, T):
     """Every router kernel: one row per wavefront (T < 64), 2 x 2 blocks with resident operands (tiny T=100,
     Xing4 T=64, batch T=128), 4 x 4 blocks (Xing4 T=300), 8 x 8 blocks (prefill T=300, 2048)."""
