@@ -735,7 +735,14 @@ __global__ __launch_bounds__(kDecThreads, 8) void k_decode_experts(DecodeArgs a)
     route_local(a, sh.route);
     gate_up_role<1>(a, a.arena + (int64_t)sh.route.ids[slot] * a.expert_bytes, slot, rt, sh);
   } else if ((blk -= a.n_routed_wg) < a.n_shared_wg) {
+    // The shared expert's gate/up, then its down rows, is one of the two
+    // longest chains of the call, and each of these workgroups shares a CU
+    // with a routed one: its waves issue first while their tiles stream.
+    // Raising the whole branch (the polling of h as well) starves the
+    // routed partner and is slower.
+    __builtin_amdgcn_s_setprio(3);
     gate_up_role<1>(a, a.shared, a.K, blk, sh);
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // the gate/up LDS is reused
     shared_down_part(a, blk, sh);
   } else {
