@@ -100,7 +100,7 @@ __device__ __forceinline__ bool give_up(const uint32_t* err, uint32_t it) {
 constexpr int kScaleWords = 32;  // 64 fp16 scales of a tile
 
 struct RouteLds {
-  float sel[256];
+  uint32_t key[256];  // selection-order keys (sel_order_bits of s + bias)
   float score[256];
   float sval[kMaxDecodeK];
   float w[kMaxDecodeK];
@@ -237,6 +237,10 @@ __device__ __forceinline__ RouteIn route_fetch(const DecodeArgs& a) {
 // brings expert e's score and bias), in two forms with the same result: the
 // K largest selection scores s + bias (ties: the lower expert index), their
 // scores, and the weights scale * s_k / (((s_0 + s_1) + ...)) in slot order.
+// Both compare the scores' order keys (sel_order_bits) with the index as the
+// tie-break: a total order whatever the scores hold, so that a NaN score (from
+// a NaN input) still leaves K distinct experts in the K slots, the same in
+// every workgroup, and no slot's expert id is left unset.
 //
 // route_rank_lds: every expert's rank among all E counted by its own thread
 // from LDS, three barriers (≈2.3 µs at E = 64).  The decode kernel's down
@@ -249,14 +253,17 @@ __device__ void route_rank_lds(const DecodeArgs& a, RouteLds& r, RouteIn v) {
   const int e = threadIdx.x;
   if (e < a.E) {
     r.score[e] = v.s;
-    r.sel[e] = a.bias ? v.s + v.b : v.s;
+    r.key[e] = sel_order_bits(a.bias ? v.s + v.b : v.s);
   }
   __syncthreads();
   if (e < a.E) {
-    const float se = r.sel[e];
+    const uint32_t ke = r.key[e];
     int rank = 0;
 #pragma unroll 8
-    for (int q = 0; q < a.E; q++) rank += sel_before(r.sel[q], q, se, e);
+    for (int q = 0; q < a.E; q++) {
+      const uint32_t kq = r.key[q];
+      rank += kq > ke || (kq == ke && q < e);
+    }
     if (rank < a.K) {
       r.ids[rank] = e;
       r.sval[rank] = r.score[e];
@@ -281,7 +288,7 @@ __device__ void route_rank_wave(const DecodeArgs& a, RouteLds& r, RouteIn v) {
   if (a.E > 64) {  // experts past wavefront 0 meet in LDS
     if (e < a.E) {
       r.score[e] = v.s;
-      r.sel[e] = a.bias ? v.s + v.b : v.s;
+      r.key[e] = sel_order_bits(a.bias ? v.s + v.b : v.s);
     }
     __syncthreads();
   }
@@ -308,7 +315,7 @@ __device__ void route_rank_wave(const DecodeArgs& a, RouteLds& r, RouteIn v) {
         const int x = e + 64 * q;
         const bool avail = x < a.E;
         s[q] = avail ? r.score[x] : 0.0f;
-        key[q] = avail ? sel_order_bits(r.sel[x]) : 0u;
+        key[q] = avail ? r.key[x] : 0u;
       }
       for (int k = 0; k < a.K; k++) {
         float sk;

@@ -91,16 +91,12 @@ __device__ __forceinline__ float router_logit(const uint16_t* xrow, int H, int l
   return router_logit_vals<MMAX>(xv, H, w);
 }
 
-// The (selection score, expert) order: a precedes b when its score is larger,
-// or equal with a smaller expert index.
-__device__ __forceinline__ bool sel_before(float sa, int ea, float sb, int eb) {
-  return sa > sb || (sa == sb && ea < eb);
-}
-
 // A selection score's bits mapped so that unsigned order is float order (a
-// selection score is never -0: a sigmoid is +0 or positive, and +0 plus a
-// bias never rounds to -0, and never NaN).  Every such key is >= 1, so 0 is
-// below every key (no candidate).
+// selection score from finite inputs is never -0: a sigmoid is +0 or
+// positive, and +0 plus a bias never rounds to -0, and never NaN).  Every such
+// key is >= 1, so 0 is below every key (no candidate).  A NaN score (from a
+// NaN input) gets a key too; the rankings compare keys and break ties by the
+// expert index, so whatever the scores hold they pick K experts in range.
 __device__ __forceinline__ uint32_t sel_order_bits(float s) {
   const uint32_t u = __float_as_uint(s);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

@@ -436,6 +436,33 @@ def test_route_ties_break_by_lower_expert_index(path):
         assert np.array_equal(w[0].view(np.uint32), rw[t].view(np.uint32)), t
 
 
+@pytest.mark.parametrize("T", [1, 2])
+def test_nan_input_still_routes_to_experts_in_range(T):
+    """A NaN in a token's activations makes every router logit NaN.  Every ranking compares order keys
+    with the expert index as the tie-break, so the token still takes K distinct experts in range: the
+    lowest indices, since all its scores tie, and the same ones in every workgroup.  No kernel then
+    streams weights from outside the arena.  T = 1 is the decode plan, T = 2 the multi-kernel plan;
+    the other token of T = 2 is finite and routed as the oracle routes it."""
+    s, inp, dl = device_layer("xing4")
+    cfg = dl.cfg
+    x = synth.tokens(s, T, first=77).copy()
+    x[0, 5] = 0x7FC0  # bf16 quiet NaN
+    log(f"NaN input T={T}")
+    ids = torch.full((T, cfg.top_k), -1, dtype=torch.int32, device="cuda")
+    w = torch.empty((T, cfg.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+    qm.moe_layer_forward(cfg, T, to_dev_bf16(x), dl.gate_w, dl.bias, dl.arena, dl.shared, out, ids, w,
+                         ws=dl.workspace(T))
+    got = ids.cpu().numpy()
+    assert got[0].tolist() == list(range(cfg.top_k))
+    if T == 1:
+        assert_status_ok(cfg, 1, dl.workspace(1))
+    else:
+        rid, _, _, _ = oracle.route(x[1:2], inp["gate_w"], s.top_k, s.routed_scale)
+        assert np.array_equal(got[1], rid[0])
+        assert np.isfinite(out[1].cpu().numpy()).all()
+
+
 def test_decode_state_survives_batched_calls_on_the_same_workspace():
     """Decode calls interleaved with batched calls (FP32 and BF16 contracts) on one workspace: the
     decode path's words at the start of the workspace are not disturbed by the batched calls."""
