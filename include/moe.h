@@ -275,7 +275,10 @@ moe_status moe_expert_forward(const moe_config* cfg, int32_t T, const void* x_de
  * times routed_scale; design record, section 1, for the Xing4 layer):
  * moe_route then moe_expert_forward.  topk_ids_out_dev and
  * topk_w_out_dev receive the routing when non-NULL (else the workspace holds
- * it).  ws: >= moe_workspace_bytes(cfg, T). */
+ * it).  ws: >= moe_workspace_bytes(cfg, T).  A token whose activations hold
+ * a NaN has NaN scores, which all tie: it takes the K lowest expert indices
+ * (on every plan) and its output row is NaN; no other token is affected and
+ * no access leaves the given buffers. */
 moe_status moe_layer_forward(const moe_config* cfg, int32_t T, const void* x_dev, const float* gate_w_dev,
                              const float* sel_bias_dev, const void* arena_dev, const void* shared_dev,
                              float* out_dev, int32_t* topk_ids_out_dev, float* topk_w_out_dev, void* ws_dev,
